@@ -1,0 +1,204 @@
+"""CPU oracle of the few-row draft-head vocabulary projection -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline`` leg may
+import this package.  The product library (``few_row_vocab_amd``) never does, and it shares
+no code with it.  This module marshals numpy arrays into ``liboracle.so`` (oracle.c, plain C
+in double precision); every definition lives, with its citation, in oracle.c.
+
+Parity pins: see tests/test_oracle_*.py.  Functions without an independent pin: the readings
+for rescore pads and out-of-range candidate ids (``rescore``), which are "parity unpinned"
+beyond their own definitions.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+FMT_BF16 = 0
+FMT_FP8_BLOCK32 = 1
+FMT_FP8_ROW = 2
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        c = ctypes
+        L.orc_bf16_value.restype = c.c_double
+        L.orc_bf16_value.argtypes = [c.c_uint16]
+        L.orc_e4m3_value.restype = c.c_double
+        L.orc_e4m3_value.argtypes = [c.c_uint8]
+        L.orc_e8m0_value.restype = c.c_double
+        L.orc_e8m0_value.argtypes = [c.c_uint8]
+        L.orc_e4m3_encode.restype = c.c_uint8
+        L.orc_e4m3_encode.argtypes = [c.c_float]
+        L.orc_beats.restype = c.c_int
+        L.orc_beats.argtypes = [c.c_float, c.c_int64, c.c_float, c.c_int64]
+        L.orc_gemv.restype = None
+        L.orc_gemv.argtypes = [c.c_int, c.c_void_p, c.c_void_p, c.c_int64, c.c_int64,
+                               c.c_void_p, c.c_int, c.c_void_p, c.c_int64, c.c_void_p]
+        L.orc_topk.restype = c.c_int
+        L.orc_topk.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
+                               c.c_void_p]
+        L.orc_rescore.restype = None
+        L.orc_rescore.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_int,
+                                  c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p]
+        L.orc_quant_row.restype = None
+        L.orc_quant_row.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p,
+                                    c.c_void_p]
+        L.orc_quant_block32.restype = None
+        L.orc_quant_block32.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p,
+                                        c.c_void_p]
+        L.orc_threads.restype = c.c_int
+        L.orc_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def bf16_value(b):
+    return lib().orc_bf16_value(int(b))
+
+
+def e4m3_value(c):
+    return lib().orc_e4m3_value(int(c))
+
+
+def e8m0_value(b):
+    return lib().orc_e8m0_value(int(b))
+
+
+def e4m3_encode(f):
+    return lib().orc_e4m3_encode(float(np.float32(f)))
+
+
+def beats(lu, u, lv, v):
+    return bool(lib().orc_beats(float(np.float32(lu)), int(u), float(np.float32(lv)), int(v)))
+
+
+def gemv(fmt, w, scale, x, vids=None):
+    """O5.  w: bf16 bits uint16 [V][H] or E4M3 codes uint8 [V][H]; scale: None, uint8
+    [ceil(V/32)][H/32] or float32 [V]; x: bf16 bits uint16 [R][H].  Returns float32
+    [R][V] (or [R][len(vids)])."""
+    w = np.ascontiguousarray(w)
+    V, H = w.shape
+    x = _c(x, np.uint16)
+    R = x.shape[0]
+    if x.shape[1] != H:
+        raise ValueError("x width != head width")
+    if fmt == FMT_BF16:
+        w = _c(w, np.uint16)
+        scale = None
+    elif fmt == FMT_FP8_BLOCK32:
+        w = _c(w, np.uint8)
+        scale = _c(scale, np.uint8)
+        if scale.shape != ((V + 31) // 32, H // 32):
+            raise ValueError("block scale shape")
+    elif fmt == FMT_FP8_ROW:
+        w = _c(w, np.uint8)
+        scale = _c(scale, np.float32)
+        if scale.shape != (V,):
+            raise ValueError("row scale shape")
+    else:
+        raise ValueError("format")
+    if vids is not None:
+        vids = _c(np.asarray(vids, dtype=np.int64), np.int64)
+        if vids.size and (vids.min() < 0 or vids.max() >= V):
+            raise ValueError("vids out of range")
+        nv = vids.size
+    else:
+        nv = V
+    out = np.empty((R, nv), np.float32)
+    lib().orc_gemv(fmt, _p(w), _p(scale), V, H, _p(x), R, _p(vids), nv, _p(out))
+    return out
+
+
+def topk(logits, k):
+    """O8/O9.  logits float32 [R][V] -> (ids int32 [R][k], vals float32 [R][k])."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    ids = np.empty((R, k), np.int32)
+    vals = np.empty((R, k), np.float32)
+    if lib().orc_topk(_p(logits), R, V, k, _p(ids), _p(vals)) != 0:
+        raise MemoryError("oracle top-k")
+    return ids, vals
+
+
+def argmax(logits):
+    return topk(logits, 1)[0][:, 0].copy()
+
+
+def rescore(dense_w, x, cand, use=None):
+    """O10.  dense_w bf16 bits [V][H]; x [R][H]; cand int32 [R][ck]; use uint8/bool [R][ck]
+    or None.  Returns (exact float32 [R][ck], draft int32 [R])."""
+    dense_w = _c(dense_w, np.uint16)
+    V, H = dense_w.shape
+    x = _c(x, np.uint16)
+    cand = _c(cand, np.int32)
+    R, ck = cand.shape
+    if use is not None:
+        use = _c(np.asarray(use).astype(np.uint8), np.uint8)
+    exact = np.empty((R, ck), np.float32)
+    draft = np.empty((R,), np.int32)
+    lib().orc_rescore(_p(dense_w), V, H, _p(x), R, _p(cand), _p(use), ck, _p(exact),
+                      _p(draft))
+    return exact, draft
+
+
+def draft(fmt, w, scale, x, k, dense_w=None):
+    """O11.  One stage: top-k of the head's logits and argmax.  Two stage (dense_w given):
+    top cand_k = k by the head's logits, then the rescore of the eligible candidates (pads
+    are not candidates).  Returns dict with logits, ids, vals, draft (+ exact)."""
+    logits = gemv(fmt, w, scale, x)
+    ids, vals = topk(logits, k)
+    out = {"logits": logits, "ids": ids, "vals": vals}
+    if dense_w is None:
+        out["draft"] = ids[:, 0].copy()
+    else:
+        use = vals > -np.inf  # pads of the stage-1 list carry -inf
+        exact, d = rescore(dense_w, x, ids, use)
+        out["exact"] = exact
+        out["draft"] = d
+    return out
+
+
+def quant_row(w_bf16):
+    """Q1 -> (codes uint8 [V][H], scale float32 [V])."""
+    w = _c(w_bf16, np.uint16)
+    V, H = w.shape
+    codes = np.empty((V, H), np.uint8)
+    scale = np.empty((V,), np.float32)
+    lib().orc_quant_row(_p(w), V, H, _p(codes), _p(scale))
+    return codes, scale
+
+
+def quant_block32(w_bf16):
+    """Q2 -> (codes uint8 [V][H], scales uint8 [ceil(V/32)][H/32])."""
+    w = _c(w_bf16, np.uint16)
+    V, H = w.shape
+    if H % 32:
+        raise ValueError("H must be a multiple of 32")
+    codes = np.empty((V, H), np.uint8)
+    scales = np.empty(((V + 31) // 32, H // 32), np.uint8)
+    lib().orc_quant_block32(_p(w), V, H, _p(codes), _p(scales))
+    return codes, scales
+
+
+def threads():
+    return lib().orc_threads()

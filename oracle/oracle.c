@@ -1,0 +1,342 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference of the few-row draft-head
+ * vocabulary projection.  TEST INFRASTRUCTURE ONLY: nothing in the product library links,
+ * loads or calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Sources (web pages on one inference engine, cited by page title and section):
+ *  [TFE]   "dsv41 Zig: the TFE draft head (TF_DS_DRAFTER=eagle), off by default"
+ *  [SUPER] "nemotron: Super's MTP drafts on the draft vocabulary's FP8 rows while a stream's
+ *           text is covered, same replies"
+ *  [METAL] "dsv41 metal: the DSpark drafter on an FP8 head, a concurrent propose and
+ *           resident buffers"
+ *
+ * Floating point: every dot product is accumulated in IEEE double, in increasing h, and
+ * rounded once to float.  Build with -O2 -ffp-contract=off and no fast-math, so that the
+ * compiler neither fuses nor reorders the sums and NaN/inf follow IEEE rules.
+ *
+ * Numbering O1..O11 / Q1..Q2 is the oracle's own list of definitions, restated in the
+ * comments of each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FMT_BF16 0
+#define ORC_FMT_FP8_BLOCK32 1
+#define ORC_FMT_FP8_ROW 2
+
+/* ---------------------------------------------------------------- number formats */
+
+/* O1: a bf16 value is the top half of an IEEE binary32; widening is exact. */
+double orc_bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* O2: OCP E4M3 ("e4m3" in [TFE] commit notes on FP8 linears, "E4M3 codes" in [METAL]
+ * 'FP8 draft head'): sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0.
+ * Exponent field 0 is subnormal (M/8 * 2^-6).  Exponent 15 with mantissa 7 is NaN; there
+ * is no infinity, so the largest finite magnitude is 1.75 * 2^8 = 448 -- the divisor of the
+ * per-row scale rule in [TFE] 'Update'. */
+double orc_e4m3_value(uint8_t c)
+{
+    int s = (c >> 7) & 1;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* O3: E8M0 block scale ([METAL] 'FP8 draft head': one E8M0 scale per 32x32 block): the
+ * byte is a biased power-of-two exponent, 2^(b-127); 255 encodes NaN. */
+double orc_e8m0_value(uint8_t b)
+{
+    if (b == 255)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* O4: the real value of weight (v, h) in each storage format.  Every product here is exact
+ * in double: at most 4 significant bits times a power of two or a 24-bit float. */
+static double weight_value(int fmt, const void *w, const void *scale, int64_t H, int64_t v,
+                           int64_t h)
+{
+    if (fmt == ORC_FMT_BF16)
+        return orc_bf16_value(((const uint16_t *)w)[v * H + h]);
+    double q = orc_e4m3_value(((const uint8_t *)w)[v * H + h]);
+    if (fmt == ORC_FMT_FP8_BLOCK32) {
+        int64_t hb = H / 32;
+        return q * orc_e8m0_value(((const uint8_t *)scale)[(v / 32) * hb + h / 32]);
+    }
+    return q * (double)((const float *)scale)[v];
+}
+
+/* ---------------------------------------------------------------- GEMV */
+
+/* O5: logits[r][j] = float( sum over h = 0..H-1 of x[r][h] * w[vids[j]][h] ), the sum taken
+ * in double in increasing h.  [TFE] commit notes on the own GEMV: up to 16 activation rows
+ * against the head, fp32 output; 'What this changes': fp32 sums.  vids == NULL means every
+ * vocabulary row in order (nv must then equal V).  Output layout [R][nv].  Rows are
+ * independent, so the OpenMP split over j does not change any result. */
+void orc_gemv(int fmt, const void *w, const void *scale, int64_t V, int64_t H,
+              const uint16_t *x, int R, const int64_t *vids, int64_t nv, float *out)
+{
+    (void)V;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nv; j++) {
+        int64_t v = vids ? vids[j] : j;
+        double acc[64];
+        for (int r = 0; r < R; r++)
+            acc[r] = 0.0;
+        for (int64_t h = 0; h < H; h++) {
+            double wv = weight_value(fmt, w, scale, H, v, h);
+            for (int r = 0; r < R; r++)
+                acc[r] += orc_bf16_value(x[(int64_t)r * H + h]) * wv;
+        }
+        for (int r = 0; r < R; r++)
+            out[(int64_t)r * nv + j] = (float)acc[r];
+    }
+}
+
+/* ---------------------------------------------------------------- ordering and top-k */
+
+/* O6: a logit can be picked iff it is neither NaN nor -inf.  [SUPER] commit notes on the
+ * few-row router top-k: once the finite scores are used up every later pick is index 0,
+ * exactly as repeated argmax over -inf gives; NaN is never the larger of a comparison. */
+static int eligible(float l)
+{
+    return !isnan(l) && l > -INFINITY;
+}
+
+/* O7: u beats v iff u is eligible and (v is not, or l_u > l_v, or l_u == l_v and u < v).
+ * [SUPER]: higher score first, then lower index; [TFE] 'Update': a tie at the k-th value
+ * goes to the lower token id.  Equality is IEEE, so -0 == +0. */
+int orc_beats(float lu, int64_t u, float lv, int64_t v)
+{
+    if (!eligible(lu))
+        return 0;
+    if (!eligible(lv))
+        return 1;
+    if (lu > lv)
+        return 1;
+    if (lu < lv)
+        return 0;
+    return u < v;
+}
+
+struct entry {
+    float l;
+    int64_t id;
+};
+
+static int cmp_entry(const void *a, const void *b)
+{
+    const struct entry *ea = a, *eb = b;
+    if (orc_beats(ea->l, ea->id, eb->l, eb->id))
+        return -1;
+    if (orc_beats(eb->l, eb->id, ea->l, ea->id))
+        return 1;
+    return 0;
+}
+
+/* O8 + O9: per row, the eligible ids sorted by O7, the first min(k, n_eligible) of them;
+ * the remaining slots are (id 0, value -inf) ([SUPER] pad rule).  Slot j holds the entry
+ * that exactly j others beat.  ids/vals are [R][k]; the argmax of a row is ids[r][0] (0 for
+ * a row with no eligible logit).  Returns 0, or -1 if memory runs out. */
+int orc_topk(const float *logits, int R, int64_t V, int k, int32_t *ids, float *vals)
+{
+    struct entry *e = malloc(sizeof *e * (size_t)(V > 0 ? V : 1));
+    if (!e)
+        return -1;
+    for (int r = 0; r < R; r++) {
+        const float *row = logits + (int64_t)r * V;
+        int64_t n = 0;
+        for (int64_t v = 0; v < V; v++)
+            if (eligible(row[v])) {
+                e[n].l = row[v];
+                e[n].id = v;
+                n++;
+            }
+        qsort(e, (size_t)n, sizeof *e, cmp_entry);
+        for (int j = 0; j < k; j++) {
+            if (j < n) {
+                ids[(int64_t)r * k + j] = (int32_t)e[j].id;
+                vals[(int64_t)r * k + j] = e[j].l;
+            } else {
+                ids[(int64_t)r * k + j] = 0;
+                vals[(int64_t)r * k + j] = -INFINITY;
+            }
+        }
+    }
+    free(e);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- two-stage rescore */
+
+/* O10: exact[r][j] = float(sum_h x[r][h] * Wd[cand[r][j]][h]) in double, increasing h, from
+ * the dense bf16 head ([TFE] 'Update': the two_stage head drafts the argmax of the exact
+ * logits of its candidates, taken from a dense bf16 copy of the target's head).
+ * Readings where the page is silent:
+ *  - a candidate id outside [0, V) is not read; its exact logit is NaN (never drafted);
+ *  - if use[r][j] == 0 the slot is a pad of the stage-1 list, not a candidate: it is not
+ *    rescored and its exact logit is -inf (use == NULL: every slot is a candidate);
+ *  - draft[r] is the candidate token that beats the others under O7 applied to (exact,
+ *    token id); 0 when no candidate is eligible. */
+void orc_rescore(const uint16_t *Wd, int64_t V, int64_t H, const uint16_t *x, int R,
+                 const int32_t *cand, const uint8_t *use, int cand_k, float *exact,
+                 int32_t *draft)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < (int64_t)R * cand_k; t++) {
+        int r = (int)(t / cand_k);
+        int64_t id = cand[t];
+        if (use && !use[t]) {
+            exact[t] = -INFINITY;
+            continue;
+        }
+        if (id < 0 || id >= V) {
+            exact[t] = NAN;
+            continue;
+        }
+        double acc = 0.0;
+        for (int64_t h = 0; h < H; h++)
+            acc += orc_bf16_value(x[(int64_t)r * H + h]) * orc_bf16_value(Wd[id * H + h]);
+        exact[t] = (float)acc;
+    }
+    for (int r = 0; r < R; r++) {
+        int best = -1;
+        for (int j = 0; j < cand_k; j++) {
+            int64_t t = (int64_t)r * cand_k + j;
+            if (!eligible(exact[t]))
+                continue;
+            if (best < 0 ||
+                orc_beats(exact[t], cand[t], exact[(int64_t)r * cand_k + best],
+                          cand[(int64_t)r * cand_k + best]))
+                best = j;
+        }
+        draft[r] = best < 0 ? 0 : cand[(int64_t)r * cand_k + best];
+    }
+}
+
+/* ---------------------------------------------------------------- quantizers (input prep) */
+
+/* E4M3 encode with round-to-nearest-even and saturation to +-448, from a float.
+ * NaN maps to the NaN code.  Written from the format definition: find the quantum of the
+ * binade the magnitude falls in, divide (exact: a power of two), round half to even. */
+uint8_t orc_e4m3_encode(float f)
+{
+    uint8_t sign = signbit(f) ? 0x80 : 0x00;
+    double a = fabs((double)f);
+    if (isnan(f))
+        return sign | 0x7F;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal binade: quantum 2^-9; m == 8 is the smallest normal, code 0x08 */
+        double m = rint(a / ldexp(1.0, -9));
+        return sign | (uint8_t)m;
+    }
+    int e = (int)floor(log2(a));
+    /* guard against log2 rounding at exact powers of two */
+    while (ldexp(1.0, e) > a)
+        e--;
+    while (ldexp(1.0, e + 1) <= a)
+        e++;
+    double m = rint(a / ldexp(1.0, e - 3)); /* in [8, 16] */
+    if (m == 16.0) {
+        m = 8.0;
+        e++;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | ((int)m - 8));
+}
+
+/* Q1, per-row FP8 ([TFE] commit notes and 'Update' on FP8 linears): from the bf16 weight,
+ * s = float(amax_row / 448) and code = E4M3_RNE(float(w / s)).  An all-zero row gets s = 0
+ * and all codes 0 (reading: the page leaves a zero row open). */
+void orc_quant_row(const uint16_t *w, int64_t V, int64_t H, uint8_t *codes, float *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < V; v++) {
+        float amax = 0.0f;
+        for (int64_t h = 0; h < H; h++) {
+            float a = fabsf((float)orc_bf16_value(w[v * H + h]));
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax / 448.0f;
+        scale[v] = s;
+        for (int64_t h = 0; h < H; h++) {
+            if (s == 0.0f) {
+                codes[v * H + h] = 0;
+                continue;
+            }
+            float q = (float)orc_bf16_value(w[v * H + h]) / s;
+            codes[v * H + h] = orc_e4m3_encode(q);
+        }
+    }
+}
+
+/* Q2, 32x32 block FP8 with E8M0 scales ([METAL] 'FP8 draft head': E4M3 codes, one E8M0
+ * scale per 32x32 block, made from the bf16 head at load).  The page gives no rule for the
+ * exponent; reading: e is the smallest integer with amax_block <= 448 * 2^e (exact
+ * comparison), stored as e + 127 clamped to [0, 254]; an all-zero block stores 127.  Codes
+ * are E4M3_RNE(w * 2^-e): one exact scaling and one rounding.  A partial last block (V not
+ * a multiple of 32) covers the rows that exist.  Scale layout [ceil(V/32)][H/32]. */
+void orc_quant_block32(const uint16_t *w, int64_t V, int64_t H, uint8_t *codes,
+                       uint8_t *scales)
+{
+    int64_t vb = (V + 31) / 32, hb = H / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < vb * hb; b++) {
+        int64_t bv = b / hb, bh = b % hb;
+        int64_t v1 = bv * 32 + 32 < V ? bv * 32 + 32 : V;
+        double amax = 0.0;
+        for (int64_t v = bv * 32; v < v1; v++)
+            for (int64_t h = bh * 32; h < bh * 32 + 32; h++) {
+                double a = fabs(orc_bf16_value(w[v * H + h]));
+                if (a > amax)
+                    amax = a;
+            }
+        int e;
+        if (amax == 0.0) {
+            e = 0;
+        } else {
+            e = -150;
+            while (amax > ldexp(448.0, e))
+                e++;
+        }
+        if (e < -127)
+            e = -127;
+        if (e > 127)
+            e = 127;
+        scales[b] = (uint8_t)(e + 127);
+        for (int64_t v = bv * 32; v < v1; v++)
+            for (int64_t h = bh * 32; h < bh * 32 + 32; h++) {
+                double q = ldexp(orc_bf16_value(w[v * H + h]), -e);
+                codes[v * H + h] = orc_e4m3_encode((float)q);
+            }
+    }
+}
+
+/* Number of threads OpenMP will use (for reporting the CPU baseline). */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,236 @@
+"""Benchmark of the few-row draft-head vocabulary projection on one MI355X.
+
+One step = one pass of the whole projection over one batch: dh_gemv (the FP8 E4M3 head with
+E8M0 32x32 block scales, H=5120, V=129280, 16 activation rows) then dh_topk (top-64 and
+argmax) -- the same kernels dh_draft launches.  Inputs are resident in HBM before timing;
+three copies of the FP8 head are rotated so that no step finds the head in the 256 MB
+Infinity Cache.
+
+Printed: one JSON line.  value = algorithmic HBM bytes of a step (head codes + scales +
+activations + fp32 logits written) / time per step, in GB/s.  Extra fields give the row
+sweep (1/5/10/15/16 rows) per entry point, the bf16 head, the two-stage head (FP8 row scale
++ dense bf16 rescore of 512 candidates), the roofline of the GEMV kernel (HIP events around
+each launch on the launching stream) and the CPU oracle timed on the host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+NCOPY = 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stats_us(times_ms):
+    t = np.sort(np.asarray(times_ms)) * 1e3
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90)), "n": int(t.size)}
+
+
+def algorithmic_bytes(fmt, V, H, R):
+    w = V * H * (2 if fmt == "bf16" else 1)
+    s = ((V + 31) // 32) * (H // 32) if fmt == "fp8_block32" else (V * 4 if fmt == "fp8_row" else 0)
+    return w + s + R * H * 2 + R * V * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--calls", type=int, default=50, help="timed calls per sweep entry")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="main step only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the projection's "
+              "multi-GPU split is a design note, not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from few_row_vocab_amd import dh
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = "row_sweep"
+    c = synth.CONFIGS[name]
+    V, H, K = c["V"], c["H"], 64
+    R = 16
+
+    t0 = time.time()
+    w = synth.head_bf16(name)
+    x = synth.activations(name, R)
+    log(f"generated {V}x{H} head in {time.time() - t0:.1f}s")
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    heads = []
+    for i in range(NCOPY):
+        codes, scale = dh.quantize(wd, dh.FP8_BLOCK32)
+        heads.append(dh.Head(dh.FP8_BLOCK32, codes, scale))
+    torch.cuda.synchronize()
+    # quantization time (load-time prep; the pages quote 0.2 s on 16 CPU workers)
+    qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    qe[0].record()
+    dh.quantize(wd, dh.FP8_BLOCK32)
+    qe[1].record()
+    torch.cuda.synchronize()
+    quant_ms = qe[0].elapsed_time(qe[1])
+
+    logits = torch.empty((R, V), dtype=torch.float32, device=dev)
+    ids = torch.empty((R, K), dtype=torch.int32, device=dev)
+    vals = torch.empty((R, K), dtype=torch.float32, device=dev)
+    am = torch.empty((R,), dtype=torch.int32, device=dev)
+    ws = dh.workspace(R, V, K)
+
+    def step(i, ev=None):
+        h = heads[i % NCOPY]
+        if ev is not None:
+            ev[0].record()
+        dh.gemv(h, xd, logits)
+        if ev is not None:
+            ev[1].record()
+        dh.topk(logits, K, ws=ws, ids=ids, vals=vals, argmax=am)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    gemv_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    step_bytes = algorithmic_bytes("fp8_block32", V, H, R)
+    gemv_avg_ms = float(np.mean(gemv_ms))
+    achieved = step_bytes / (gemv_avg_ms * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us, gemv {gemv_avg_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s)")
+
+    out = {
+        "metric": "draft-head µs/call and achieved HBM GB/s (FP8 head, 1/5/10/16 rows)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2), "rows_per_s": round(R / (ms_per_step * 1e-3), 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) head quantized to FP8 on the GPU, N(0,1) rows)",
+        "config": {"workload": f"FP8 E4M3 head with E8M0 32x32 block scales, H={H}, V={V}, "
+                               f"{R} activation rows, dh_gemv + dh_topk(k={K}) with argmax",
+                   "H": H, "V": V, "rows": R, "k": K, "format": "fp8_block32",
+                   "head_copies_rotated": NCOPY, "step_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "kernel": "gemv_kernel<FP8_BLOCK32, 5>",
+                     "kernel_us": round(gemv_avg_ms * 1e3, 2)},
+        "quantize_fp8_block32_ms": round(quant_ms, 3),
+    }
+
+    if not args.quick:
+        out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
+    print(json.dumps(out), flush=True)
+
+
+def timed(fn, n, warm=3):
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def sweep(dh, torch, heads, wd, xd, V, H, K, n):
+    res = {"fp8_block32": [], "bf16": []}
+    dense = [dh.Head(dh.BF16, wd)] + [dh.Head(dh.BF16, wd.clone()) for _ in range(1)]
+    torch.cuda.synchronize()
+    for fmt, hs in (("fp8_block32", heads), ("bf16", dense)):
+        for R in (1, 5, 10, 15, 16):
+            x = xd[:R].contiguous()
+            lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
+            ws = dh.workspace(R, V, K)
+            o = {"ids": torch.empty((R, K), dtype=torch.int32, device=xd.device),
+                 "vals": torch.empty((R, K), dtype=torch.float32, device=xd.device),
+                 "draft": torch.empty((R,), dtype=torch.int32, device=xd.device)}
+            g = stats_us(timed(lambda i: dh.gemv(hs[i % len(hs)], x, lg), n))
+            t = stats_us(timed(lambda i: dh.topk(lg, K, ws=ws, ids=o["ids"], vals=o["vals"],
+                                                  argmax=o["draft"]), n))
+            d = stats_us(timed(lambda i: dh.draft(hs[i % len(hs)], x, K, ws=ws, out=o), n))
+            b = algorithmic_bytes(fmt, V, H, R)
+            res[fmt].append({"rows": R, "dh_gemv_us": g, "dh_topk_us": t, "dh_draft_us": d,
+                             "gemv_GBps": round(b / (g["median"] * 1e-6) / 1e9, 1),
+                             "draft_GBps": round(b / (d["median"] * 1e-6) / 1e9, 1),
+                             "rows_per_s": round(R / (d["median"] * 1e-6), 1),
+                             "frac_of_8TBps": round(b / (g["median"] * 1e-6) / 8e12, 4)})
+            log(f"{fmt} R={R}: gemv {g['median']:.1f} us, topk {t['median']:.1f} us, "
+                f"draft {d['median']:.1f} us")
+    # two-stage: FP8 row-scaled stage 1 + dense bf16 rescore of 512 candidates, 16 rows
+    rc, rs = dh.quantize(wd, dh.FP8_ROW)
+    h1 = dh.Head(dh.FP8_ROW, rc, rs)
+    R, k = 16, 512
+    ws = dh.workspace(R, V, k)
+    o = {"ids": torch.empty((R, k), dtype=torch.int32, device=xd.device),
+         "vals": torch.empty((R, k), dtype=torch.float32, device=xd.device),
+         "draft": torch.empty((R,), dtype=torch.int32, device=xd.device),
+         "exact": torch.empty((R, k), dtype=torch.float32, device=xd.device)}
+    d = stats_us(timed(lambda i: dh.draft(h1, xd, k, dense=dense[0], ws=ws, out=o), n))
+    lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
+    g = stats_us(timed(lambda i: dh.gemv(h1, xd, lg), n))
+    t = stats_us(timed(lambda i: dh.topk(lg, k, ws=ws, ids=o["ids"], vals=o["vals"]), n))
+    s = stats_us(timed(lambda i: dh.rescore(dense[0], xd, o["ids"], exact=o["exact"],
+                                            draft=o["draft"]), n))
+    b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
+    res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
+                        "dh_topk_us": t, "dh_rescore_us": s,
+                        "draft_GBps_upper_bytes": round(b / (d["median"] * 1e-6) / 1e9, 1)}
+    log(f"two-stage: draft {d['median']:.1f} us (gemv {g['median']:.1f}, topk "
+        f"{t['median']:.1f}, rescore {s['median']:.1f})")
+    return res
+
+
+def cpu_baseline(w, x, V, H, R, K):
+    """The oracle as it stands (C, double precision, OpenMP over vocabulary rows) on the
+    host's cores: one full step (GEMV + top-k) over the first `rows` vocabulary rows of the
+    same head; the FP8 codes come from the oracle's own quantizer (not timed)."""
+    import oracle
+    S = min(V, 32768)
+    t0 = time.time()
+    codes, scales = oracle.quant_block32(w[:S])
+    tq = time.time() - t0
+    t0 = time.time()
+    lg = oracle.gemv(oracle.FMT_FP8_BLOCK32, codes, scales, x)
+    oracle.topk(lg, K)
+    dt = time.time() - t0
+    b = algorithmic_bytes("fp8_block32", S, H, R)
+    log(f"cpu oracle: {S} vocab rows x {R} rows in {dt:.2f}s ({oracle.threads()} threads)")
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(dt, 3), "quantize_seconds": round(tq, 3),
+            "sample": f"first {S} of {V} vocabulary rows of the FP8 block head, {R} rows, "
+                      f"GEMV + top-{K}, once; GB/s over the sample's algorithmic bytes"}
+
+
+if __name__ == "__main__":
+    main()

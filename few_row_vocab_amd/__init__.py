@@ -1,0 +1,11 @@
+"""few_row_vocab_amd -- the few-row draft-head vocabulary projection on MI355X (gfx950).
+
+The product is the C-ABI library libdh.so (include/dh.h) built from csrc/*.hip; this package
+holds it, its build script and a thin Python binding (dh.py).
+"""
+from . import dh
+from .dh import (BF16, FP8_BLOCK32, FP8_ROW, DHError, Head, draft, gemv, quantize, rescore,
+                 topk, workspace, workspace_bytes)
+
+__all__ = ["dh", "BF16", "FP8_BLOCK32", "FP8_ROW", "DHError", "Head", "draft", "gemv",
+           "quantize", "rescore", "topk", "workspace", "workspace_bytes"]

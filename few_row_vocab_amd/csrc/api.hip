@@ -1,0 +1,303 @@
+// The C ABI (include/dh.h): host-side checks, then the launches.  Every refusal happens
+// before anything is enqueued, so a refused call leaves the outputs untouched -- the pages'
+// stance of refusing a larger span rather than clipping it ("dsv41 Zig: the TFE draft head
+// (TF_DS_DRAFTER=eagle), off by default", commit notes on absorb and the review thread).
+#include <atomic>
+#include <stdint.h>
+
+#include "dh_internal.h"
+
+namespace dh {
+
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n > 0 && dev < 64)
+        return n;
+    n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+        n = 256;
+    if (dev < 64)
+        cache[slot].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace dh
+
+namespace {
+
+using dh::TopkWs;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void *p, size_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p + bytes}; }
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+size_t elem_bytes(int format) { return format == DH_BF16 ? 2 : 1; }
+
+size_t scale_bytes(const dh_head &h)
+{
+    if (h.format == DH_FP8_BLOCK32)
+        return (size_t)((h.vocab + 31) / 32) * (size_t)(h.hidden / 32);
+    if (h.format == DH_FP8_ROW)
+        return (size_t)h.vocab * sizeof(float);
+    return 0;
+}
+
+dh_status check_head(const dh_head *h)
+{
+    if (!h || !h->weight)
+        return DH_ERR_INVALID;
+    if (h->format != DH_BF16 && h->format != DH_FP8_BLOCK32 && h->format != DH_FP8_ROW)
+        return DH_ERR_INVALID;
+    if (h->vocab < 1 || h->hidden < 32 || h->hidden % 32 != 0)
+        return DH_ERR_INVALID;
+    if (h->hidden > DH_MAX_HIDDEN || h->vocab > (int64_t)INT32_MAX - 16)
+        return DH_ERR_UNSUPPORTED;
+    if (!aligned(h->weight, 16))
+        return DH_ERR_INVALID;
+    if (h->format == DH_BF16) {
+        if (h->scale)
+            return DH_ERR_INVALID;
+    } else {
+        if (!h->scale)
+            return DH_ERR_INVALID;
+        if (h->format == DH_FP8_ROW && !aligned(h->scale, 4))
+            return DH_ERR_INVALID;
+    }
+    return DH_OK;
+}
+
+Span head_weight(const dh_head &h)
+{
+    return span(h.weight, (size_t)h.vocab * (size_t)h.hidden * elem_bytes(h.format));
+}
+
+Span head_scale(const dh_head &h) { return span(h.scale, scale_bytes(h)); }
+
+dh_status check_rows(int32_t rows)
+{
+    if (rows < 1)
+        return DH_ERR_INVALID;
+    if (rows > DH_MAX_ROWS)
+        return DH_ERR_UNSUPPORTED;
+    return DH_OK;
+}
+
+dh_status check_k(int32_t k, int64_t vocab)
+{
+    if (k < 1 || k > vocab)
+        return DH_ERR_INVALID;
+    if (k > DH_MAX_K)
+        return DH_ERR_UNSUPPORTED;
+    return DH_OK;
+}
+
+dh_status device_status(hipError_t e) { return e == hipSuccess ? DH_OK : DH_ERR_DEVICE; }
+
+#define DH_TRY(expr)                        \
+    do {                                    \
+        const dh_status s_ = (expr);        \
+        if (s_ != DH_OK)                    \
+            return s_;                      \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *logits,
+                  void *stream)
+{
+    DH_TRY(check_head(head));
+    DH_TRY(check_rows(rows));
+    if (!x || !logits || !aligned(x, 16) || !aligned(logits, 4))
+        return DH_ERR_INVALID;
+    const Span out = span(logits, (size_t)rows * (size_t)head->vocab * sizeof(float));
+    if (overlap(out, head_weight(*head)) || overlap(out, head_scale(*head)) ||
+        overlap(out, span(x, (size_t)rows * (size_t)head->hidden * 2)))
+        return DH_ERR_INVALID;
+    return device_status(dh::launch_gemv(*head, x, rows, logits, (hipStream_t)stream));
+}
+
+size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k)
+{
+    if (check_rows(rows) != DH_OK || vocab < 1 || vocab > DH_MAX_VOCAB ||
+        check_k(k, vocab) != DH_OK)
+        return 0;
+    const TopkWs w = dh::topk_ws_layout(rows, vocab, k);
+    const size_t logits = (size_t)rows * (size_t)vocab * sizeof(float);
+    return w.bytes + ((logits + 255) & ~(size_t)255);
+}
+
+static dh_status check_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k,
+                            int32_t *ids, float *vals, int32_t *argmax, void *workspace,
+                            size_t workspace_bytes)
+{
+    DH_TRY(check_rows(rows));
+    if (vocab < 1)
+        return DH_ERR_INVALID;
+    if (vocab > DH_MAX_VOCAB)
+        return DH_ERR_UNSUPPORTED;
+    DH_TRY(check_k(k, vocab));
+    if (!logits || !ids || !vals || !aligned(logits, 4) || !aligned(ids, 4) ||
+        !aligned(vals, 4) || (argmax && !aligned(argmax, 4)))
+        return DH_ERR_INVALID;
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < dh::topk_ws_layout(rows, vocab, k).bytes)
+        return DH_ERR_WORKSPACE;
+    const Span in = span(logits, (size_t)rows * (size_t)vocab * sizeof(float));
+    const Span si = span(ids, (size_t)rows * k * 4), sv = span(vals, (size_t)rows * k * 4);
+    const Span sa = span(argmax, argmax ? (size_t)rows * 4 : 0);
+    const Span sw = span(workspace, dh::topk_ws_layout(rows, vocab, k).bytes);
+    if (overlap(in, si) || overlap(in, sv) || overlap(in, sa) || overlap(si, sv) ||
+        overlap(si, sa) || overlap(sv, sa) || overlap(sw, in) || overlap(sw, si) ||
+        overlap(sw, sv) || overlap(sw, sa))
+        return DH_ERR_INVALID;
+    return DH_OK;
+}
+
+dh_status dh_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k, int32_t *ids,
+                  float *vals, int32_t *argmax, void *workspace, size_t workspace_bytes,
+                  void *stream)
+{
+    DH_TRY(check_topk(logits, rows, vocab, k, ids, vals, argmax, workspace, workspace_bytes));
+    return device_status(dh::launch_topk(logits, rows, vocab, k, ids, vals, argmax, workspace,
+                                         (hipStream_t)stream));
+}
+
+static dh_status check_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
+                               const int32_t *cand_ids, int32_t cand_k, float *exact,
+                               int32_t *draft)
+{
+    DH_TRY(check_head(dense));
+    if (dense->format != DH_BF16)
+        return DH_ERR_INVALID;
+    DH_TRY(check_rows(rows));
+    if (cand_k < 1)
+        return DH_ERR_INVALID;
+    if (cand_k > DH_MAX_K)
+        return DH_ERR_UNSUPPORTED;
+    if (!x || !cand_ids || !exact || !draft || !aligned(x, 16) || !aligned(cand_ids, 4) ||
+        !aligned(exact, 4) || !aligned(draft, 4))
+        return DH_ERR_INVALID;
+    const Span se = span(exact, (size_t)rows * cand_k * 4), sd = span(draft, (size_t)rows * 4);
+    const Span sc = span(cand_ids, (size_t)rows * cand_k * 4);
+    const Span sx = span(x, (size_t)rows * (size_t)dense->hidden * 2);
+    const Span sw = head_weight(*dense);
+    if (overlap(se, sd) || overlap(se, sc) || overlap(sd, sc) || overlap(se, sx) ||
+        overlap(sd, sx) || overlap(se, sw) || overlap(sd, sw))
+        return DH_ERR_INVALID;
+    return DH_OK;
+}
+
+dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
+                     const int32_t *cand_ids, int32_t cand_k, float *exact, int32_t *draft,
+                     void *stream)
+{
+    DH_TRY(check_rescore(dense, x, rows, cand_ids, cand_k, exact, draft));
+    return device_status(dh::launch_rescore(*dense, x, rows, cand_ids, nullptr, cand_k, exact,
+                                            draft, (hipStream_t)stream));
+}
+
+dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x, int32_t rows,
+                   int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
+                   float *logits, void *workspace, size_t workspace_bytes, void *stream)
+{
+    DH_TRY(check_head(head));
+    DH_TRY(check_rows(rows));
+    if (head->vocab > DH_MAX_VOCAB)
+        return DH_ERR_UNSUPPORTED;
+    DH_TRY(check_k(k, head->vocab));
+    if (!x || !aligned(x, 16) || !draft || !aligned(draft, 4) || (logits && !aligned(logits, 4)))
+        return DH_ERR_INVALID;
+    if (dense) {
+        DH_TRY(check_head(dense));
+        if (dense->format != DH_BF16 || dense->vocab != head->vocab ||
+            dense->hidden != head->hidden || !exact)
+            return DH_ERR_INVALID;
+    } else if (exact) {
+        return DH_ERR_INVALID;
+    }
+    const TopkWs tw = dh::topk_ws_layout(rows, head->vocab, k);
+    const size_t lbytes = (size_t)rows * (size_t)head->vocab * sizeof(float);
+    const size_t need = tw.bytes + (logits ? 0 : ((lbytes + 255) & ~(size_t)255));
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+        return DH_ERR_WORKSPACE;
+    float *L = logits ? logits : reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
+    // The stage-1 outputs and the workspace must be clear of the inputs and of each other.
+    const Span sl = span(L, lbytes), sw = span(workspace, tw.bytes);
+    const Span in[] = {head_weight(*head), head_scale(*head),
+                       span(x, (size_t)rows * (size_t)head->hidden * 2),
+                       dense ? head_weight(*dense) : Span{0, 0}};
+    for (const Span &s : in)
+        if (overlap(sl, s) || overlap(sw, s))
+            return DH_ERR_INVALID;
+    if (logits && overlap(sl, span(workspace, need)))
+        return DH_ERR_INVALID;
+    DH_TRY(check_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft, workspace,
+                      tw.bytes));
+    if (dense)
+        DH_TRY(check_rescore(dense, x, rows, ids, k, exact, draft));
+    for (const Span &s : in) {
+        if (overlap(span(ids, (size_t)rows * k * 4), s) ||
+            overlap(span(vals, (size_t)rows * k * 4), s) || overlap(span(draft, (size_t)rows * 4), s))
+            return DH_ERR_INVALID;
+    }
+    const hipStream_t st = (hipStream_t)stream;
+    hipError_t e = dh::launch_gemv(*head, x, rows, L, st);
+    if (e == hipSuccess)
+        e = dh::launch_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft,
+                            workspace, st);
+    if (e == hipSuccess && dense)
+        e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st);
+    return device_status(e);
+}
+
+dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
+                      uint8_t *codes, void *scale, void *stream)
+{
+    if (format != DH_FP8_BLOCK32 && format != DH_FP8_ROW)
+        return DH_ERR_INVALID;
+    if (vocab < 1 || hidden < 32 || hidden % 32 != 0)
+        return DH_ERR_INVALID;
+    if (hidden > DH_MAX_HIDDEN || vocab > (int64_t)INT32_MAX / 2)
+        return DH_ERR_UNSUPPORTED;
+    if (!w || !codes || !scale || !aligned(w, 2) || (format == DH_FP8_ROW && !aligned(scale, 4)))
+        return DH_ERR_INVALID;
+    dh_head h{format, vocab, hidden, codes, scale};
+    const Span sw = span(w, (size_t)vocab * (size_t)hidden * 2), sc = head_weight(h),
+               ss = head_scale(h);
+    if (overlap(sw, sc) || overlap(sw, ss) || overlap(sc, ss))
+        return DH_ERR_INVALID;
+    return device_status(
+        dh::launch_quantize(format, w, vocab, hidden, codes, scale, (hipStream_t)stream));
+}
+
+const char *dh_status_string(int32_t status)
+{
+    switch (status) {
+    case DH_OK: return "ok";
+    case DH_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad format, "
+                                "bad size, or overlapping buffers)";
+    case DH_ERR_UNSUPPORTED: return "size outside the implemented limits (rows <= 16, "
+                                    "k <= 512, hidden <= 8192, vocab <= 262144)";
+    case DH_ERR_WORKSPACE: return "workspace missing, misaligned or too small "
+                                  "(see dh_workspace_bytes)";
+    case DH_ERR_DEVICE: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

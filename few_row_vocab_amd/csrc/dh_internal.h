@@ -1,0 +1,51 @@
+// Internal declarations shared by the library's translation units (kernels and the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dh.h"
+
+namespace dh {
+
+// Vector types the gfx950 builtins take.
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int kWave = 64;
+
+// Top-k layout: a row is cut into chunks of kChunk logits; pass 1 keeps each chunk's best
+// min(k, chunk) entries, pass 2 merges a row's lists.  Pass 2 holds up to kMergeSlots
+// (chunks * k) list slots per row in registers.
+constexpr int kChunk = 4096;
+constexpr int kP1Threads = 256;
+constexpr int kP1PerThread = kChunk / kP1Threads;   // 16
+constexpr int kMergeThreads = 1024;
+constexpr int kMergePerThread = 32;
+constexpr int kMergeSlots = kMergeThreads * kMergePerThread;   // 32768
+
+inline int64_t topk_chunks(int64_t vocab) { return (vocab + kChunk - 1) / kChunk; }
+
+// Workspace layout of the top-k (offsets in bytes, each 256-byte aligned).
+struct TopkWs {
+    size_t val_off, id_off, cnt_off, bytes;
+};
+TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
+
+// Launchers: argument checking has been done by the caller (api.cpp).  Each returns the
+// hipError_t of its launches.
+hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
+                       hipStream_t stream);
+hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int32_t *ids,
+                       float *vals, int32_t *argmax, void *ws, hipStream_t stream);
+hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
+                          const int32_t *cand_ids, const float *cand_vals, int cand_k,
+                          float *exact, int32_t *draft, hipStream_t stream);
+hipError_t launch_quantize(int format, const uint16_t *w, int64_t vocab, int64_t hidden,
+                           uint8_t *codes, void *scale, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
+}  // namespace dh

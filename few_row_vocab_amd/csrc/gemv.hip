@@ -1,0 +1,279 @@
+// Few-row vocabulary GEMV on gfx950 matrix cores.
+//
+// logits[r][v] = sum_h x[r][h] * w[v][h] for up to 16 activation rows r against a [V][H]
+// head stored as bf16, as E4M3 codes with E8M0 scales per 32x32 block, or as E4M3 codes with
+// an fp32 scale per row.  Sources: "dsv41 Zig: the TFE draft head (TF_DS_DRAFTER=eagle), off
+// by default" (commit notes: the own GEMV for up to 16 rows, fp32 output; 'What this
+// changes': fp32 sums; 'Update': FP8 linears with a row scale) and "dsv41 metal: the DSpark
+// drafter on an FP8 head, a concurrent propose and resident buffers" ('FP8 draft head':
+// E4M3 codes with E8M0 scales per 32x32 block).
+//
+// Design (MI355X):
+//  * The head is streamed from HBM exactly once; it is the whole cost (>98% of the bytes).
+//  * One v_mfma_f32_16x16x32_bf16 multiplies a 16-row x 32-column weight tile by the
+//    32 x 16 activation block; its N = 16 columns are the (up to) 16 activation rows, so
+//    the same instruction sequence serves 1..16 rows and a row's sums never depend on how
+//    many rows share the call.
+//  * FP8 codes are widened to bf16 in registers with v_cvt_scalef32_pk_bf16_fp8, the block
+//    scale applied in the same instruction.  E4M3 times a power of two is exact in bf16, so
+//    the products are the exact products; only fp32 accumulation rounds.
+//  * A workgroup splits H over its waves (up to 16).  Each wave keeps its H-slice of the
+//    activations in VGPRs for the whole kernel, so activations are read once per workgroup,
+//    and streams 16-row tiles of the head: lane l reads 16 contiguous bytes (bf16: 32) of
+//    row l%16 at column 16*(l/16) of each 64-column block.  The waves' partial 16x16 tiles
+//    are summed through LDS in a fixed wave order (deterministic) and written as fp32.
+//  * Persistent grid: one workgroup per CU slot, tiles taken round-robin; each 64-column
+//    block's registers are refilled with the next tile as soon as they are widened, so a
+//    tile of loads is always in flight, also across the reduction's barrier.
+#include "dh_internal.h"
+#include "launch.h"
+
+namespace dh {
+namespace {
+
+constexpr int kTileRows = 16;
+constexpr int kMaxWaves = 16;
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
+constexpr int kNonTemporal = 2;          // cache policy bit: streamed once
+
+struct GemvArgs {
+    const uint8_t *w;       // weight bytes
+    const uint8_t *bscale;  // E8M0 [ceil(V/32)][H/32] (block format)
+    const float *rscale;    // fp32 [V] (row format)
+    const uint16_t *x;      // bf16 [R][H]
+    float *logits;          // fp32 [R][V]
+    int64_t V;
+    int H;
+    int R;
+    int ntiles;
+    int nkb;                // number of 64-column blocks, ceil(H / 64)
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+union Pack8 {
+    bf16x8 v;
+    uint32_t u[4];
+    u32x4 q;
+};
+
+template <bool HI>
+__device__ inline uint32_t cvt2(uint32_t src, float scale)
+{
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)src, scale, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 16 E4M3 codes -> two groups of 8 bf16 (bytes 0..7 and 8..15), each times `scale`.
+__device__ inline void widen16(u32x4 q, float scale, bf16x8 &a0, bf16x8 &a1)
+{
+    Pack8 p0, p1;
+    p0.u[0] = cvt2<false>(q.x, scale);
+    p0.u[1] = cvt2<true>(q.x, scale);
+    p0.u[2] = cvt2<false>(q.y, scale);
+    p0.u[3] = cvt2<true>(q.y, scale);
+    p1.u[0] = cvt2<false>(q.z, scale);
+    p1.u[1] = cvt2<true>(q.z, scale);
+    p1.u[2] = cvt2<false>(q.w, scale);
+    p1.u[3] = cvt2<true>(q.w, scale);
+    a0 = p0.v;
+    a1 = p1.v;
+}
+
+// An E8M0 byte as the fp32 scale operand: the bit pattern b << 23, which is the power of
+// two 2^(b-127) for bytes 1..254.
+__device__ inline float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23); }
+
+template <int FMT, int KBW>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
+{
+    constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
+    constexpr int ES = FMT == DH_BF16 ? 2 : 1;   // bytes per weight element
+    __shared__ float red[2][kMaxWaves][4][kWave];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int rr = lane & 15;
+    const int g = lane >> 4;
+    const int H = a.H;
+    const int64_t V = a.V;
+
+    // This wave's H-slice of the activations: the B operands of every tile.
+    bf16x8 xb[KBW][2];
+#pragma unroll
+    for (int kb = 0; kb < KBW; kb++) {
+        const int blk = wave * KBW + kb;
+        const int k0 = blk * 64 + 16 * g;
+        Pack8 p0, p1;
+        p0.q = u32x4{0u, 0u, 0u, 0u};
+        p1.q = u32x4{0u, 0u, 0u, 0u};
+        if (rr < a.R && blk < a.nkb && k0 < H) {
+            const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)rr * H + k0);
+            p0.q = px[0];
+            p1.q = px[1];
+        }
+        xb[kb][0] = p0.v;
+        xb[kb][1] = p1.v;
+    }
+
+    // One register slot per 64-column block.  A slot is refilled with the next tile's
+    // block as soon as its current contents have been widened, so a whole tile of loads
+    // stays in flight (through the reduction below) with a single set of registers.
+    u32x4 raw[KBW][RQ];
+    uint32_t sc[KBW];
+
+    // Buffer loads: the descriptor (SGPRs) is rebased on each tile and bounded by the
+    // tile's existing rows, so rows past V read as zeros; a lane's offset within a tile is
+    // the same for every tile, and a block adds an immediate offset.
+    const uint32_t wrow = (uint32_t)H * ES;
+    const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KBW * 64 + 16 * g) * ES;
+    const uint32_t soff = (uint32_t)(2 * wave * KBW + (g >> 1));
+    auto load_block = [&](__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr, int kb) {
+        const int blk = wave * KBW + kb;
+        if (blk < a.nkb && blk * 64 + 16 * g < H) {
+#pragma unroll
+            for (int q = 0; q < RQ; q++)
+                raw[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, woff + (uint32_t)(kb * 64 * ES + 16 * q), 0, kNonTemporal);
+            sc[kb] = FMT == DH_FP8_BLOCK32
+                         ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, soff + 2 * kb, 0, 0)
+                         : 127u;
+        } else {
+#pragma unroll
+            for (int q = 0; q < RQ; q++)
+                raw[kb][q] = u32x4{0u, 0u, 0u, 0u};
+            sc[kb] = 127u;
+        }
+    };
+    auto wrsrc = [&](int tile) {
+        const int64_t v0 = (int64_t)tile * kTileRows;
+        const int64_t rows = V - v0 < kTileRows ? V - v0 : kTileRows;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + v0 * wrow), (short)0,
+                                                 (int)(rows * wrow), kRsrcWord3);
+    };
+    auto srsrc = [&](int tile) {
+        const uint8_t *p = FMT == DH_FP8_BLOCK32 ? a.bscale + (int64_t)(tile >> 1) * (H >> 5)
+                                                 : a.w;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, H >> 5, kRsrcWord3);
+    };
+
+    int tile = blockIdx.x;
+    if (tile >= a.ntiles)
+        return;
+    {
+        const __amdgpu_buffer_rsrc_t wr = wrsrc(tile), sr = srsrc(tile);
+#pragma unroll
+        for (int kb = 0; kb < KBW; kb++)
+            load_block(wr, sr, kb);
+    }
+    int buf = 0;
+    for (;;) {
+        const int next = tile + gridDim.x;
+        const bool more = next < a.ntiles;
+        const __amdgpu_buffer_rsrc_t wr = wrsrc(more ? next : tile);
+        const __amdgpu_buffer_rsrc_t sr = srsrc(more ? next : tile);
+
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KBW; kb++) {
+            bf16x8 a0, a1;
+            if constexpr (FMT == DH_BF16) {
+                Pack8 p0, p1;
+                p0.q = raw[kb][0];
+                p1.q = raw[kb][RQ - 1];
+                a0 = p0.v;
+                a1 = p1.v;
+            } else {
+                widen16(raw[kb][0], FMT == DH_FP8_BLOCK32 ? e8m0_scale(sc[kb]) : 1.0f, a0, a1);
+            }
+            if (more)
+                load_block(wr, sr, kb);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb[kb][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb[kb][1], acc, 0, 0, 0);
+        }
+
+        // acc[j] of lane l is the partial sum of head row 4*(l/16)+j of the tile for
+        // activation row l%16 over this wave's H-slice.
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            red[buf][wave][j][lane] = acc[j];
+        __syncthreads();
+        if (threadIdx.x < kTileRows * 16) {
+            const int c = threadIdx.x >> 4;        // activation row
+            const int i = threadIdx.x & 15;        // head row within the tile
+            const int src = c + 16 * (i >> 2);
+            const int j = i & 3;
+            float s = 0.f;
+            for (int w = 0; w < nw; w++)
+                s += red[buf][w][j][src];
+            const int64_t v = (int64_t)tile * kTileRows + i;
+            if (c < a.R && v < V) {
+                if (FMT == DH_FP8_ROW)
+                    s *= a.rscale[v];
+                a.logits[(int64_t)c * V + v] = s;
+            }
+        }
+        buf ^= 1;
+        if (!more)
+            break;
+        tile = next;
+    }
+}
+
+template <int FMT, int KBW>
+hipError_t run(const GemvArgs &a, hipStream_t stream)
+{
+    static int occ_cache[kMaxWaves + 1];
+    const int nw = (a.nkb + KBW - 1) / KBW;
+    const int block = nw * kWave;
+    const int occ = occupancy(gemv_kernel<FMT, KBW>, block, occ_cache[nw]);
+    int64_t grid = (int64_t)device_cus() * occ;
+    if (grid > a.ntiles)
+        grid = a.ntiles;
+    return launch(gemv_kernel<FMT, KBW>, dim3((unsigned)grid), dim3(block), 0, stream, a);
+}
+
+template <int FMT>
+hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
+{
+    const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;
+    switch (kbw) {
+    case 1: return run<FMT, 1>(a, stream);
+    case 2: return run<FMT, 2>(a, stream);
+    case 3: return run<FMT, 3>(a, stream);
+    case 4: return run<FMT, 4>(a, stream);
+    case 5: return run<FMT, 5>(a, stream);
+    case 6: return run<FMT, 6>(a, stream);
+    case 7: return run<FMT, 7>(a, stream);
+    case 8: return run<FMT, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
+                       hipStream_t stream)
+{
+    GemvArgs a;
+    a.w = static_cast<const uint8_t *>(head.weight);
+    a.bscale = head.format == DH_FP8_BLOCK32 ? static_cast<const uint8_t *>(head.scale)
+                                             : nullptr;
+    a.rscale = head.format == DH_FP8_ROW ? static_cast<const float *>(head.scale) : nullptr;
+    a.x = x;
+    a.logits = logits;
+    a.V = head.vocab;
+    a.H = (int)head.hidden;
+    a.R = rows;
+    a.ntiles = (int)((head.vocab + kTileRows - 1) / kTileRows);
+    a.nkb = (int)((head.hidden + 63) / 64);
+    switch (head.format) {
+    case DH_BF16: return run_fmt<DH_BF16>(a, stream);
+    case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32>(a, stream);
+    case DH_FP8_ROW: return run_fmt<DH_FP8_ROW>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dh

@@ -1,0 +1,222 @@
+"""Python binding of libdh.so (include/dh.h): argument marshalling only.
+
+Every step of the projection runs in the library's HIP kernels; torch provides device
+buffers and the current stream.  There is no fallback: if libdh.so is missing or a call is
+refused, this module raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdh.so")
+
+BF16 = 0
+FP8_BLOCK32 = 1
+FP8_ROW = 2
+FORMATS = {"bf16": BF16, "fp8_block32": FP8_BLOCK32, "fp8_row": FP8_ROW}
+
+MAX_ROWS = 16
+MAX_K = 512
+MAX_HIDDEN = 8192
+MAX_VOCAB = 262144
+
+STATUS = {0: "DH_OK", 1: "DH_ERR_INVALID", 2: "DH_ERR_UNSUPPORTED", 3: "DH_ERR_WORKSPACE",
+          4: "DH_ERR_DEVICE"}
+
+
+class DHError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _Head(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("vocab", ctypes.c_int64),
+                ("hidden", ctypes.c_int64), ("weight", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdh.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python few_row_vocab_amd/build.py` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        c = ctypes
+        hp, vp, i32, i64, sz = c.POINTER(_Head), c.c_void_p, c.c_int32, c.c_int64, c.c_size_t
+        L.dh_gemv.argtypes = [hp, vp, i32, vp, vp]
+        L.dh_topk.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, sz, vp]
+        L.dh_rescore.argtypes = [hp, vp, i32, vp, i32, vp, vp, vp]
+        L.dh_draft.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
+        L.dh_workspace_bytes.argtypes = [i32, i64, i32]
+        L.dh_workspace_bytes.restype = sz
+        L.dh_status_string.argtypes = [i32]
+        L.dh_status_string.restype = c.c_char_p
+        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize):
+            f.restype = i32
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise DHError(status, lib().dh_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _want(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+
+
+def _bits16(t):
+    """bf16 tensors are passed as their bit patterns."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@dataclass
+class Head:
+    """A vocabulary head: weight [V][H] (bf16, or uint8 E4M3 codes) and its scale (None,
+    uint8 E8M0 [ceil(V/32)][H/32], or float32 [V])."""
+    format: int
+    weight: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+
+    @property
+    def vocab(self):
+        return self.weight.shape[0]
+
+    @property
+    def hidden(self):
+        return self.weight.shape[1]
+
+    def _c(self):
+        w = self.weight
+        if self.format == BF16:
+            if w.dtype not in (torch.bfloat16, torch.int16):
+                raise TypeError("bf16 head: weight must be bfloat16 (or its int16 bits)")
+        elif w.dtype != torch.uint8:
+            raise TypeError("FP8 head: weight must be uint8 E4M3 codes")
+        _want(w, w.dtype, "weight")
+        if self.scale is not None:
+            _want(self.scale, self.scale.dtype, "scale")
+        return _Head(self.format, w.shape[0], w.shape[1], w.data_ptr(),
+                     None if self.scale is None else self.scale.data_ptr())
+
+
+def workspace_bytes(rows, vocab, k):
+    return int(lib().dh_workspace_bytes(rows, vocab, k))
+
+
+def workspace(rows, vocab, k, device="cuda"):
+    n = workspace_bytes(rows, vocab, k)
+    if n == 0:
+        raise DHError(2, "sizes outside the library's limits")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gemv(head: Head, x, logits=None, stream=None):
+    """logits [R][V] fp32 = x [R][H] (bf16) times the head."""
+    _want(x, x.dtype if x.dtype in (torch.bfloat16, torch.int16) else torch.bfloat16, "x")
+    R = x.shape[0]
+    if logits is None:
+        logits = torch.empty((R, head.vocab), dtype=torch.float32, device=x.device)
+    _want(logits, torch.float32, "logits")
+    h = head._c()
+    _check(lib().dh_gemv(ctypes.byref(h), _ptr(x), R, _ptr(logits), _stream(stream)))
+    return logits
+
+
+def topk(logits, k, ws=None, ids=None, vals=None, argmax=None, with_argmax=True,
+         stream=None):
+    """(ids int32 [R][k], vals fp32 [R][k], argmax int32 [R] or None)."""
+    _want(logits, torch.float32, "logits")
+    R, V = logits.shape
+    dev = logits.device
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev) if ids is None else ids
+    vals = torch.empty((R, k), dtype=torch.float32, device=dev) if vals is None else vals
+    if with_argmax and argmax is None:
+        argmax = torch.empty((R,), dtype=torch.int32, device=dev)
+    ws = workspace(R, V, k, dev) if ws is None else ws
+    _check(lib().dh_topk(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
+                         _ptr(ws), ws.numel(), _stream(stream)))
+    return ids, vals, argmax
+
+
+def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
+    """(exact fp32 [R][cand_k], draft int32 [R])."""
+    _want(cand_ids, torch.int32, "cand_ids")
+    R, ck = cand_ids.shape
+    dev = x.device
+    exact = torch.empty((R, ck), dtype=torch.float32, device=dev) if exact is None else exact
+    draft = torch.empty((R,), dtype=torch.int32, device=dev) if draft is None else draft
+    h = dense._c()
+    _check(lib().dh_rescore(ctypes.byref(h), _ptr(x), R, _ptr(cand_ids), ck, _ptr(exact),
+                            _ptr(draft), _stream(stream)))
+    return exact, draft
+
+
+def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=False,
+          out=None, stream=None):
+    """The whole projection: dict with ids, vals, draft (+ exact, logits)."""
+    R = x.shape[0]
+    dev = x.device
+    o = {} if out is None else out
+    o.setdefault("ids", torch.empty((R, k), dtype=torch.int32, device=dev))
+    o.setdefault("vals", torch.empty((R, k), dtype=torch.float32, device=dev))
+    o.setdefault("draft", torch.empty((R,), dtype=torch.int32, device=dev))
+    if dense is not None:
+        o.setdefault("exact", torch.empty((R, k), dtype=torch.float32, device=dev))
+    if keep_logits:
+        o.setdefault("logits", torch.empty((R, head.vocab), dtype=torch.float32, device=dev))
+    ws = workspace(R, head.vocab, k, dev) if ws is None else ws
+    h = head._c()
+    d = dense._c() if dense is not None else None
+    _check(lib().dh_draft(ctypes.byref(h), ctypes.byref(d) if d is not None else None,
+                          _ptr(x), R, k, _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
+                          _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(),
+                          _stream(stream)))
+    return o
+
+
+def quantize(w, format, stream=None):
+    """FP8 head from a bf16 head [V][H]: (codes uint8 [V][H], scale)."""
+    if w.dtype not in (torch.bfloat16, torch.int16):
+        raise TypeError("w must be bfloat16 (or its int16 bits)")
+    _want(w, w.dtype, "w")
+    V, H = w.shape
+    codes = torch.empty((V, H), dtype=torch.uint8, device=w.device)
+    if format == FP8_BLOCK32:
+        scale = torch.empty(((V + 31) // 32, H // 32), dtype=torch.uint8, device=w.device)
+    elif format == FP8_ROW:
+        scale = torch.empty((V,), dtype=torch.float32, device=w.device)
+    else:
+        raise ValueError("format must be FP8_BLOCK32 or FP8_ROW")
+    _check(lib().dh_quantize(format, _ptr(w), V, H, _ptr(codes), _ptr(scale), _stream(stream)))
+    return codes, scale
+
+
+def status_string(status):
+    return lib().dh_status_string(status).decode()

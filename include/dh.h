@@ -1,0 +1,156 @@
+/*
+ * dh.h -- C ABI of the few-row draft-head vocabulary projection for MI355X (gfx950).
+ *
+ * A speculative-decoding draft head ends in a projection of its last hidden rows onto the
+ * vocabulary: a GEMV of 1..16 bf16 activation rows against a [V][H] head, fp32 logits, a
+ * per-row top-k and argmax, and optionally a rescore of the top-k candidates against a dense
+ * bf16 head.  Sources (web pages on one inference engine, cited by title and section):
+ *   [TFE]   "dsv41 Zig: the TFE draft head (TF_DS_DRAFTER=eagle), off by default"
+ *   [SUPER] "nemotron: Super's MTP drafts on the draft vocabulary's FP8 rows while a
+ *            stream's text is covered, same replies"
+ *   [METAL] "dsv41 metal: the DSpark drafter on an FP8 head, a concurrent propose and
+ *            resident buffers"
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must point to device memory of the current HIP
+ *    device; the caller allocates and frees every buffer and keeps it alive until the work
+ *    on `stream` has completed.  The library allocates nothing, frees nothing and keeps no
+ *    pointer past the call.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Calls only enqueue work and return;
+ *    outputs are valid once the stream has reached that point.
+ *  - Every argument is checked on the host before anything is enqueued.  On a refusal the
+ *    call returns a non-zero dh_status, enqueues nothing and leaves every output untouched.
+ *    Sizes out of range are refused, never clipped.
+ *  - A failure reported by the HIP runtime at launch returns DH_ERR_DEVICE.
+ *  - Outputs must not overlap inputs or each other.
+ *  - The library keeps no mutable global state: calls on different streams may overlap.
+ *  - Matrices are row-major and dense (row stride == row length).
+ */
+#ifndef DH_H
+#define DH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DH_OK = 0,
+    DH_ERR_INVALID = 1,     /* null/misaligned pointer, bad format code, negative size,
+                               outputs overlapping inputs */
+    DH_ERR_UNSUPPORTED = 2, /* a size outside what the kernels implement (see limits) */
+    DH_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    DH_ERR_DEVICE = 4       /* the HIP runtime reported an error at launch */
+} dh_status;
+
+/* Storage formats of a vocabulary head [V][H].
+ *  DH_BF16        weight: bf16 bits, uint16 [V][H]; scale: NULL.  [TFE] two_stage commit
+ *                 note and 'Update': the dense bf16 copy of the target's head.
+ *  DH_FP8_BLOCK32 weight: OCP E4M3 codes, uint8 [V][H]; scale: E8M0 bytes, uint8
+ *                 [ceil(V/32)][H/32], the value of weight (v,h) being
+ *                 e4m3(code[v][h]) * 2^(scale[v/32][h/32] - 127).  [METAL] 'FP8 draft head'.
+ *  DH_FP8_ROW     weight: OCP E4M3 codes, uint8 [V][H]; scale: float32 [V], the value of
+ *                 weight (v,h) being e4m3(code[v][h]) * scale[v].  [TFE] commit notes and
+ *                 'Update' on FP8 linears (one fp32 scale a row).
+ * The GPU widens each scaled weight to bf16 before its products; that is exact while
+ * e4m3(code) * 2^(byte-127) is a normal bf16 number, which holds for every code when the
+ * scale byte is in 10..246 (a head the quantizer below makes from weights whose 32x32 block
+ * maxima lie in [2^-100, 2^100] always is). */
+typedef enum { DH_BF16 = 0, DH_FP8_BLOCK32 = 1, DH_FP8_ROW = 2 } dh_format;
+
+/* A head: a host struct naming device buffers.  `weight` must be 16-byte aligned; a float32
+ * row scale must be 4-byte aligned. */
+typedef struct dh_head {
+    int32_t format;     /* dh_format */
+    int64_t vocab;      /* V >= 1 rows (token ids 0..V-1) */
+    int64_t hidden;     /* H >= 32 columns, a multiple of 32 */
+    const void *weight; /* device */
+    const void *scale;  /* device, or NULL for DH_BF16 */
+} dh_head;
+
+/* Limits of this implementation (refused with DH_ERR_UNSUPPORTED beyond them).
+ * Rows: [TFE] commit notes -- the head's own GEMV takes up to 16 rows.
+ * k: [TFE] 'Update' -- the candidate count runs from 1 to 512. */
+#define DH_MAX_ROWS 16
+#define DH_MAX_K 512
+#define DH_MAX_HIDDEN 8192
+#define DH_MAX_VOCAB 262144
+
+/* dh_gemv -- logits[r][v] = sum_h x[r][h] * w[v][h] for r < rows, v < V, in fp32.
+ * [TFE] commit notes: the own GEMV for up to 16 rows with fp32 output; 'What this changes':
+ * fp32 sums.  x: device bf16 bits [rows][H], 16-byte aligned.  logits: device float32
+ * [rows][V].  Summation order is fixed by the kernel and independent of `rows`, so a row's
+ * logits are bitwise the same in a 1-row and a 16-row call.  NaN and infinities propagate
+ * as in IEEE arithmetic. */
+dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *logits,
+                  void *stream);
+
+/* dh_topk -- per row, the k best logits in order: entry u beats entry v iff u is eligible
+ * and (v is not, or l_u > l_v, or l_u == l_v and u < v); NaN and -inf are not eligible, so
+ * they are never returned; -0 == +0.  Slot j holds the entry that exactly j others beat.
+ * When a row has fewer than k eligible logits the remaining slots hold (id 0, -inf).
+ * [TFE] two_stage commit note and 'Update': top cand_k fp32 logits, a tie at the k-th value
+ * going to the lower token id, cand_k from 1 to 512.  [SUPER] commit note on the few-row
+ * top-k: ranking by how many others beat an entry (higher score, then lower index), and
+ * every pick after the finite scores run out being index 0.
+ * logits: device float32 [rows][vocab].  ids: device int32 [rows][k].  vals: device float32
+ * [rows][k] (the logits' own bits, so -0 stays -0).  argmax: device int32 [rows], or NULL;
+ * argmax[r] == ids[r][0].  workspace: device, 256-byte aligned, at least
+ * dh_workspace_bytes(rows, vocab, k) bytes; its contents are scratch. */
+dh_status dh_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k, int32_t *ids,
+                  float *vals, int32_t *argmax, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* dh_rescore -- the exact logits of candidate tokens from a dense bf16 head and the
+ * candidate that wins among them.  [TFE] two_stage commit note and 'Update': the draft is
+ * the argmax of the candidates' exact logits from a dense bf16 copy of the target's head,
+ * taken through the candidates' id map.
+ * dense: a DH_BF16 head.  x: device bf16 bits [rows][H].  cand_ids: device int32
+ * [rows][cand_k].  exact: device float32 [rows][cand_k]: exact[r][j] = sum_h x[r][h] *
+ * dense[cand_ids[r][j]][h] (fp32); an id outside [0, V) is not read and gets NaN.
+ * draft: device int32 [rows]: the candidate token that beats every other candidate of the
+ * row under the dh_topk rule applied to (exact, token id); 0 if none is eligible. */
+dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
+                     const int32_t *cand_ids, int32_t cand_k, float *exact, int32_t *draft,
+                     void *stream);
+
+/* dh_draft -- the whole projection in one call: dh_gemv, then dh_topk (k), then -- when
+ * `dense` is not NULL -- the two-stage rescore of the top k candidates.  In the two-stage
+ * form the pad slots of a row with fewer than k eligible logits are not candidates: their
+ * exact logit is -inf and they are never drafted.
+ * head: the stage-1 head (any format).  dense: NULL (one stage) or a DH_BF16 head of the
+ * same V and H.  ids/vals: device [rows][k].  draft: device int32 [rows]: the argmax (one
+ * stage) or the rescored winner (two stage).  exact: device float32 [rows][k] when dense is
+ * given, else NULL.  logits: device float32 [rows][V] to receive the logits, or NULL (they
+ * then live in the workspace).  workspace: as for dh_topk, sized by dh_workspace_bytes. */
+dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x, int32_t rows,
+                   int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
+                   float *logits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* dh_quantize -- make an FP8 head from a bf16 head (load-time preparation).
+ *  DH_FP8_ROW ([TFE] 'Update' on FP8 linears): s[v] = float(max_h |w[v][h]| / 448) and
+ *    code = E4M3 round-to-nearest-even of float(w / s[v]); an all-zero row gets s = 0 and
+ *    codes 0.  scale: device float32 [V].
+ *  DH_FP8_BLOCK32 ([METAL] 'FP8 draft head': E4M3 codes with E8M0 scales per 32x32 block,
+ *    made from the bf16 head at load): e is the least integer with block amax <= 448 * 2^e,
+ *    stored as e + 127 clamped to [0, 254] (127 for an all-zero block), and code = E4M3
+ *    round-to-nearest-even of w * 2^-e.  scale: device uint8 [ceil(V/32)][H/32].
+ * E4M3 rounding saturates at +-448.  w: device bf16 bits [V][H] (finite values).  codes:
+ * device uint8 [V][H]. */
+dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
+                      uint8_t *codes, void *scale, void *stream);
+
+/* Bytes of workspace dh_topk and dh_draft need for these sizes (dh_draft with logits ==
+ * NULL included).  Pure host function; returns 0 for sizes the library refuses. */
+size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k);
+
+/* A static, NUL-terminated description of a status code. */
+const char *dh_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DH_H */

@@ -1,0 +1,175 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/dh.h declares, and
+refuses bad arguments on the host before touching any pointer (no GPU needed: refused calls
+never reach the HIP runtime, so host buffers stand in for device buffers and must come back
+untouched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from few_row_vocab_amd import dh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dh.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dh_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = dh.lib()
+    names = declared_functions()
+    assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
+                          "dh_workspace_bytes", "dh_status_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert dh.status_string(s)
+    assert dh.status_string(99) == "unknown status"
+
+
+def test_workspace_bytes_limits():
+    assert dh.workspace_bytes(16, 163840, 512) > 16 * 163840 * 4
+    assert dh.workspace_bytes(0, 1000, 8) == 0
+    assert dh.workspace_bytes(17, 1000, 8) == 0
+    assert dh.workspace_bytes(1, 1000, 0) == 0
+    assert dh.workspace_bytes(1, 1000, 513) == 0
+    assert dh.workspace_bytes(1, 10, 11) == 0
+    assert dh.workspace_bytes(1, dh.MAX_VOCAB + 1, 8) == 0
+    # grows with each size
+    assert dh.workspace_bytes(2, 5000, 8) > dh.workspace_bytes(1, 5000, 8)
+    assert dh.workspace_bytes(1, 5000, 64) > dh.workspace_bytes(1, 5000, 8)
+
+
+@pytest.fixture
+def no_device():
+    # These calls hand host memory to the library as if it were device memory; they are
+    # only safe because every one of them is refused before a launch.  Where a GPU is
+    # visible, the GPU suite repeats the refusals on real device buffers instead.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-buffer refusal tests run only where no GPU is visible")
+
+
+class HostBuf:
+    """Aligned host memory standing in for device buffers in refusal tests."""
+
+    def __init__(self, nbytes, fill=0xAB, align=256):
+        self.raw = np.full(nbytes + align, fill, np.uint8)
+        off = (-self.raw.ctypes.data) % align
+        self.a = self.raw[off:off + nbytes]
+        self.fill = fill
+
+    @property
+    def p(self):
+        return ctypes.c_void_p(self.a.ctypes.data)
+
+    def untouched(self):
+        return bool(np.all(self.a == self.fill))
+
+
+def head(fmt, V, H, w, s=None):
+    return dh._Head(fmt, V, H, w.a.ctypes.data if w else None,
+                    s.a.ctypes.data if s else None)
+
+
+def call_gemv(h, x, rows, out):
+    return dh.lib().dh_gemv(ctypes.byref(h), x.p if x else None, rows,
+                            out.p if out else None, None)
+
+
+def test_gemv_refusals_leave_outputs_untouched(no_device):
+    V, H = 100, 64
+    w, s, x, out = HostBuf(V * H), HostBuf(4 * H // 32), HostBuf(16 * H * 2), HostBuf(16 * V * 4)
+    ok = head(dh.FP8_BLOCK32, V, H, w, s)
+    cases = [
+        (ok, x, 0, out, 1), (ok, x, 17, out, 2), (ok, None, 1, out, 1), (ok, x, 1, None, 1),
+        (head(7, V, H, w, s), x, 1, out, 1),                       # bad format
+        (head(dh.FP8_BLOCK32, V, 48, w, s), x, 1, out, 1),         # H % 32
+        (head(dh.FP8_BLOCK32, V, 8224, w, s), x, 1, out, 2),       # H > 8192
+        (head(dh.FP8_BLOCK32, 0, H, w, s), x, 1, out, 1),          # V < 1
+        (head(dh.FP8_BLOCK32, V, H, w, None), x, 1, out, 1),       # missing scale
+        (head(dh.BF16, V, H, w, s), x, 1, out, 1),                 # bf16 with a scale
+        (head(dh.FP8_BLOCK32, V, H, None, s), x, 1, out, 1),       # null weight
+    ]
+    for h, xx, rows, o, want in cases:
+        assert call_gemv(h, xx, rows, o) == want, (h.format, h.vocab, h.hidden, rows)
+    # misaligned weight / activations
+    h = dh._Head(dh.FP8_BLOCK32, V, H, w.a.ctypes.data + 4, s.a.ctypes.data)
+    assert call_gemv(h, x, 1, out) == 1
+    xm = ctypes.c_void_p(x.a.ctypes.data + 2)
+    assert dh.lib().dh_gemv(ctypes.byref(ok), xm, 1, out.p, None) == 1
+    # output overlapping the weights
+    assert dh.lib().dh_gemv(ctypes.byref(ok), x.p, 1, w.p, None) == 1
+    assert out.untouched()
+
+
+def test_topk_refusals_leave_outputs_untouched(no_device):
+    R, V, k = 2, 1000, 8
+    lg, ids, vals, am = HostBuf(R * V * 4), HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * 4)
+    ws = HostBuf(dh.workspace_bytes(R, V, k))
+    L = dh.lib()
+
+    def call(rows=R, vocab=V, kk=k, wsb=None, wsp=None, logits=None, i=None):
+        wsb = ws.a.size if wsb is None else wsb
+        return L.dh_topk((logits or lg).p, rows, vocab, kk, (i or ids).p, vals.p, am.p,
+                         ws.p if wsp is None else wsp, wsb, None)
+
+    assert call(kk=0) == 1
+    assert call(kk=513) == 2
+    assert call(kk=V + 1) == 1
+    assert call(rows=0) == 1 and call(rows=17) == 2
+    assert call(vocab=dh.MAX_VOCAB + 1) == 2
+    assert call(wsb=64) == 3
+    assert call(wsp=ctypes.c_void_p(ws.a.ctypes.data + 16)) == 3      # misaligned workspace
+    assert call(i=vals) == 1                                            # ids overlap vals
+    assert ids.untouched() and vals.untouched() and am.untouched()
+
+
+def test_rescore_and_draft_refusals(no_device):
+    R, V, H, k = 2, 600, 64, 16
+    w, wd, s = HostBuf(V * H), HostBuf(V * H * 2), HostBuf(V * 4)
+    x, ids, vals, ex, dr = (HostBuf(R * H * 2), HostBuf(R * k * 4), HostBuf(R * k * 4),
+                            HostBuf(R * k * 4), HostBuf(R * 4))
+    ws = HostBuf(dh.workspace_bytes(R, V, k))
+    L = dh.lib()
+    dense = head(dh.BF16, V, H, wd)
+    stage1 = head(dh.FP8_ROW, V, H, w, s)
+    # rescore: dense head must be bf16; cand_k range
+    assert L.dh_rescore(ctypes.byref(stage1), x.p, R, ids.p, k, ex.p, dr.p, None) == 1
+    assert L.dh_rescore(ctypes.byref(dense), x.p, R, ids.p, 0, ex.p, dr.p, None) == 1
+    assert L.dh_rescore(ctypes.byref(dense), x.p, R, ids.p, 513, ex.p, dr.p, None) == 2
+    assert L.dh_rescore(ctypes.byref(dense), x.p, R, ids.p, k, ids.p, dr.p, None) == 1
+
+    def draft(h=stage1, d=dense, rows=R, kk=k, exact=ex, wsb=None):
+        return L.dh_draft(ctypes.byref(h), ctypes.byref(d) if d else None, x.p, rows, kk,
+                          ids.p, vals.p, dr.p, exact.p if exact else None, None, ws.p,
+                          ws.a.size if wsb is None else wsb, None)
+
+    assert draft(exact=None) == 1                       # two-stage needs `exact`
+    assert draft(d=None) == 1                           # one-stage must not pass `exact`
+    assert draft(d=head(dh.BF16, V - 1, H, wd)) == 1   # dense head of another size
+    assert draft(d=stage1) == 1                         # dense head not bf16
+    assert draft(kk=513) == 2
+    assert draft(wsb=100) == 3
+    assert draft(rows=17) == 2
+    for b in (ids, vals, ex, dr):
+        assert b.untouched()
+
+
+def test_quantize_refusals(no_device):
+    L = dh.lib()
+    w, c, s = HostBuf(64 * 64 * 2), HostBuf(64 * 64), HostBuf(256)
+    assert L.dh_quantize(dh.BF16, w.p, 64, 64, c.p, s.p, None) == 1
+    assert L.dh_quantize(dh.FP8_ROW, w.p, 64, 48, c.p, s.p, None) == 1
+    assert L.dh_quantize(dh.FP8_ROW, w.p, 0, 64, c.p, s.p, None) == 1
+    assert L.dh_quantize(dh.FP8_ROW, w.p, 64, 64, None, s.p, None) == 1
+    assert L.dh_quantize(dh.FP8_BLOCK32, w.p, 64, 64, w.p, s.p, None) == 1   # overlap
+    assert c.untouched() and s.untouched()

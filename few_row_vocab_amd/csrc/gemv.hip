@@ -199,9 +199,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         for (int j = 0; j < 4; j++)
             red[buf][wave][j][lane] = acc[j];
         __syncthreads();
-        if (threadIdx.x < kTileRows * 16) {
-            const int c = threadIdx.x >> 4;        // activation row
-            const int i = threadIdx.x & 15;        // head row within the tile
+        for (int o = threadIdx.x; o < kTileRows * 16; o += blockDim.x) {
+            const int c = o >> 4;                  // activation row
+            const int i = o & 15;                  // head row within the tile
             const int src = c + 16 * (i >> 2);
             const int j = i & 3;
             float s = 0.f;

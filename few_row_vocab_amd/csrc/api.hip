@@ -63,7 +63,7 @@ dh_status check_head(const dh_head *h)
         return DH_ERR_INVALID;
     if (h->vocab < 1 || h->hidden < 32 || h->hidden % 32 != 0)
         return DH_ERR_INVALID;
-    if (h->hidden > DH_MAX_HIDDEN || h->vocab > (int64_t)INT32_MAX - 16)
+    if (h->hidden > DH_MAX_HIDDEN || h->vocab > ((int64_t)1 << 25))
         return DH_ERR_UNSUPPORTED;
     if (!aligned(h->weight, 16))
         return DH_ERR_INVALID;

@@ -24,17 +24,18 @@
 //    are summed through LDS in a fixed wave order (deterministic) and written as fp32.
 //  * Persistent grid: one workgroup per CU slot, tiles taken round-robin; each 64-column
 //    block's registers are refilled with the next tile as soon as they are widened, so a
-//    tile of loads is always in flight, also across the reduction's barrier.
+//    tile of loads is always in flight, also across the reduction's barrier.  The loop
+//    has no branches around loads and no stores (logits wait in LDS until the end).
 #include "dh_internal.h"
 #include "launch.h"
 
 namespace dh {
 namespace {
 
-constexpr int kTileRows = 16;
 constexpr int kMaxWaves = 16;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
-constexpr int kNonTemporal = 2;          // cache policy bit: streamed once
+constexpr int kCachePolicy = 0;          // plain loads: the non-temporal hint measured ~15% slower
+constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
 
 struct GemvArgs {
     const uint8_t *w;       // weight bytes
@@ -84,12 +85,19 @@ __device__ inline void widen16(u32x4 q, float scale, bf16x8 &a0, bf16x8 &a1)
 // two 2^(b-127) for bytes 1..254.
 __device__ inline float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23); }
 
-template <int FMT, int KBW>
+// FULL: every wave's 64-column blocks lie inside the row (H a multiple of 64 and the
+// blocks split evenly over the waves), so no load needs a guard.
+// TR: 16-row MFMA groups per tile (a tile is 16 * TR head rows, inside one 32-row block
+// of scales); two groups double the bytes in flight and halve the barriers per byte.
+template <int FMT, int KBW, bool FULL, int TR>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
     constexpr int ES = FMT == DH_BF16 ? 2 : 1;   // bytes per weight element
-    __shared__ float red[2][kMaxWaves][4][kWave];
+    constexpr int TILE = 16 * TR;                // head rows per tile
+    constexpr int OUTS = TILE * 16;              // (head row, activation row) sums per tile
+    __shared__ float red[2][kMaxWaves][4 * TR][kWave];
+    extern __shared__ float stage[];             // [tile of this block][group][c][i]
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         Pack8 p0, p1;
         p0.q = u32x4{0u, 0u, 0u, 0u};
         p1.q = u32x4{0u, 0u, 0u, 0u};
-        if (rr < a.R && blk < a.nkb && k0 < H) {
+        if (rr < a.R && (FULL || (blk < a.nkb && k0 < H))) {
             const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)rr * H + k0);
             p0.q = px[0];
             p1.q = px[1];
@@ -117,121 +125,185 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         xb[kb][1] = p1.v;
     }
 
-    // One register slot per 64-column block.  A slot is refilled with the next tile's
-    // block as soon as its current contents have been widened, so a whole tile of loads
-    // stays in flight (through the reduction below) with a single set of registers.
-    u32x4 raw[KBW][RQ];
+    // One register slot per (group, 64-column block).  A slot is refilled with the next
+    // tile's block as soon as its current contents have been widened, so a whole tile of
+    // loads stays in flight (through the reduction below) with a single set of registers.
+    u32x4 raw[TR][KBW][RQ];
     uint32_t sc[KBW];
 
-    // Buffer loads: the descriptor (SGPRs) is rebased on each tile and bounded by the
-    // tile's existing rows, so rows past V read as zeros; a lane's offset within a tile is
-    // the same for every tile, and a block adds an immediate offset.
+    // Buffer loads: descriptors (SGPRs) are rebased on each tile, one per 16-row group, and
+    // bounded by the group's existing rows, so rows past V read as zeros (a descriptor of
+    // length 0 makes the loads after the last tile empty); a lane's offset within a group
+    // is the same for every tile, and a block adds an immediate offset.  No load sits under
+    // a branch, so the wait before each block is a fixed count of younger loads.
     const uint32_t wrow = (uint32_t)H * ES;
     const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KBW * 64 + 16 * g) * ES;
     const uint32_t soff = (uint32_t)(2 * wave * KBW + (g >> 1));
-    auto load_block = [&](__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t sr, int kb) {
+    auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], __amdgpu_buffer_rsrc_t sr,
+                          int kb) {
         const int blk = wave * KBW + kb;
-        if (blk < a.nkb && blk * 64 + 16 * g < H) {
+        if (FULL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
 #pragma unroll
-            for (int q = 0; q < RQ; q++)
-                raw[kb][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                    wr, woff + (uint32_t)(kb * 64 * ES + 16 * q), 0, kNonTemporal);
+            for (int r = 0; r < TR; r++)
+#pragma unroll
+                for (int q = 0; q < RQ; q++)
+                    raw[r][kb][q] = __builtin_amdgcn_raw_buffer_load_b128(
+                        wr[r], woff + (uint32_t)(kb * 64 * ES + 16 * q), 0, kCachePolicy);
             sc[kb] = FMT == DH_FP8_BLOCK32
                          ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, soff + 2 * kb, 0, 0)
                          : 127u;
         } else {
 #pragma unroll
-            for (int q = 0; q < RQ; q++)
-                raw[kb][q] = u32x4{0u, 0u, 0u, 0u};
+            for (int r = 0; r < TR; r++)
+#pragma unroll
+                for (int q = 0; q < RQ; q++)
+                    raw[r][kb][q] = u32x4{0u, 0u, 0u, 0u};
             sc[kb] = 127u;
         }
     };
-    auto wrsrc = [&](int tile) {
-        const int64_t v0 = (int64_t)tile * kTileRows;
-        const int64_t rows = V - v0 < kTileRows ? V - v0 : kTileRows;
-        return __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + v0 * wrow), (short)0,
-                                                 (int)(rows * wrow), kRsrcWord3);
-    };
-    auto srsrc = [&](int tile) {
-        const uint8_t *p = FMT == DH_FP8_BLOCK32 ? a.bscale + (int64_t)(tile >> 1) * (H >> 5)
-                                                 : a.w;
-        return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, H >> 5, kRsrcWord3);
+    auto rsrcs = [&](int tile, bool live, __amdgpu_buffer_rsrc_t (&wr)[TR],
+                     __amdgpu_buffer_rsrc_t &sr) {
+#pragma unroll
+        for (int r = 0; r < TR; r++) {
+            const int64_t v0 = (int64_t)tile * TILE + 16 * r;
+            int64_t rows = V - v0 < 16 ? V - v0 : 16;
+            rows = rows < 0 || !live ? 0 : rows;
+            wr[r] = __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + (rows ? v0 : 0) * wrow),
+                                                      (short)0, (int)(rows * wrow), kRsrcWord3);
+        }
+        const uint8_t *p = FMT == DH_FP8_BLOCK32
+                               ? a.bscale + (((int64_t)tile * TILE) >> 5) * (H >> 5)
+                               : a.w;
+        sr = __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, live ? (H >> 5) : 0,
+                                               kRsrcWord3);
     };
 
-    int tile = blockIdx.x;
-    if (tile >= a.ntiles)
-        return;
+    int tile = blockIdx.x;   // the launch keeps gridDim.x <= ntiles
     {
-        const __amdgpu_buffer_rsrc_t wr = wrsrc(tile), sr = srsrc(tile);
+        __amdgpu_buffer_rsrc_t wr[TR], sr;
+        rsrcs(tile, true, wr, sr);
 #pragma unroll
         for (int kb = 0; kb < KBW; kb++)
             load_block(wr, sr, kb);
     }
-    int buf = 0;
-    for (;;) {
+    int buf = 0, it = 0;
+    for (;; it++) {
         const int next = tile + gridDim.x;
         const bool more = next < a.ntiles;
-        const __amdgpu_buffer_rsrc_t wr = wrsrc(more ? next : tile);
-        const __amdgpu_buffer_rsrc_t sr = srsrc(more ? next : tile);
+        __amdgpu_buffer_rsrc_t wr[TR], sr;
+        rsrcs(more ? next : tile, more, wr, sr);
 
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[TR];
+#pragma unroll
+        for (int r = 0; r < TR; r++)
+            acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KBW; kb++) {
-            bf16x8 a0, a1;
-            if constexpr (FMT == DH_BF16) {
-                Pack8 p0, p1;
-                p0.q = raw[kb][0];
-                p1.q = raw[kb][RQ - 1];
-                a0 = p0.v;
-                a1 = p1.v;
-            } else {
-                widen16(raw[kb][0], FMT == DH_FP8_BLOCK32 ? e8m0_scale(sc[kb]) : 1.0f, a0, a1);
+            bf16x8 a0[TR], a1[TR];
+#pragma unroll
+            for (int r = 0; r < TR; r++) {
+                if constexpr (FMT == DH_BF16) {
+                    Pack8 p0, p1;
+                    p0.q = raw[r][kb][0];
+                    p1.q = raw[r][kb][RQ - 1];
+                    a0[r] = p0.v;
+                    a1[r] = p1.v;
+                } else {
+                    widen16(raw[r][kb][0], FMT == DH_FP8_BLOCK32 ? e8m0_scale(sc[kb]) : 1.0f,
+                            a0[r], a1[r]);
+                }
             }
-            if (more)
-                load_block(wr, sr, kb);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xb[kb][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xb[kb][1], acc, 0, 0, 0);
+            load_block(wr, sr, kb);
+            // keep the refill here: the scheduler would otherwise sink every load below the
+            // last MFMA, and the pipeline would drain once per tile
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < TR; r++) {
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[r], xb[kb][0], acc[r], 0, 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[r], xb[kb][1], acc[r], 0, 0, 0);
+            }
         }
 
-        // acc[j] of lane l is the partial sum of head row 4*(l/16)+j of the tile for
-        // activation row l%16 over this wave's H-slice.
+        // acc[r][j] of lane l is the partial sum of head row 16r + 4*(l/16) + j of the tile
+        // for activation row l%16 over this wave's H-slice.  The waves' partials are summed
+        // in wave order and kept in LDS until the end, so the loop issues no stores.
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            red[buf][wave][j][lane] = acc[j];
+        for (int r = 0; r < TR; r++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                red[buf][wave][4 * r + j][lane] = acc[r][j];
         __syncthreads();
-        for (int o = threadIdx.x; o < kTileRows * 16; o += blockDim.x) {
-            const int c = o >> 4;                  // activation row
-            const int i = o & 15;                  // head row within the tile
+        for (int o = threadIdx.x; o < OUTS; o += blockDim.x) {
+            const int r = o >> 8;                  // row group
+            const int c = (o >> 4) & 15;           // activation row
+            const int i = o & 15;                  // head row within the group
             const int src = c + 16 * (i >> 2);
-            const int j = i & 3;
+            const int j = 4 * r + (i & 3);
             float s = 0.f;
             for (int w = 0; w < nw; w++)
                 s += red[buf][w][j][src];
-            const int64_t v = (int64_t)tile * kTileRows + i;
-            if (c < a.R && v < V) {
-                if (FMT == DH_FP8_ROW)
-                    s *= a.rscale[v];
-                a.logits[(int64_t)c * V + v] = s;
-            }
+            stage[it * OUTS + o] = s;
         }
         buf ^= 1;
         if (!more)
             break;
         tile = next;
     }
+    __syncthreads();
+    // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.
+    const int per_tile = TR * a.R * 16;
+    const int n = (it + 1) * per_tile;
+    for (int o = threadIdx.x; o < n; o += blockDim.x) {
+        const int t = o / per_tile;
+        const int rem = o - t * per_tile;
+        const int r = rem / (a.R * 16);
+        const int rc = rem - r * (a.R * 16);
+        const int c = rc >> 4, i = rc & 15;
+        const int64_t v = (int64_t)(blockIdx.x + t * gridDim.x) * TILE + 16 * r + i;
+        if (v < V) {
+            float s = stage[t * OUTS + r * 256 + c * 16 + i];
+            if (FMT == DH_FP8_ROW)
+                s *= a.rscale[v];
+            a.logits[(int64_t)c * V + v] = s;
+        }
+    }
+}
+
+template <int FMT, int KBW, bool FULL, int TR>
+hipError_t run(GemvArgs a, hipStream_t stream)
+{
+    static int occ_cache[kMaxWaves + 1];
+    static int lds_set;
+    const int nw = (a.nkb + KBW - 1) / KBW;
+    const int block = nw * kWave;
+    auto kern = gemv_kernel<FMT, KBW, FULL, TR>;
+    if (!__atomic_load_n(&lds_set, __ATOMIC_RELAXED)) {
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kMaxStageBytes);
+        __atomic_store_n(&lds_set, 1, __ATOMIC_RELAXED);
+    }
+    a.ntiles = (int)((a.V + 16 * TR - 1) / (16 * TR));
+    const int occ = occupancy(kern, block, occ_cache[nw]);
+    int64_t grid = (int64_t)device_cus() * occ;
+    // each block keeps its tiles' logits in LDS: at most kMaxStageBytes of them
+    const int64_t max_per = kMaxStageBytes / (TR * 256 * (int)sizeof(float));
+    const int64_t min_grid = (a.ntiles + max_per - 1) / max_per;
+    if (grid < min_grid)
+        grid = min_grid;
+    if (grid > a.ntiles)
+        grid = a.ntiles;
+    const int64_t per = (a.ntiles + grid - 1) / grid;
+    return launch(kern, dim3((unsigned)grid), dim3(block),
+                  (size_t)per * TR * 256 * sizeof(float), stream, a);
 }
 
 template <int FMT, int KBW>
-hipError_t run(const GemvArgs &a, hipStream_t stream)
+hipError_t run_kbw(const GemvArgs &a, hipStream_t stream)
 {
-    static int occ_cache[kMaxWaves + 1];
-    const int nw = (a.nkb + KBW - 1) / KBW;
-    const int block = nw * kWave;
-    const int occ = occupancy(gemv_kernel<FMT, KBW>, block, occ_cache[nw]);
-    int64_t grid = (int64_t)device_cus() * occ;
-    if (grid > a.ntiles)
-        grid = a.ntiles;
-    return launch(gemv_kernel<FMT, KBW>, dim3((unsigned)grid), dim3(block), 0, stream, a);
+    constexpr int TR = 1;   // two groups measured slower: the loop is not latency-bound
+    if (a.H % 64 == 0 && a.nkb % KBW == 0)
+        return run<FMT, KBW, true, TR>(a, stream);
+    return run<FMT, KBW, false, TR>(a, stream);
 }
 
 template <int FMT>
@@ -239,14 +311,14 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
 {
     const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;
     switch (kbw) {
-    case 1: return run<FMT, 1>(a, stream);
-    case 2: return run<FMT, 2>(a, stream);
-    case 3: return run<FMT, 3>(a, stream);
-    case 4: return run<FMT, 4>(a, stream);
-    case 5: return run<FMT, 5>(a, stream);
-    case 6: return run<FMT, 6>(a, stream);
-    case 7: return run<FMT, 7>(a, stream);
-    case 8: return run<FMT, 8>(a, stream);
+    case 1: return run_kbw<FMT, 1>(a, stream);
+    case 2: return run_kbw<FMT, 2>(a, stream);
+    case 3: return run_kbw<FMT, 3>(a, stream);
+    case 4: return run_kbw<FMT, 4>(a, stream);
+    case 5: return run_kbw<FMT, 5>(a, stream);
+    case 6: return run_kbw<FMT, 6>(a, stream);
+    case 7: return run_kbw<FMT, 7>(a, stream);
+    case 8: return run_kbw<FMT, 8>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -266,7 +338,7 @@ hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *
     a.V = head.vocab;
     a.H = (int)head.hidden;
     a.R = rows;
-    a.ntiles = (int)((head.vocab + kTileRows - 1) / kTileRows);
+    a.ntiles = 0;   // set per tile height by run()
     a.nkb = (int)((head.hidden + 63) / 64);
     switch (head.format) {
     case DH_BF16: return run_fmt<DH_BF16>(a, stream);

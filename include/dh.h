@@ -76,7 +76,8 @@ typedef struct dh_head {
 #define DH_MAX_ROWS 16
 #define DH_MAX_K 512
 #define DH_MAX_HIDDEN 8192
-#define DH_MAX_VOCAB 262144
+#define DH_MAX_VOCAB 262144        /* dh_topk / dh_draft */
+#define DH_MAX_GEMV_VOCAB 33554432 /* dh_gemv, dh_rescore: 2^25 rows */
 
 /* dh_gemv -- logits[r][v] = sum_h x[r][h] * w[v][h] for r < rows, v < V, in fp32.
  * [TFE] commit notes: the own GEMV for up to 16 rows with fp32 output; 'What this changes':

@@ -16,18 +16,17 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 constexpr int kWave = 64;
 
 // Top-k layout: a row is cut into chunks of kChunk logits; pass 1 keeps each chunk's best
-// min(k, chunk) entries, pass 2 merges a row's lists.  Pass 2 holds up to kMergeSlots
-// (chunks * k) list slots per row in registers.
-constexpr int kChunk = 4096;
-constexpr int kP1Threads = 256;
-constexpr int kP1PerThread = kChunk / kP1Threads;   // 16
+// min(k, chunk) entries, pass 2 merges a row's lists (at most kMergeSlots = chunks * k keys,
+// held in registers).
+constexpr int kChunk = 8192;
+constexpr int kP1Threads = 512;
 constexpr int kMergeThreads = 1024;
-constexpr int kMergePerThread = 32;
-constexpr int kMergeSlots = kMergeThreads * kMergePerThread;   // 32768
+constexpr int kMergeSlots = 16384;   // (262144 / kChunk) * 512
 
 inline int64_t topk_chunks(int64_t vocab) { return (vocab + kChunk - 1) / kChunk; }
 
-// Workspace layout of the top-k (offsets in bytes, each 256-byte aligned).
+// Workspace layout of the top-k (offsets in bytes, each 256-byte aligned): the chunk lists
+// of 64-bit keys, [rows][chunks][k].
 struct TopkWs {
     size_t val_off, id_off, cnt_off, bytes;
 };

@@ -13,8 +13,10 @@ sweep (1/5/10/15/16 rows) per entry point, the bf16 head, the two-stage head (FP
 each launch on the launching stream) and the CPU oracle timed on the host's cores.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,6 +27,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 NCOPY = 3
+# HBM traffic of the GEMV launch, from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
+# calibrated on a plain copy kernel; valid only for the kernel source it was taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_fp8_block32_R16_H5120_V129280_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "few_row_vocab_amd", "csrc", f)
+                  for f in ("gemv.hip", "dh_internal.h", "launch.h")]
 
 
 def log(*a):
@@ -35,6 +42,62 @@ def stats_us(times_ms):
     t = np.sort(np.asarray(times_ms)) * 1e3
     return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
             "p90": float(np.percentile(t, 90)), "n": int(t.size)}
+
+
+def gemv_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per GEMV launch from the committed counter summary, or None when there is
+    none or when the kernel's source has changed since the counters were taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"^source_hash:\s*(\S+)", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    if not src or not val or src.group(1) != gemv_source_hash():
+        return None
+    return int(val.group(1))
+
+
+def gemv_kernel_name(fmt_code, H):
+    """The template instance the library launches for this head width (its rule for the
+    per-wave K blocks and the unguarded tile loop), as rocprofv3 names it."""
+    nkb = (H + 63) // 64
+    kbw = -(-nkb // 16)
+    full = H % 64 == 0 and nkb % kbw == 0
+    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1>"
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, run under the same counters as the
+    GEMV to turn FETCH_SIZE / WRITE_SIZE into bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes 3 times")
+
+
+def copy_ceiling(torch):
+    """A practical bandwidth figure for the same device: torch's 1 GiB device copy
+    (read + write bytes over its median time)."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = stats_us(timed(lambda i: dst.copy_(src), 20))
+    del src, dst
+    return {"bytes_moved": 2 * n, "median_us": round(t["median"], 1),
+            "GBps": round(2 * n / (t["median"] * 1e-6) / 1e9, 1)}
 
 
 def algorithmic_bytes(fmt, V, H, R):
@@ -51,11 +114,17 @@ def main():
     ap.add_argument("--calls", type=int, default=50, help="timed calls per sweep entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="main step only (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the projection's "
-              "multi-GPU split is a design note, not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the projection "
+              "shards by vocabulary rows across GPUs, which is a design note here, not "
+              "something this benchmark runs.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import synth
@@ -137,13 +206,16 @@ def main():
                    "head_copies_rotated": NCOPY, "step_bytes": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "kernel": "gemv_kernel<FP8_BLOCK32, 5>",
-                     "kernel_us": round(gemv_avg_ms * 1e3, 2)},
+                     "traffic": measured_traffic(),
+                     "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H),
+                     "kernel_us": round(gemv_avg_ms * 1e3, 2),
+                     "algorithmic_bytes": step_bytes, "kernel_source": gemv_source_hash()},
         "quantize_fp8_block32_ms": round(quant_ms, 3),
     }
 
     if not args.quick:
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
+        out["copy_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
     print(json.dumps(out), flush=True)
@@ -213,23 +285,41 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
 
 def cpu_baseline(w, x, V, H, R, K):
     """The oracle as it stands (C, double precision, OpenMP over vocabulary rows) on the
-    host's cores: one full step (GEMV + top-k) over the first `rows` vocabulary rows of the
-    same head; the FP8 codes come from the oracle's own quantizer (not timed)."""
+    host's cores: the whole step (GEMV of all 16 rows over the full FP8 head, then the
+    top-k) repeated until about 10 s have passed, plus one GEMV on a single thread over
+    the first 8192 vocabulary rows.  The FP8 codes come from the oracle's own quantizer
+    (not timed)."""
     import oracle
-    S = min(V, 32768)
     t0 = time.time()
-    codes, scales = oracle.quant_block32(w[:S])
+    codes, scales = oracle.quant_block32(w)
     tq = time.time() - t0
+    times = []
+    while not times or (sum(times) < 10.0 and len(times) < 20):
+        t0 = time.time()
+        lg = oracle.gemv(oracle.FMT_FP8_BLOCK32, codes, scales, x)
+        oracle.topk(lg, K)
+        times.append(time.time() - t0)
+    dt = float(np.median(times))
+    b = algorithmic_bytes("fp8_block32", V, H, R)
+    nt = oracle.threads()
+    S = 8192
+    oracle.threads(1)
     t0 = time.time()
-    lg = oracle.gemv(oracle.FMT_FP8_BLOCK32, codes, scales, x)
-    oracle.topk(lg, K)
-    dt = time.time() - t0
-    b = algorithmic_bytes("fp8_block32", S, H, R)
-    log(f"cpu oracle: {S} vocab rows x {R} rows in {dt:.2f}s ({oracle.threads()} threads)")
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
-            "kind": "oracle", "seconds": round(dt, 3), "quantize_seconds": round(tq, 3),
-            "sample": f"first {S} of {V} vocabulary rows of the FP8 block head, {R} rows, "
-                      f"GEMV + top-{K}, once; GB/s over the sample's algorithmic bytes"}
+    oracle.gemv(oracle.FMT_FP8_BLOCK32, codes[:S], scales[:S // 32], x)
+    d1 = time.time() - t0
+    oracle.threads(nt)
+    b1 = algorithmic_bytes("fp8_block32", S, H, R)
+    log(f"cpu oracle: full step {dt:.2f}s median of {len(times)} on {nt} threads; "
+        f"1 thread: {S} vocab rows in {d1:.2f}s")
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": nt,
+            "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": len(times),
+            "quantize_seconds": round(tq, 3),
+            "single_thread": {"value": round(b1 / d1 / 1e9, 4), "unit": "GB/s",
+                              "seconds": round(d1, 3),
+                              "sample": f"GEMV only, first {S} vocabulary rows, {R} rows"},
+            "sample": f"the full step (GEMV over all {V} vocabulary rows of the FP8 block "
+                      f"head for {R} rows, then top-{K}), {len(times)} times, median; GB/s "
+                      f"over the step's algorithmic bytes"}
 
 
 if __name__ == "__main__":

@@ -36,6 +36,7 @@ constexpr int kMaxWaves = 16;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 constexpr int kCachePolicy = 0;          // plain loads: the non-temporal hint measured ~15% slower
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
+constexpr int kMaxDevices = 64;
 
 struct GemvArgs {
     const uint8_t *w;       // weight bytes
@@ -273,14 +274,22 @@ template <int FMT, int KBW, bool FULL, int TR>
 hipError_t run(GemvArgs a, hipStream_t stream)
 {
     static int occ_cache[kMaxWaves + 1];
-    static int lds_set;
+    static int lds_set[kMaxDevices];               // per device: the LDS limit has been raised
     const int nw = (a.nkb + KBW - 1) / KBW;
     const int block = nw * kWave;
     auto kern = gemv_kernel<FMT, KBW, FULL, TR>;
-    if (!__atomic_load_n(&lds_set, __ATOMIC_RELAXED)) {
-        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kMaxStageBytes);
-        __atomic_store_n(&lds_set, 1, __ATOMIC_RELAXED);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    if (!__atomic_load_n(&lds_set[dev], __ATOMIC_RELAXED)) {
+        e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kMaxStageBytes);
+        if (e != hipSuccess)
+            return e;
+        __atomic_store_n(&lds_set[dev], 1, __ATOMIC_RELAXED);
     }
     a.ntiles = (int)((a.V + 16 * TR - 1) / (16 * TR));
     const int occ = occupancy(kern, block, occ_cache[nw]);

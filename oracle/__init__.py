@@ -56,7 +56,7 @@ def lib():
         L.orc_quant_block32.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p,
                                         c.c_void_p]
         L.orc_threads.restype = c.c_int
-        L.orc_threads.argtypes = []
+        L.orc_threads.argtypes = [c.c_int]
         _lib = L
     return _lib
 
@@ -200,5 +200,6 @@ def quant_block32(w_bf16):
     return codes, scales
 
 
-def threads():
-    return lib().orc_threads()
+def threads(n=0):
+    """Threads the oracle's loops use; n > 0 sets that number first."""
+    return lib().orc_threads(n)

@@ -330,13 +330,17 @@ void orc_quant_block32(const uint16_t *w, int64_t V, int64_t H, uint8_t *codes,
     }
 }
 
-/* Number of threads OpenMP will use (for reporting the CPU baseline). */
-int orc_threads(void)
+/* Number of threads OpenMP will use (for reporting the CPU baseline); n > 0 sets it first. */
+int orc_threads(int n)
 {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);
+    extern void omp_set_num_threads(int);
+    if (n > 0)
+        omp_set_num_threads(n);
     return omp_get_max_threads();
 #else
+    (void)n;
     return 1;
 #endif
 }

@@ -22,3 +22,11 @@ def _announce(request):
     # Name every test before it starts, so a run that dies mid-test still says which one.
     print(f"\n[start] {request.node.nodeid}", flush=True)
     yield
+
+
+def pytest_terminal_summary(terminalreporter):
+    mod = sys.modules.get("tests.parity") or sys.modules.get("parity")
+    if mod is not None and mod.WORST["what"]:
+        terminalreporter.write_line(
+            f"largest logit error relative to its tolerance: {mod.WORST['ratio']:.3e} "
+            f"({mod.WORST['what']})")

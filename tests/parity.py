@@ -26,6 +26,11 @@ def eligible(v):
     return ~np.isnan(v) & (v != -np.inf)
 
 
+# The largest observed |gpu - oracle| / tol over every checked row of the session (reported by
+# conftest.py at the end of the run).
+WORST = {"ratio": 0.0, "what": None}
+
+
 def check_logits(gpu, orc, rel=1e-3, what="logits"):
     """Asserts the logit rule; returns the per-row tolerances."""
     gpu = np.asarray(gpu, np.float32)
@@ -47,6 +52,9 @@ def check_logits(gpu, orc, rel=1e-3, what="logits"):
             err = np.abs(g[fin].astype(np.float64) - o[fin].astype(np.float64))
             worst = float(err.max())
             assert worst <= tol, f"{what} row {r}: max abs err {worst:.3e} > tol {tol:.3e}"
+            if tol > 0 and worst / tol > WORST["ratio"]:
+                WORST["ratio"] = worst / tol
+                WORST["what"] = f"{what} row {r}: {worst:.3e} of tol {tol:.3e}"
     return np.array(tols)
 
 

@@ -15,15 +15,27 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 
 constexpr int kWave = 64;
 
-// Top-k layout: a row is cut into chunks of kChunk logits; pass 1 keeps each chunk's best
-// min(k, chunk) entries, pass 2 merges a row's lists (at most kMergeSlots = chunks * k keys,
-// held in registers).
-constexpr int kChunk = 8192;
-constexpr int kP1Threads = 512;
+// Top-k layout: a row is cut into chunks; pass 1 keeps each chunk's best min(k, chunk)
+// entries, pass 2 merges a row's lists (chunks * k keys, at most kMergeSlots).  The chunk is
+// the smallest of 2048, 4096, 8192 logits whose lists fit: small chunks spread pass 1 over
+// more compute units.
+constexpr int kMaxChunk = 8192;
+constexpr int kP1PerThread = 8;      // logits a pass-1 thread holds
 constexpr int kMergeThreads = 1024;
-constexpr int kMergeSlots = 16384;   // (262144 / kChunk) * 512
+constexpr int kMergeSlots = 16384;   // (262144 / kMaxChunk) * 512
 
-inline int64_t topk_chunks(int64_t vocab) { return (vocab + kChunk - 1) / kChunk; }
+inline int topk_chunk(int64_t vocab, int k)
+{
+    for (int c = 2048; c < kMaxChunk; c *= 2)
+        if ((vocab + c - 1) / c * k <= kMergeSlots)
+            return c;
+    return kMaxChunk;
+}
+inline int64_t topk_chunks(int64_t vocab, int k)
+{
+    const int c = topk_chunk(vocab, k);
+    return (vocab + c - 1) / c;
+}
 
 // Workspace layout of the top-k (offsets in bytes, each 256-byte aligned): the chunk lists
 // of 64-bit keys, [rows][chunks][k].
@@ -38,6 +50,7 @@ hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *
                        hipStream_t stream);
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int32_t *ids,
                        float *vals, int32_t *argmax, void *ws, hipStream_t stream);
+
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,
                           float *exact, int32_t *draft, hipStream_t stream);

@@ -260,3 +260,40 @@ def test_draft_composition_and_parity(fmt, two):
     etol = check_logits(host(out["exact"]), oe, what="exact")
     for r in range(R):
         check_topk_winner(host(out["draft"])[r], oe[r], gi[r], etol[r], od[r])
+
+
+@pytest.mark.parametrize("fmt,V,H,R,k", [
+    ("block", 37, 32, 16, 1), ("block", 37, 32, 16, 31), ("bf16", 70, 64, 4, 64),
+    ("row", 4133, 1376, 5, 22), ("block", 20000, 256, 3, 64), ("bf16", 20000, 256, 16, 8),
+    ("block", 50000, 1024, 16, 64), ("row", 9001, 7168, 2, 33)])
+def test_draft_equals_topk_of_logits(fmt, V, H, R, k):
+    """dh_draft's ids, values and drafts equal dh_topk run on its logits, bit for bit, also
+    with exact ties (repeated head rows and coarse activations), a zero row (ids 0..k-1), a
+    NaN row (all pads) and +-inf rows."""
+    need_gpu()
+    rng = np.random.default_rng(V + H + R + k)
+    w = synth.random_head(V, H, seed=V + 3, std=0.02)
+    for s in range(0, V - 40, max(V // 7, 41)):
+        w[s + 1:s + 33] = w[s]                     # 33 identical rows: ties across ids
+    x = synth.to_bf16_bits(rng.integers(-2, 3, (R, H)).astype(np.float32) / 8)
+    if R > 1:
+        x[1] = 0                                   # every logit +-0: ids 0..k-1
+    if R > 2:
+        x[2, 7] = 0x7FC0                           # NaN: every logit NaN, all pads
+    if R > 3:
+        x[3, 0:32] = synth.to_bf16_bits(np.full(32, 3e38, np.float32))
+    gh, _ = make_heads(fmt, w)
+    xd = dev_u16(x)
+    say(f"draft vs topk {fmt} V={V} H={H} R={R} k={k}")
+    out = dh.draft(gh, xd, k, keep_logits=True)
+    ids, vals, am = dh.topk(out["logits"], k)
+    lg = dh.gemv(gh, xd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["logits"]).view(np.uint32), host(lg).view(np.uint32))
+    assert np.array_equal(host(out["ids"]), host(ids))
+    assert np.array_equal(host(out["vals"]).view(np.uint32), host(vals).view(np.uint32))
+    assert np.array_equal(host(out["draft"]), host(am))
+    if R > 2:
+        assert np.all(host(out["ids"])[2] == 0) and np.all(host(out["vals"])[2] == -np.inf)
+    if R > 1:
+        assert np.array_equal(host(out["ids"])[1], np.arange(k))

@@ -130,18 +130,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     // tile's block as soon as its current contents have been widened, so a whole tile of
     // loads stays in flight (through the reduction below) with a single set of registers.
     u32x4 raw[TR][KBW][RQ];
-    uint32_t sc[KBW];
 
     // Buffer loads: descriptors (SGPRs) are rebased on each tile, one per 16-row group, and
     // bounded by the group's existing rows, so rows past V read as zeros (a descriptor of
     // length 0 makes the loads after the last tile empty); a lane's offset within a group
-    // is the same for every tile, and a block adds an immediate offset.  No load sits under
+    // is the same for every tile, and a block adds a constant offset.  No load sits under
     // a branch, so the wait before each block is a fixed count of younger loads.
     const uint32_t wrow = (uint32_t)H * ES;
     const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KBW * 64 + 16 * g) * ES;
-    const uint32_t soff = (uint32_t)(2 * wave * KBW + (g >> 1));
-    auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], __amdgpu_buffer_rsrc_t sr,
-                          int kb) {
+    const uint32_t sbase = (uint32_t)(2 * wave * KBW);
+    auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], int kb) {
         const int blk = wave * KBW + kb;
         if (FULL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
 #pragma unroll
@@ -149,18 +147,23 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
 #pragma unroll
                 for (int q = 0; q < RQ; q++)
                     raw[r][kb][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                        wr[r], woff + (uint32_t)(kb * 64 * ES + 16 * q), 0, kCachePolicy);
-            sc[kb] = FMT == DH_FP8_BLOCK32
-                         ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, soff + 2 * kb, 0, 0)
-                         : 127u;
+                        wr[r], woff, kb * 64 * ES + 16 * q, kCachePolicy);
         } else {
 #pragma unroll
             for (int r = 0; r < TR; r++)
 #pragma unroll
                 for (int q = 0; q < RQ; q++)
                     raw[r][kb][q] = u32x4{0u, 0u, 0u, 0u};
-            sc[kb] = 127u;
         }
+    };
+    // E8M0 scales of a tile: lane i loads byte i of this wave's 2 * KBW scale bytes (one
+    // load per tile instead of one per block); a block's scale is then read from lane
+    // 2 * kb (lanes with g < 2) or 2 * kb + 1 (the second 32 columns).  Bytes past the row
+    // read as 0, which only meet zero codes.
+    auto load_scales = [&](__amdgpu_buffer_rsrc_t sr) -> uint32_t {
+        return FMT == DH_FP8_BLOCK32
+                   ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(sr, sbase + lane, 0, 0)
+                   : 0u;
     };
     auto rsrcs = [&](int tile, bool live, __amdgpu_buffer_rsrc_t (&wr)[TR],
                      __amdgpu_buffer_rsrc_t &sr) {
@@ -180,12 +183,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     };
 
     int tile = blockIdx.x;   // the launch keeps gridDim.x <= ntiles
+    uint32_t sbytes;
     {
         __amdgpu_buffer_rsrc_t wr[TR], sr;
         rsrcs(tile, true, wr, sr);
+        sbytes = load_scales(sr);
 #pragma unroll
         for (int kb = 0; kb < KBW; kb++)
-            load_block(wr, sr, kb);
+            load_block(wr, kb);
     }
     int buf = 0, it = 0;
     for (;; it++) {
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         const bool more = next < a.ntiles;
         __amdgpu_buffer_rsrc_t wr[TR], sr;
         rsrcs(more ? next : tile, more, wr, sr);
+        const uint32_t sbytes_next = load_scales(sr);
 
         f32x4 acc[TR];
 #pragma unroll
@@ -210,11 +216,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
                     a0[r] = p0.v;
                     a1[r] = p1.v;
                 } else {
-                    widen16(raw[r][kb][0], FMT == DH_FP8_BLOCK32 ? e8m0_scale(sc[kb]) : 1.0f,
-                            a0[r], a1[r]);
+                    float scale = 1.0f;
+                    if constexpr (FMT == DH_FP8_BLOCK32) {
+                        const uint32_t lo = __builtin_amdgcn_readlane(sbytes, 2 * kb);
+                        const uint32_t hi = __builtin_amdgcn_readlane(sbytes, 2 * kb + 1);
+                        scale = e8m0_scale(g < 2 ? lo : hi);
+                    }
+                    widen16(raw[r][kb][0], scale, a0[r], a1[r]);
                 }
             }
-            load_block(wr, sr, kb);
+            load_block(wr, kb);
             // keep the refill here: the scheduler would otherwise sink every load below the
             // last MFMA, and the pipeline would drain once per tile
             __builtin_amdgcn_sched_barrier(0);
@@ -249,6 +260,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         if (!more)
             break;
         tile = next;
+        sbytes = sbytes_next;
     }
     __syncthreads();
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.

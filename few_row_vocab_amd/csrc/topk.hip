@@ -15,8 +15,8 @@
 // numeric order is exactly the ordering above, so ties need no special case.  Ineligible
 // entries get the key 0.
 //  * Pass 1, a workgroup per (row, chunk of 2048 to 8192 logits): a radix select over the chunk's keys
-//    (most significant digit first, histograms in LDS, stopping as soon as the boundary
-//    digit's bin is taken whole) finds the chunk's best min(k, n); they go to the workspace
+//    (most significant byte first, histograms in LDS, stopping as soon as the boundary
+//    byte's bin is taken whole) finds the chunk's best min(k, n); they go to the workspace
 //    in any order, the rest of the chunk's k slots as zeros.  Any entry of the row's top-k
 //    is in its chunk's top-k.
 //  * Pass 2, a workgroup per row: the same select over the row's chunk lists keeps k; each
@@ -37,22 +37,12 @@ namespace {
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
-// Radix select over 64-bit keys, most significant digit first.  Digit widths: four of 10
-// bits, then three of 8 (64 bits in at most seven rounds).  Each round has a histogram of its
-// own (all cleared once at the start), so a round needs one barrier: after it every wave scans
-// the whole histogram itself and reaches the same decision, and no wave writes what another
-// may still be reading.
-constexpr int kRounds = 7;
-__host__ __device__ constexpr int digit_bits(int round) { return round < 4 ? 10 : 8; }
-__host__ __device__ constexpr int digit_shift(int round)
-{
-    return round < 4 ? 54 - 10 * round : 16 - 8 * (round - 4);
-}
-constexpr int kHistWords = 4 * 1024 + 3 * 256;
-__host__ __device__ constexpr int hist_offset(int round)
-{
-    return round < 4 ? round * 1024 : 4096 + (round - 4) * 256;
-}
+// Radix select over 64-bit keys, most significant byte first (eight rounds at most).  Each
+// round has a histogram of 256 bins of its own (all cleared once at the start), so a round
+// needs one barrier: after it every wave scans the whole histogram itself (four bins a lane)
+// and reaches the same decision, and no wave writes what another may still be reading.
+constexpr int kRounds = 8;
+constexpr int kHistWords = kRounds * 256;
 
 struct SelectLds {
     uint32_t hist[kHistWords];
@@ -75,34 +65,30 @@ template <int N, int NT>
 __device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds &sh,
                                uint32_t &total)
 {
-    // round 0 takes every non-zero key: its digit is the top 10 bits of the high word
+    // round 0 takes every non-zero key: its digit is the top byte
 #pragma unroll
     for (int i = 0; i < N; i++)
         if (key[i] != 0)
-            atomicAdd(&sh.hist[(uint32_t)(key[i] >> 54)], 1u);
+            atomicAdd(&sh.hist[(uint32_t)(key[i] >> 56)], 1u);
     __syncthreads();
     uint32_t d, above, count;
-    total = locate<1024>(sh.hist, k, d, above, count);
+    total = locate<256>(sh.hist, k, d, above, count);
     if (total <= k)
         return 1;                                  // every non-zero key
-    uint64_t prefix = (uint64_t)d << 54, mask = 0x3ffull << 54;
+    uint64_t prefix = (uint64_t)d << 56, mask = 0xffull << 56;
     uint32_t rem = k - above;
 #pragma unroll 1
     for (int round = 1; round < kRounds && count != rem; round++) {
-        const int shift = digit_shift(round);
-        const uint32_t dmask = (1u << digit_bits(round)) - 1u;
-        uint32_t *h = sh.hist + hist_offset(round);
+        const int shift = 56 - 8 * round;
+        uint32_t *h = sh.hist + 256 * round;
 #pragma unroll
         for (int i = 0; i < N; i++)
             if ((key[i] & mask) == prefix)         // prefix != 0, so key != 0
-                atomicAdd(&h[(uint32_t)(key[i] >> shift) & dmask], 1u);
+                atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
         __syncthreads();
-        if (round < 4)
-            locate<1024>(h, rem, d, above, count);
-        else
-            locate<256>(h, rem, d, above, count);
+        locate<256>(h, rem, d, above, count);
         prefix |= (uint64_t)d << shift;
-        mask |= (uint64_t)dmask << shift;
+        mask |= 0xffull << shift;
         rem -= above;
     }
     return prefix;                                 // the boundary bin is taken whole
@@ -158,6 +144,19 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         out[s] = 0ull;                             // empty slots
 }
 
+// One step of a descending bitonic network on the key x held by slot i (a lane): the
+// partner is slot i ^ stride, and in a block of `size` whose size bit is clear the lower
+// slot keeps the larger key.
+__device__ inline uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size, int stride)
+{
+    const bool lower = (i & stride) == 0, desc = (i & size) == 0;
+    const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
+    return lower == desc ? hi : lo;
+}
+
+// Up to this many survivors the merge ranks by counting; above, by sorted runs of 64.
+constexpr int kCountMax = 128;
+
 // Pass 2: one workgroup per row; a thread holds PER of the row's nchunks * k list slots
 // (PER * kMergeThreads >= nchunks * k).
 template <int PER>
@@ -206,17 +205,65 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
     int32_t *rid = ids + (int64_t)r * k;
     float *rval = vals + (int64_t)r * k;
     const int i = threadIdx.x;
-    if (i < kk) {
-        const uint64_t x = sel[i];
-        uint32_t rank = 0;
-        int j = 0;
-        for (; j + 2 <= kk; j += 2) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(&sel[j]);
-            rank += (((uint64_t)q.y << 32) | q.x) > x;
-            rank += (((uint64_t)q.w << 32) | q.z) > x;
+    uint32_t rank = 0;
+    uint64_t x = 0;
+    if (kk <= kCountMax) {
+        // few survivors: count directly
+        if (i < kk) {
+            x = sel[i];
+            int j = 0;
+            for (; j + 2 <= kk; j += 2) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(&sel[j]);
+                rank += (((uint64_t)q.y << 32) | q.x) > x;
+                rank += (((uint64_t)q.w << 32) | q.z) > x;
+            }
+            if (j < kk)
+                rank += sel[j] > x;
         }
-        if (j < kk)
-            rank += sel[j] > x;
+    } else {
+        // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then
+        // a survivor's rank is its place in its run plus, for each other run, the number of
+        // that run's keys above it (a binary search)
+        const int nruns = (kk + 63) >> 6;
+        const int w = i >> 6, l = i & 63;
+        if (w < nruns) {
+            x = i < kk ? sel[i] : 0ull;
+            for (int size = 2; size <= 64; size <<= 1)
+                for (int stride = size >> 1; stride > 0; stride >>= 1)
+                    x = bitonic_step(x, __shfl_xor(x, stride), l, size, stride);
+        }
+        __syncthreads();
+        if (w < nruns)
+            sel[i] = x;
+        __syncthreads();
+        if (w < nruns && x != 0) {
+            // the searches of all runs advance together (independent LDS reads per step);
+            // run q keeps run[0..lo) > x >= run[hi..64), and 7 halvings settle 64 keys
+            constexpr int kMaxRuns = DH_MAX_K / 64;
+            int lo[kMaxRuns], hi[kMaxRuns];
+#pragma unroll
+            for (int q = 0; q < kMaxRuns; q++) {
+                lo[q] = 0;
+                hi[q] = q < nruns && q != w ? 64 : 0;
+            }
+#pragma unroll
+            for (int step = 0; step < 7; step++)
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++)
+                    if (lo[q] < hi[q]) {
+                        const int mid = (lo[q] + hi[q]) >> 1;
+                        if (sel[64 * q + mid] > x)
+                            lo[q] = mid + 1;
+                        else
+                            hi[q] = mid;
+                    }
+            rank = (uint32_t)l;
+#pragma unroll
+            for (int q = 0; q < kMaxRuns; q++)
+                rank += (uint32_t)lo[q];
+        }
+    }
+    if (x != 0 && rank < (uint32_t)kk) {
         const uint32_t id = key_id(x);
         rid[rank] = (int32_t)id;
         rval[rank] = image_value(x, logits + (int64_t)r * V + id);

@@ -156,12 +156,12 @@ def _planted(R, V, seed):
             r[rng.random(V) < 0.3] = np.nan
         elif kind == "straddle":              # equal values on both sides of chunk edges
             r = rng.standard_normal(V).astype(np.float32) - 10
-            for e in range(4096, V, 4096):
+            for e in range(2048, V, 2048):     # every chunk size is a multiple of 2048
                 r[max(0, e - 300):e + 300] = 5.0
         else:                                  # every top value inside one chunk
             r = rng.standard_normal(V).astype(np.float32) - 10
-            c0 = (V // 2) // 4096 * 4096
-            r[c0:min(V, c0 + 4096)] += 20
+            c0 = (V // 2) // 2048 * 2048
+            r[c0:min(V, c0 + 2048)] += 20
         rows.append(r)
     return np.stack(rows)
 
@@ -182,6 +182,22 @@ def test_topk_bit_exact(V, k):
     assert np.array_equal(gi, oi)
     assert np.array_equal(gv.view(np.uint32), ov.view(np.uint32))
     assert np.array_equal(host(am), oi[:, 0])
+
+
+def test_topk_prefix_property():
+    """The top-k1 list is the first k1 slots of the top-k2 list (k1 < k2), pads included,
+    across every chunk size the top-k picks (k decides it)."""
+    need_gpu()
+    logits = _planted(16, 40000, seed=77)
+    d = dev(logits)
+    lists = {k: [host(t) for t in dh.topk(d, k)] for k in (1, 7, 64, 65, 300, 512)}
+    ks = sorted(lists)
+    for k1, k2 in zip(ks, ks[1:]):
+        i1, v1, a1 = lists[k1]
+        i2, v2, a2 = lists[k2]
+        assert np.array_equal(i1, i2[:, :k1]), (k1, k2)
+        assert np.array_equal(v1.view(np.uint32), v2[:, :k1].view(np.uint32)), (k1, k2)
+        assert np.array_equal(a1, a2)
 
 
 @pytest.mark.parametrize("R", [1, 3, 16])

@@ -90,15 +90,20 @@ def copy_calibration():
 
 
 def copy_ceiling(torch):
-    """A practical bandwidth figure for the same device: torch's 1 GiB device copy
-    (read + write bytes over its median time)."""
+    """Practical bandwidth figures for the same device from library kernels: torch's 1 GiB
+    device copy (read + write bytes) and a 2 GiB int32 sum (a streaming read), each over
+    back-to-back calls."""
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    t = stats_us(timed(lambda i: dst.copy_(src), 20))
+    tc = back_to_back_us(lambda i: dst.copy_(src), 20)
     del src, dst
-    return {"bytes_moved": 2 * n, "median_us": round(t["median"], 1),
-            "GBps": round(2 * n / (t["median"] * 1e-6) / 1e9, 1)}
+    big = torch.ones(2 * n // 4, dtype=torch.int32, device="cuda")
+    ts = back_to_back_us(lambda i: big.sum(dtype=torch.int64), 20)
+    del big
+    return {"copy_bytes": 2 * n, "copy_us": tc, "copy_GBps": round(2 * n / (tc * 1e-6) / 1e9, 1),
+            "sum_read_bytes": 2 * n, "sum_us": ts,
+            "sum_read_GBps": round(2 * n / (ts * 1e-6) / 1e9, 1)}
 
 
 def algorithmic_bytes(fmt, V, H, R):
@@ -224,7 +229,7 @@ def main():
 
     if not args.quick:
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
-        out["copy_ceiling"] = copy_ceiling(torch)
+        out["device_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
     print(json.dumps(out), flush=True)
@@ -339,9 +344,17 @@ def cpu_baseline(w, x, V, H, R, K):
     d1 = time.time() - t0
     oracle.threads(nt)
     b1 = algorithmic_bytes("fp8_block32", S, H, R)
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     log(f"cpu oracle: full step {dt:.2f}s median of {len(times)} on {nt} threads; "
-        f"1 thread: {S} vocab rows in {d1:.2f}s")
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": nt,
+        f"1 thread: {S} vocab rows in {d1:.2f}s ({cpu})")
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": nt, "cpu": cpu,
             "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": len(times),
             "quantize_seconds": round(tq, 3),
             "single_thread": {"value": round(b1 / d1 / 1e9, 4), "unit": "GB/s",

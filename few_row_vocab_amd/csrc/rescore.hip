@@ -7,8 +7,9 @@
 // Design: the work is a gather of rows*cand_k head rows (10 KB each at H = 5120) -- memory
 // bound, with one activation row per gathered head row, so plain FP32 FMAs on the vector
 // ALUs.  One wave per (row, slot): each lane reads 16 bytes of the head row and of the
-// activation row per step (a wave covers 1 KB of the head row per load), sums its products
-// in order, and the wave sums lanes with a fixed butterfly.  A second small kernel picks
+// activation row per step (a wave covers 1 KB of the head row per load), with eight steps
+// in flight before any is summed, sums its products in order, and the wave sums lanes with
+// a fixed butterfly.  A second small kernel picks
 // each row's winner under the same ordering as the top-k.
 #include "dh_internal.h"
 #include "launch.h"
@@ -17,6 +18,8 @@ namespace dh {
 namespace {
 
 constexpr int kRescoreWaves = 4;
+constexpr int kSteps = 8;                // 512-column steps a lane has in flight
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -40,20 +43,32 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(
     } else if (id < 0 || id >= V) {
         out = __builtin_nanf("");         // not a token of this head: never read
     } else {
-        const uint16_t *wr = W + id * H;
-        const uint16_t *xr = x + (int64_t)r * H;
+        // bounded buffer loads (bytes past the row read as 0, adding nothing), eight steps of
+        // 512 columns issued before any is used
+        const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(W + id * H), (short)0, H * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(x + (int64_t)r * H), (short)0, H * 2, kRsrcWord3);
         float acc = 0.f;
-        for (int h = lane * 8; h < H; h += 8 * kWave) {
-            const u32x4 wq = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wr + h));
-            const u32x4 xq = *reinterpret_cast<const u32x4 *>(xr + h);
-            acc = __builtin_fmaf(lo_bf16(xq.x), lo_bf16(wq.x), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.x), hi_bf16(wq.x), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.y), lo_bf16(wq.y), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.y), hi_bf16(wq.y), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.z), lo_bf16(wq.z), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.z), hi_bf16(wq.z), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.w), lo_bf16(wq.w), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.w), hi_bf16(wq.w), acc);
+        for (int h0 = 0; h0 < H; h0 += kSteps * 8 * kWave) {
+            u32x4 wq[kSteps], xq[kSteps];
+#pragma unroll
+            for (int j = 0; j < kSteps; j++) {
+                const uint32_t off = (uint32_t)(h0 + j * 8 * kWave + lane * 8) * 2u;
+                wq[j] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
+                xq[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < kSteps; j++) {
+                acc = __builtin_fmaf(lo_bf16(xq[j].x), lo_bf16(wq[j].x), acc);
+                acc = __builtin_fmaf(hi_bf16(xq[j].x), hi_bf16(wq[j].x), acc);
+                acc = __builtin_fmaf(lo_bf16(xq[j].y), lo_bf16(wq[j].y), acc);
+                acc = __builtin_fmaf(hi_bf16(xq[j].y), hi_bf16(wq[j].y), acc);
+                acc = __builtin_fmaf(lo_bf16(xq[j].z), lo_bf16(wq[j].z), acc);
+                acc = __builtin_fmaf(hi_bf16(xq[j].z), hi_bf16(wq[j].z), acc);
+                acc = __builtin_fmaf(lo_bf16(xq[j].w), lo_bf16(wq[j].w), acc);
+                acc = __builtin_fmaf(hi_bf16(xq[j].w), hi_bf16(wq[j].w), acc);
+            }
         }
         for (int off = 32; off > 0; off >>= 1)
             acc += __shfl_xor(acc, off);

@@ -54,6 +54,39 @@ __device__ inline uint32_t wave_scan(uint32_t v)
     return v;
 }
 
+// The smallest and largest of the non-zero 64-bit keys over the 64 lanes of a wave (the same
+// DPP pattern as wave_scan; masked lanes keep the identity).  An all-zero wave gives
+// (~0, 0).
+__device__ inline void wave_min_max(uint64_t &mn, uint64_t &mx)
+{
+#define DH_MINMAX_STEP(ctrl, rmask)                                                            \
+    {                                                                                          \
+        const uint32_t al = __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)mn, ctrl, rmask, \
+                                                        0xf, false);                           \
+        const uint32_t ah = __builtin_amdgcn_update_dpp(0xffffffffu, (uint32_t)(mn >> 32),     \
+                                                        ctrl, rmask, 0xf, false);              \
+        const uint32_t bl = __builtin_amdgcn_update_dpp(0u, (uint32_t)mx, ctrl, rmask, 0xf,    \
+                                                        false);                                \
+        const uint32_t bh = __builtin_amdgcn_update_dpp(0u, (uint32_t)(mx >> 32), ctrl, rmask, \
+                                                        0xf, false);                           \
+        const uint64_t a = ((uint64_t)ah << 32) | al, b = ((uint64_t)bh << 32) | bl;           \
+        mn = a < mn ? a : mn;                                                                  \
+        mx = b > mx ? b : mx;                                                                  \
+    }
+    DH_MINMAX_STEP(0x111, 0xf)   // row_shr:1
+    DH_MINMAX_STEP(0x112, 0xf)   // row_shr:2
+    DH_MINMAX_STEP(0x114, 0xf)   // row_shr:4
+    DH_MINMAX_STEP(0x118, 0xf)   // row_shr:8
+    DH_MINMAX_STEP(0x142, 0xa)   // row_bcast:15
+    DH_MINMAX_STEP(0x143, 0xc)   // row_bcast:31
+#undef DH_MINMAX_STEP
+    // lane 63 now holds the wave's extremes
+    mn = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mn >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mn, 63);
+    mx = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mx >> 32), 63) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mx, 63);
+}
+
 // One wave's view of a round's histogram: lane l holds the bins just below NB - l * (NB/64),
 // in descending order, so a prefix sum over lanes is a suffix sum over bins.  Finds the bin d
 // with above < rem <= above + count, where `above` counts the keys in higher bins.  Returns

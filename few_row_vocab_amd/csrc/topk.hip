@@ -37,20 +37,27 @@ namespace {
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
-// Radix select over 64-bit keys, most significant byte first (eight rounds at most).  Each
-// round has a histogram of 256 bins of its own (all cleared once at the start), so a round
-// needs one barrier: after it every wave scans the whole histogram itself (four bins a lane)
-// and reaches the same decision, and no wave writes what another may still be reading.
+// Radix select over 64-bit keys by ranges: a round sorts the keys of the current range into
+// 256 bins of width 2^shift from its base, the boundary bin becomes the next range (its width
+// 2^shift, the next bins 2^(shift - 8) wide), and the select stops as soon as that bin is
+// taken whole.  The
+// first range is [min, max] of the block's non-zero keys, so the first round spreads the keys
+// over the bins even when they share their leading bits (top logits share their exponent).
+// Each round has a histogram of its own (all cleared once at the start): after a round's one
+// barrier every wave scans the histogram itself (four bins a lane) and reaches the same
+// decision.  Eight rounds at most (the first shift is at most 56).
 constexpr int kRounds = 8;
 constexpr int kHistWords = kRounds * 256;
 
+template <int NT>
 struct SelectLds {
     uint32_t hist[kHistWords];
+    uint64_t wmin[NT / 64], wmax[NT / 64];         // per-wave extremes of the non-zero keys
     uint32_t fill;                                 // survivors placed so far
 };
 
 template <int NT>
-__device__ inline void clear_select(SelectLds &sh)
+__device__ inline void clear_select(SelectLds<NT> &sh)
 {
     for (int i = threadIdx.x; i < kHistWords; i += NT)
         sh.hist[i] = 0;
@@ -58,40 +65,85 @@ __device__ inline void clear_select(SelectLds &sh)
         sh.fill = 0;
 }
 
+// This wave's extremes to LDS (call before the barrier that follows clear_select).
+template <int N, int NT>
+__device__ inline void publish_min_max(const uint64_t (&key)[N], SelectLds<NT> &sh)
+{
+    uint64_t mn = ~0ull, mx = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        mn = key[i] != 0 && key[i] < mn ? key[i] : mn;
+        mx = key[i] > mx ? key[i] : mx;
+    }
+    wave_min_max(mn, mx);
+    if ((threadIdx.x & 63) == 0) {
+        sh.wmin[threadIdx.x >> 6] = mn;
+        sh.wmax[threadIdx.x >> 6] = mx;
+    }
+}
+
 // Selects among the non-zero keys held in registers (all distinct).  Returns P such that
 // the keys >= P are exactly the min(k, n) largest, where n (returned in `total`) is the
-// number of non-zero keys.  `sh` must have been cleared (and a barrier passed) before.
-template <int N, int NT>
-__device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds &sh,
+// number of non-zero keys.  RANGED: the first range is [min, max] of the non-zero keys (call
+// publish_min_max before the barrier); otherwise it is the whole key space, i.e. the digits
+// are the keys' bytes from the top, which costs no reduction and suits keys whose top byte
+// already varies.  Before the call: clear_select (and publish_min_max), a barrier.
+template <bool RANGED, int N, int NT>
+__device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds<NT> &sh,
                                uint32_t &total)
 {
-    // round 0 takes every non-zero key: its digit is the top byte
+    uint64_t lo = 0, hi = ~0ull;
+    if constexpr (RANGED) {
+        lo = ~0ull;
+        hi = 0;
 #pragma unroll
-    for (int i = 0; i < N; i++)
-        if (key[i] != 0)
-            atomicAdd(&sh.hist[(uint32_t)(key[i] >> 56)], 1u);
-    __syncthreads();
-    uint32_t d, above, count;
-    total = locate<256>(sh.hist, k, d, above, count);
-    if (total <= k)
-        return 1;                                  // every non-zero key
-    uint64_t prefix = (uint64_t)d << 56, mask = 0xffull << 56;
-    uint32_t rem = k - above;
-#pragma unroll 1
-    for (int round = 1; round < kRounds && count != rem; round++) {
-        const int shift = 56 - 8 * round;
-        uint32_t *h = sh.hist + 256 * round;
-#pragma unroll
-        for (int i = 0; i < N; i++)
-            if ((key[i] & mask) == prefix)         // prefix != 0, so key != 0
-                atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
-        __syncthreads();
-        locate<256>(h, rem, d, above, count);
-        prefix |= (uint64_t)d << shift;
-        mask |= 0xffull << shift;
-        rem -= above;
+        for (int w = 0; w < NT / 64; w++) {
+            lo = sh.wmin[w] < lo ? sh.wmin[w] : lo;
+            hi = sh.wmax[w] > hi ? sh.wmax[w] : hi;
+        }
+        total = 0;
+        if (hi == 0)
+            return 1;                              // no non-zero key
     }
-    return prefix;                                 // the boundary bin is taken whole
+    const uint64_t span = hi - lo;
+    int shift = span >> 8 ? 64 - __builtin_clzll(span >> 8) : 0;   // span >> shift < 256
+    uint64_t base = lo;
+    uint32_t rem = k;
+    int wshift = 64;                               // the range's width is 2^wshift (64: all)
+#pragma unroll 1
+    for (int round = 0; round < kRounds; round++) {
+        uint32_t *h = sh.hist + 256 * round;
+        if constexpr (RANGED) {
+#pragma unroll
+            for (int i = 0; i < N; i++) {
+                const uint64_t off = key[i] - base;
+                if (key[i] != 0 && key[i] >= base && (wshift == 64 || (off >> wshift) == 0))
+                    atomicAdd(&h[(uint32_t)(off >> shift)], 1u);
+            }
+        } else {
+            // whole key space: the range is the keys sharing base's bits above wshift
+            const uint64_t mask = wshift == 64 ? 0ull : ~0ull << wshift;
+#pragma unroll
+            for (int i = 0; i < N; i++)
+                if (key[i] != 0 && (key[i] & mask) == base)
+                    atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        uint32_t d, above, count;
+        const uint32_t t = locate<256>(h, rem, d, above, count);
+        if (round == 0) {
+            total = t;
+            if (t <= k)
+                return 1;                          // every non-zero key
+        }
+        rem -= above;
+        base += (uint64_t)d << shift;
+        if (count == rem || shift == 0)            // the boundary bin is taken whole
+            return base;
+        wshift = shift;                            // the boundary bin is the next range
+        shift = shift > 8 ? shift - 8 : 0;
+    }
+    return base;                                   // not reached: shift 0 ends by then
 }
 
 // Pass 1: one workgroup of NT threads per (chunk of NT * kP1PerThread logits, row); thread
@@ -100,7 +152,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V, int k,
                                                  int nchunks, uint64_t *cand)
 {
-    __shared__ __align__(16) SelectLds sh;
+    __shared__ __align__(16) SelectLds<NT> sh;
     constexpr int PER = kP1PerThread;
     const int r = blockIdx.y, c = blockIdx.x;
     const int64_t base = (int64_t)c * (NT * PER);
@@ -115,7 +167,6 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         u[j] = __builtin_amdgcn_raw_buffer_load_b32(
             rs, (uint32_t)(base + j * NT + threadIdx.x) * 4u, 0, 0);
     clear_select<NT>(sh);
-    __syncthreads();
     uint64_t key[PER];
 #pragma unroll
     for (int j = 0; j < PER; j++) {
@@ -123,8 +174,9 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         const uint32_t im = id < V ? order_key(__uint_as_float(u[j])) : 0u;
         key[j] = im ? entry_key(im, (uint32_t)id) : 0ull;
     }
+    __syncthreads();
     uint32_t n;
-    const uint64_t P = select_top<PER, NT>(key, (uint32_t)k, sh, n);
+    const uint64_t P = select_top<false, PER, NT>(key, (uint32_t)k, sh, n);
     const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
 
     // survivors in any order (the merge takes the lists as sets)
@@ -156,16 +208,20 @@ __device__ inline uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size,
 
 // Up to this many survivors the merge ranks by counting; above, by sorted runs of 64.
 constexpr int kCountMax = 128;
+// Above this k the merge's select ranges over [min, max] of the keys (measured: for k = 1
+// the reduction costs more than the rounds it saves).
+constexpr int kRangedMinK = 8;
 
 // Pass 2: one workgroup per row; a thread holds PER of the row's nchunks * k list slots
-// (PER * kMergeThreads >= nchunks * k).
-template <int PER>
+// (PER * kMergeThreads >= nchunks * k).  The lists hold the chunks' top values, which share
+// their leading bits, so for more than a few winners the select ranges over [min, max].
+template <int PER, bool RANGED>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits, int64_t V,
                                                             int k, int nchunks,
                                                             const uint64_t *cand, int32_t *ids,
                                                             float *vals, int32_t *argmax)
 {
-    __shared__ __align__(16) SelectLds sh;
+    __shared__ __align__(16) SelectLds<kMergeThreads> sh;
     __shared__ __align__(16) uint64_t sel[DH_MAX_K];
     const int r = blockIdx.x;
     const int slots = nchunks * k;
@@ -182,9 +238,11 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         key[j] = ((uint64_t)q.y << 32) | q.x;
     }
     clear_select<kMergeThreads>(sh);
+    if constexpr (RANGED)
+        publish_min_max<PER, kMergeThreads>(key, sh);
     __syncthreads();
     uint32_t n;
-    const uint64_t P = select_top<PER, kMergeThreads>(key, (uint32_t)k, sh, n);
+    const uint64_t P = select_top<RANGED, PER, kMergeThreads>(key, (uint32_t)k, sh, n);
     const int kk = n < (uint32_t)k ? (int)n : k;
 
     // the survivors, in any order, to sel[0..kk)
@@ -297,8 +355,11 @@ hipError_t launch_merge(const float *logits, int rows, int64_t vocab, int k, int
                         const uint64_t *cand, int32_t *ids, float *vals, int32_t *argmax,
                         hipStream_t stream)
 {
-    return launch(topk_merge<PER>, dim3(rows), dim3(kMergeThreads), 0, stream, logits, vocab,
-                  k, nc, cand, ids, vals, argmax);
+    if (k > kRangedMinK)
+        return launch(topk_merge<PER, true>, dim3(rows), dim3(kMergeThreads), 0, stream,
+                      logits, vocab, k, nc, cand, ids, vals, argmax);
+    return launch(topk_merge<PER, false>, dim3(rows), dim3(kMergeThreads), 0, stream, logits,
+                  vocab, k, nc, cand, ids, vals, argmax);
 }
 
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int32_t *ids,

@@ -263,21 +263,21 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         sbytes = sbytes_next;
     }
     __syncthreads();
-    // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.
-    const int per_tile = TR * a.R * 16;
-    const int n = (it + 1) * per_tile;
-    for (int o = threadIdx.x; o < n; o += blockDim.x) {
-        const int t = o / per_tile;
-        const int rem = o - t * per_tile;
-        const int r = rem / (a.R * 16);
-        const int rc = rem - r * (a.R * 16);
-        const int c = rc >> 4, i = rc & 15;
-        const int64_t v = (int64_t)(blockIdx.x + t * gridDim.x) * TILE + 16 * r + i;
-        if (v < V) {
-            float s = stage[t * OUTS + r * 256 + c * 16 + i];
-            if (FMT == DH_FP8_ROW)
-                s *= a.rscale[v];
-            a.logits[(int64_t)c * V + v] = s;
+    // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave
+    // w writes tiles w, w + nw, ...; a lane takes (activation row c, head row i) pairs.
+    static_assert(TR == 1, "the writer below assumes one 16-row group per tile");
+    const int per_tile = a.R * 16;
+    for (int t = wave; t <= it; t += nw) {
+        const int64_t v0 = (int64_t)(blockIdx.x + t * gridDim.x) * TILE;
+        for (int o = lane; o < per_tile; o += kWave) {
+            const int c = o >> 4, i = o & 15;
+            const int64_t v = v0 + i;
+            if (v < V) {
+                float s = stage[t * OUTS + c * 16 + i];
+                if (FMT == DH_FP8_ROW)
+                    s *= a.rscale[v];
+                a.logits[(int64_t)c * V + v] = s;
+            }
         }
     }
 }

@@ -238,6 +238,7 @@ def main():
 
     if not args.quick:
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
+        out["subset_head"] = subset_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
@@ -324,6 +325,57 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
     log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
         f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f})")
+    return res
+
+
+def subset_sweep(dh, torch, n):
+    """The draft-vocabulary subset head against the whole head it is gathered from: an FP8
+    head with a row scale, H=4096, V=131072, and 49,152 of its rows with their token ids;
+    dh_draft on the whole head and dh_draft_mapped on the subset, top-64, 1 and 16 rows,
+    back to back over rotated copies (each subset copy is 201 MB, so three of them do not
+    fit the 256 MB Infinity Cache), plus the gather itself."""
+    import synth
+    name = "subset_head"
+    c = synth.CONFIGS[name]
+    V, H, nd, K = c["V"], c["H"], c["n_draft"], 64
+    dev = torch.device("cuda:0")
+    wd = torch.from_numpy(synth.head_bf16(name).view(np.int16)).to(dev)
+    x16 = torch.from_numpy(synth.activations(name, 16).view(np.int16)).to(dev)
+    im = torch.from_numpy(synth.draft_ids(name)).to(dev)
+    fulls, subs = [], []
+    for i in range(NCOPY):
+        codes, scale = dh.quantize(wd, dh.FP8_ROW)
+        fulls.append(dh.Head(dh.FP8_ROW, codes, scale))
+        subs.append(dh.gather_rows(fulls[-1], im))
+    del wd
+    torch.cuda.synchronize()
+    fg = lambda i: dh.gather_rows(fulls[i % NCOPY], im, out=subs[i % NCOPY])
+    gat = back_to_back_us(fg, n)
+    gbytes = 2 * nd * H + 2 * nd * 4 + nd * 4
+    res = {"workload": f"FP8 E4M3 head with a row scale, H={H}, V={V}; subset of {nd} "
+                       f"sorted token ids; top-{K}",
+           "gather_us": gat, "gather_bytes": gbytes,
+           "gather_GBps": round(gbytes / (gat * 1e-6) / 1e9, 1), "rows": []}
+    for R in (1, 16):
+        x = x16[:R].contiguous()
+        ws_f, ws_s = dh.workspace(R, V, K), dh.workspace(R, nd, K)
+        mk = lambda: {"ids": torch.empty((R, K), dtype=torch.int32, device=dev),
+                      "vals": torch.empty((R, K), dtype=torch.float32, device=dev),
+                      "draft": torch.empty((R,), dtype=torch.int32, device=dev)}
+        of, os_ = mk(), mk()
+        ff = lambda i: dh.draft(fulls[i % NCOPY], x, K, ws=ws_f, out=of)
+        fs = lambda i: dh.draft_mapped(subs[i % NCOPY], im, x, K, ws=ws_s, out=os_)
+        tf, ts = back_to_back_us(ff, n), back_to_back_us(fs, n)
+        bf = algorithmic_bytes("fp8_row", V, H, R)
+        bs = algorithmic_bytes("fp8_row", nd, H, R)
+        res["rows"].append({"rows": R, "whole_head_dh_draft_us": tf,
+                            "subset_dh_draft_mapped_us": ts,
+                            "speedup": round(tf / ts, 3),
+                            "whole_head_GBps": round(bf / (tf * 1e-6) / 1e9, 1),
+                            "subset_GBps": round(bs / (ts * 1e-6) / 1e9, 1)})
+        log(f"subset head R={R}: whole head {tf:.1f} us, subset {ts:.1f} us "
+            f"({tf / ts:.2f}x)")
+    log(f"subset gather: {gat:.1f} us ({gbytes / (gat * 1e-6) / 1e9:.0f} GB/s)")
     return res
 
 

@@ -3,6 +3,7 @@
 // stance of refusing a larger span rather than clipping it ("dsv41 Zig: the TFE draft head
 // (TF_DS_DRAFTER=eagle), off by default", commit notes on absorb and the review thread).
 #include <atomic>
+#include <initializer_list>
 #include <stdint.h>
 
 #include "dh_internal.h"
@@ -173,8 +174,61 @@ dh_status dh_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k, i
                   void *stream)
 {
     DH_TRY(check_topk(logits, rows, vocab, k, ids, vals, argmax, workspace, workspace_bytes));
-    return device_status(dh::launch_topk(logits, rows, vocab, k, ids, vals, argmax, workspace,
-                                         (hipStream_t)stream));
+    return device_status(dh::launch_topk(logits, rows, vocab, k, nullptr, ids, vals, argmax,
+                                         workspace, (hipStream_t)stream));
+}
+
+// The id map of a subset head is an input: no output may overlap it.
+static dh_status check_idmap(const int32_t *idmap, int64_t vocab, std::initializer_list<Span> outs)
+{
+    if (!idmap || !aligned(idmap, 4))
+        return DH_ERR_INVALID;
+    const Span sm = span(idmap, (size_t)vocab * 4);
+    for (const Span &o : outs)
+        if (overlap(sm, o))
+            return DH_ERR_INVALID;
+    return DH_OK;
+}
+
+dh_status dh_topk_mapped(const float *logits, int32_t rows, int64_t vocab, int32_t k,
+                         const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    DH_TRY(check_topk(logits, rows, vocab, k, ids, vals, argmax, workspace, workspace_bytes));
+    DH_TRY(check_idmap(idmap, vocab,
+                       {span(ids, (size_t)rows * k * 4), span(vals, (size_t)rows * k * 4),
+                        span(argmax, argmax ? (size_t)rows * 4 : 0),
+                        span(workspace, dh::topk_ws_layout(rows, vocab, k).bytes)}));
+    return device_status(dh::launch_topk(logits, rows, vocab, k, idmap, ids, vals, argmax,
+                                         workspace, (hipStream_t)stream));
+}
+
+dh_status dh_gather_rows(const dh_head *head, const int32_t *ids, int64_t n, void *weight,
+                         void *scale, void *stream)
+{
+    DH_TRY(check_head(head));
+    if (head->format == DH_FP8_BLOCK32)
+        return DH_ERR_UNSUPPORTED;
+    if (n < 1)
+        return DH_ERR_INVALID;
+    if (n > ((int64_t)1 << 25))
+        return DH_ERR_UNSUPPORTED;
+    if (!ids || !weight || !aligned(ids, 4) || !aligned(weight, 16))
+        return DH_ERR_INVALID;
+    const bool row_scale = head->format == DH_FP8_ROW;
+    if (row_scale ? (!scale || !aligned(scale, 4)) : scale != nullptr)
+        return DH_ERR_INVALID;
+    const Span sw = span(weight, (size_t)n * (size_t)head->hidden * elem_bytes(head->format));
+    const Span ss = span(scale, row_scale ? (size_t)n * 4 : 0);
+    const Span in[] = {head_weight(*head), head_scale(*head), span(ids, (size_t)n * 4)};
+    for (const Span &s : in)
+        if (overlap(sw, s) || overlap(ss, s))
+            return DH_ERR_INVALID;
+    if (overlap(sw, ss))
+        return DH_ERR_INVALID;
+    return device_status(dh::launch_gather_rows(*head, ids, n, weight,
+                                                static_cast<float *>(scale),
+                                                (hipStream_t)stream));
 }
 
 static dh_status check_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
@@ -211,9 +265,12 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                                             draft, (hipStream_t)stream));
 }
 
-dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x, int32_t rows,
-                   int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
-                   float *logits, void *workspace, size_t workspace_bytes, void *stream)
+// dh_draft and dh_draft_mapped: with an id map the head is a subset head whose entry j is
+// vocabulary id idmap[j], and the dense head spans the whole vocabulary.
+static dh_status run_draft(const dh_head *head, const int32_t *idmap, const dh_head *dense,
+                           const uint16_t *x, int32_t rows, int32_t k, int32_t *ids,
+                           float *vals, int32_t *draft, float *exact, float *logits,
+                           void *workspace, size_t workspace_bytes, void *stream)
 {
     DH_TRY(check_head(head));
     DH_TRY(check_rows(rows));
@@ -224,7 +281,7 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
         return DH_ERR_INVALID;
     if (dense) {
         DH_TRY(check_head(dense));
-        if (dense->format != DH_BF16 || dense->vocab != head->vocab ||
+        if (dense->format != DH_BF16 || (!idmap && dense->vocab != head->vocab) ||
             dense->hidden != head->hidden || !exact)
             return DH_ERR_INVALID;
     } else if (exact) {
@@ -255,14 +312,38 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
             overlap(span(vals, (size_t)rows * k * 4), s) || overlap(span(draft, (size_t)rows * 4), s))
             return DH_ERR_INVALID;
     }
+    if (idmap)
+        DH_TRY(check_idmap(idmap, head->vocab,
+                           {sl, sw, span(ids, (size_t)rows * k * 4),
+                            span(vals, (size_t)rows * k * 4), span(draft, (size_t)rows * 4),
+                            span(exact, exact ? (size_t)rows * k * 4 : 0)}));
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e = dh::launch_gemv(*head, x, rows, L, st);
     if (e == hipSuccess)
-        e = dh::launch_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft,
+        e = dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals, dense ? nullptr : draft,
                             workspace, st);
     if (e == hipSuccess && dense)
         e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st);
     return device_status(e);
+}
+
+dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x, int32_t rows,
+                   int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
+                   float *logits, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_draft(head, nullptr, dense, x, rows, k, ids, vals, draft, exact, logits,
+                   workspace, workspace_bytes, stream);
+}
+
+dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_head *dense,
+                          const uint16_t *x, int32_t rows, int32_t k, int32_t *ids,
+                          float *vals, int32_t *draft, float *exact, float *logits,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!idmap)
+        return DH_ERR_INVALID;
+    return run_draft(head, idmap, dense, x, rows, k, ids, vals, draft, exact, logits, workspace,
+                   workspace_bytes, stream);
 }
 
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,

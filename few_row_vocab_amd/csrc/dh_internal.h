@@ -48,12 +48,16 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
 // hipError_t of its launches.
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream);
-hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int32_t *ids,
-                       float *vals, int32_t *argmax, void *ws, hipStream_t stream);
+// idmap: NULL, or the vocabulary id of each logit column (ids and argmax are mapped).
+hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
+                       const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                       void *ws, hipStream_t stream);
 
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,
                           float *exact, int32_t *draft, hipStream_t stream);
+hipError_t launch_gather_rows(const dh_head &head, const int32_t *ids, int64_t n, void *weight,
+                              float *scale, hipStream_t stream);
 hipError_t launch_quantize(int format, const uint16_t *w, int64_t vocab, int64_t hidden,
                            uint8_t *codes, void *scale, hipStream_t stream);
 

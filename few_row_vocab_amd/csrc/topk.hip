@@ -218,7 +218,8 @@ constexpr int kRangedMinK = 8;
 template <int PER, bool RANGED>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits, int64_t V,
                                                             int k, int nchunks,
-                                                            const uint64_t *cand, int32_t *ids,
+                                                            const uint64_t *cand,
+                                                            const int32_t *idmap, int32_t *ids,
                                                             float *vals, int32_t *argmax)
 {
     __shared__ __align__(16) SelectLds<kMergeThreads> sh;
@@ -323,10 +324,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
     }
     if (x != 0 && rank < (uint32_t)kk) {
         const uint32_t id = key_id(x);
-        rid[rank] = (int32_t)id;
+        // a subset head's entry id is vocabulary id idmap[id]
+        const int32_t out = idmap ? idmap[id] : (int32_t)id;
+        rid[rank] = out;
         rval[rank] = image_value(x, logits + (int64_t)r * V + id);
         if (rank == 0 && argmax)
-            argmax[r] = (int32_t)id;
+            argmax[r] = out;
     }
     for (int p = kk + i; p < k; p += kMergeThreads) {
         rid[p] = 0;
@@ -352,18 +355,19 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
 
 template <int PER>
 hipError_t launch_merge(const float *logits, int rows, int64_t vocab, int k, int nc,
-                        const uint64_t *cand, int32_t *ids, float *vals, int32_t *argmax,
-                        hipStream_t stream)
+                        const uint64_t *cand, const int32_t *idmap, int32_t *ids, float *vals,
+                        int32_t *argmax, hipStream_t stream)
 {
     if (k > kRangedMinK)
         return launch(topk_merge<PER, true>, dim3(rows), dim3(kMergeThreads), 0, stream,
-                      logits, vocab, k, nc, cand, ids, vals, argmax);
+                      logits, vocab, k, nc, cand, idmap, ids, vals, argmax);
     return launch(topk_merge<PER, false>, dim3(rows), dim3(kMergeThreads), 0, stream, logits,
-                  vocab, k, nc, cand, ids, vals, argmax);
+                  vocab, k, nc, cand, idmap, ids, vals, argmax);
 }
 
-hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int32_t *ids,
-                       float *vals, int32_t *argmax, void *ws, hipStream_t stream)
+hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
+                       const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                       void *ws, hipStream_t stream)
 {
     const TopkWs w = topk_ws_layout(rows, vocab, k);
     const int chunk = topk_chunk(vocab, k);
@@ -390,14 +394,19 @@ hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k, int3
     const uint64_t *cc = cand;
     const int64_t slots = (int64_t)nc * k;         // <= kMergeSlots by the chunk choice
     if (slots <= kMergeThreads)
-        return launch_merge<1>(logits, rows, vocab, k, nc, cc, ids, vals, argmax, stream);
+        return launch_merge<1>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
+                               stream);
     if (slots <= 2 * kMergeThreads)
-        return launch_merge<2>(logits, rows, vocab, k, nc, cc, ids, vals, argmax, stream);
+        return launch_merge<2>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
+                               stream);
     if (slots <= 4 * kMergeThreads)
-        return launch_merge<4>(logits, rows, vocab, k, nc, cc, ids, vals, argmax, stream);
+        return launch_merge<4>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
+                               stream);
     if (slots <= 8 * kMergeThreads)
-        return launch_merge<8>(logits, rows, vocab, k, nc, cc, ids, vals, argmax, stream);
-    return launch_merge<16>(logits, rows, vocab, k, nc, cc, ids, vals, argmax, stream);
+        return launch_merge<8>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
+                               stream);
+    return launch_merge<16>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
+                            stream);
 }
 
 }  // namespace dh

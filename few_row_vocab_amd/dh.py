@@ -58,11 +58,15 @@ def lib():
         L.dh_rescore.argtypes = [hp, vp, i32, vp, i32, vp, vp, vp]
         L.dh_draft.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
+        L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
+        L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.dh_draft_mapped.argtypes = [hp, vp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_workspace_bytes.argtypes = [i32, i64, i32]
         L.dh_workspace_bytes.restype = sz
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
-        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize):
+        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
+                  L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped):
             f.restype = i32
         _lib = L
     return _lib
@@ -149,9 +153,7 @@ def gemv(head: Head, x, logits=None, stream=None):
     return logits
 
 
-def topk(logits, k, ws=None, ids=None, vals=None, argmax=None, with_argmax=True,
-         stream=None):
-    """(ids int32 [R][k], vals fp32 [R][k], argmax int32 [R] or None)."""
+def _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream):
     _want(logits, torch.float32, "logits")
     R, V = logits.shape
     dev = logits.device
@@ -160,9 +162,54 @@ def topk(logits, k, ws=None, ids=None, vals=None, argmax=None, with_argmax=True,
     if with_argmax and argmax is None:
         argmax = torch.empty((R,), dtype=torch.int32, device=dev)
     ws = workspace(R, V, k, dev) if ws is None else ws
-    _check(lib().dh_topk(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
-                         _ptr(ws), ws.numel(), _stream(stream)))
+    if idmap is None:
+        st = lib().dh_topk(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        _want(idmap, torch.int32, "idmap")
+        if idmap.numel() != V:
+            raise ValueError(f"idmap: expected {V} ids, got {idmap.numel()}")
+        st = lib().dh_topk_mapped(_ptr(logits), R, V, k, _ptr(idmap), _ptr(ids), _ptr(vals),
+                                  _ptr(argmax), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st)
     return ids, vals, argmax
+
+
+def topk(logits, k, ws=None, ids=None, vals=None, argmax=None, with_argmax=True,
+         stream=None):
+    """(ids int32 [R][k], vals fp32 [R][k], argmax int32 [R] or None)."""
+    return _topk_call(logits, k, None, ws, ids, vals, argmax, with_argmax, stream)
+
+
+def topk_mapped(logits, k, idmap, ws=None, ids=None, vals=None, argmax=None,
+                with_argmax=True, stream=None):
+    """topk over a subset head's logits; ids and argmax are vocabulary ids idmap[j]."""
+    return _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream)
+
+
+def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):
+    """The subset head of `head` (BF16 or FP8_ROW) whose row j is row ids[j] (int32);
+    written into `out` when given."""
+    _want(ids, torch.int32, "ids")
+    n = ids.numel()
+    dev = head.weight.device
+    if out is None:
+        weight = torch.empty((n, head.hidden), dtype=head.weight.dtype, device=dev)
+        scale = (torch.empty((n,), dtype=torch.float32, device=dev)
+                 if head.format == FP8_ROW else None)
+    else:
+        weight, scale = out.weight, out.scale
+        if weight.shape != (n, head.hidden) or weight.dtype != head.weight.dtype:
+            raise ValueError("out: weight must be [len(ids)][H] of the head's dtype")
+        _want(weight, weight.dtype, "out.weight")
+        if scale is not None:
+            _want(scale, torch.float32, "out.scale")
+            if scale.numel() != n:
+                raise ValueError("out: scale must hold len(ids) floats")
+    h = head._c()
+    _check(lib().dh_gather_rows(ctypes.byref(h), _ptr(ids), n, _ptr(weight), _ptr(scale),
+                                _stream(stream)))
+    return Head(head.format, weight, scale)
 
 
 def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
@@ -179,8 +226,9 @@ def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
 
 
 def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=False,
-          out=None, stream=None):
-    """The whole projection: dict with ids, vals, draft (+ exact, logits)."""
+          out=None, stream=None, idmap=None):
+    """The whole projection: dict with ids, vals, draft (+ exact, logits).  With `idmap`
+    (int32 [head.vocab]) the head is a subset head and the call is dh_draft_mapped."""
     R = x.shape[0]
     dev = x.device
     o = {} if out is None else out
@@ -194,11 +242,22 @@ def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=F
     ws = workspace(R, head.vocab, k, dev) if ws is None else ws
     h = head._c()
     d = dense._c() if dense is not None else None
-    _check(lib().dh_draft(ctypes.byref(h), ctypes.byref(d) if d is not None else None,
-                          _ptr(x), R, k, _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
-                          _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(),
-                          _stream(stream)))
+    tail = (_ptr(x), R, k, _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
+            _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(), _stream(stream))
+    dref = ctypes.byref(d) if d is not None else None
+    if idmap is None:
+        _check(lib().dh_draft(ctypes.byref(h), dref, *tail))
+    else:
+        _want(idmap, torch.int32, "idmap")
+        if idmap.numel() != head.vocab:
+            raise ValueError(f"idmap: expected {head.vocab} ids, got {idmap.numel()}")
+        _check(lib().dh_draft_mapped(ctypes.byref(h), _ptr(idmap), dref, *tail))
     return o
+
+
+def draft_mapped(head: Head, idmap, x, k, dense: Optional[Head] = None, **kw):
+    """dh_draft_mapped: draft on a subset head whose row j is vocabulary id idmap[j]."""
+    return draft(head, x, k, dense=dense, idmap=idmap, **kw)
 
 
 def quantize(w, format, stream=None):

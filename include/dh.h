@@ -143,6 +143,40 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream);
 
+/* Draft-vocabulary subset heads.  [SUPER] 'What this changes': a draft head packs the FP8
+ * rows of its draft vocabulary's ids into a weight of their own (keeping the head's scales)
+ * and uploads their vocabulary ids; a level projects over that subset only, and the ids it
+ * proposes are vocabulary ids.
+ *
+ * dh_gather_rows -- the subset head: row j of the output is row ids[j] of `head`, codes and
+ * (DH_FP8_ROW) its row scale.  head: DH_BF16 or DH_FP8_ROW; DH_FP8_BLOCK32 is refused with
+ * DH_ERR_UNSUPPORTED (a 32x32 scale block cannot be split by rows).  ids: device int32 [n];
+ * an id outside [0, V) gives a row of zero codes (and scale 0), never a read outside the
+ * head.  weight: device buffer of n * H elements of the head's format, 16-byte aligned;
+ * scale: device float32 [n] for DH_FP8_ROW, else NULL.  The subset head is then
+ * {head->format, n, H, weight, scale}. */
+dh_status dh_gather_rows(const dh_head *head, const int32_t *ids, int64_t n, void *weight,
+                         void *scale, void *stream);
+
+/* dh_topk_mapped -- dh_topk over logits [rows][vocab] of a subset head, whose entry j is
+ * vocabulary id idmap[j]: ids (and argmax) are vocabulary ids, values and pads as dh_topk
+ * (a pad is vocabulary id 0).  idmap: device int32 [vocab], strictly increasing, so that the
+ * lower entry of a tie is the lower vocabulary id (a precondition: not checked).  Workspace
+ * as dh_topk. */
+dh_status dh_topk_mapped(const float *logits, int32_t rows, int64_t vocab, int32_t k,
+                         const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* dh_draft_mapped -- dh_draft on a subset head (see dh_gather_rows) whose row j is
+ * vocabulary id idmap[j] (device int32 [head->vocab], strictly increasing): ids and drafts
+ * are vocabulary ids.  In the two-stage form `dense` is the full-vocabulary bf16 head (same
+ * H; any V) and the candidates' exact logits come from its rows at their vocabulary ids.
+ * Workspace: dh_workspace_bytes(rows, head->vocab, k). */
+dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_head *dense,
+                          const uint16_t *x, int32_t rows, int32_t k, int32_t *ids,
+                          float *vals, int32_t *draft, float *exact, float *logits,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace dh_topk and dh_draft need for these sizes (dh_draft with logits ==
  * NULL included).  Pure host function; returns 0 for sizes the library refuses. */
 size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k);

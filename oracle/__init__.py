@@ -46,6 +46,12 @@ def lib():
         L.orc_topk.restype = c.c_int
         L.orc_topk.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
                                c.c_void_p]
+        L.orc_topk_mapped.restype = c.c_int
+        L.orc_topk_mapped.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
+                                      c.c_void_p, c.c_void_p]
+        L.orc_subset_rows.restype = None
+        L.orc_subset_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
+                                      c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
         L.orc_rescore.restype = None
         L.orc_rescore.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_int,
                                   c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p]
@@ -138,6 +144,58 @@ def topk(logits, k):
     if lib().orc_topk(_p(logits), R, V, k, _p(ids), _p(vals)) != 0:
         raise MemoryError("oracle top-k")
     return ids, vals
+
+
+def topk_mapped(logits, k, idmap):
+    """O13.  Top-k of a subset head's logits [R][n] whose column j is token idmap[j]: ids are
+    token ids, ties go to the lower token id.  -> (ids int32 [R][k], vals float32 [R][k])."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    idmap = _c(idmap, np.int32)
+    if idmap.shape != (V,):
+        raise ValueError("idmap length != logits width")
+    ids = np.empty((R, k), np.int32)
+    vals = np.empty((R, k), np.float32)
+    if lib().orc_topk_mapped(_p(logits), R, V, k, _p(idmap), _p(ids), _p(vals)) != 0:
+        raise MemoryError("oracle top-k")
+    return ids, vals
+
+
+def subset_rows(fmt, w, scale, ids):
+    """O12.  The subset head of (w, scale) for token ids (int32 [n]): (w' [n][H], scale'
+    float32 [n] or None).  Per-row FP8 or bf16; ids outside [0, V) give zero rows."""
+    if fmt == FMT_BF16:
+        w = _c(w, np.uint16)
+        es, scale = 2, None
+    elif fmt == FMT_FP8_ROW:
+        w = _c(w, np.uint8)
+        es = 1
+        scale = _c(scale, np.float32)
+    else:
+        raise ValueError("subset rows: bf16 or per-row FP8 heads only")
+    V, H = w.shape
+    ids = _c(ids, np.int32)
+    n = ids.size
+    out = np.empty((n, H), w.dtype)
+    out_s = np.empty((n,), np.float32) if scale is not None else None
+    lib().orc_subset_rows(_p(w), _p(scale), V, H, es, _p(ids), n, _p(out), _p(out_s))
+    return out, out_s
+
+
+def draft_mapped(fmt, w, scale, idmap, x, k, dense_w=None):
+    """O11 on a subset head (O12) whose row j is token idmap[j], with O13's top-k; the
+    two-stage dense head spans the whole vocabulary."""
+    logits = gemv(fmt, w, scale, x)
+    ids, vals = topk_mapped(logits, k, idmap)
+    out = {"logits": logits, "ids": ids, "vals": vals}
+    if dense_w is None:
+        out["draft"] = ids[:, 0].copy()
+    else:
+        use = vals > -np.inf
+        exact, d = rescore(dense_w, x, ids, use)
+        out["exact"] = exact
+        out["draft"] = d
+    return out
 
 
 def argmax(logits):

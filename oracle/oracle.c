@@ -15,7 +15,7 @@
  * rounded once to float.  Build with -O2 -ffp-contract=off and no fast-math, so that the
  * compiler neither fuses nor reorders the sums and NaN/inf follow IEEE rules.
  *
- * Numbering O1..O11 / Q1..Q2 is the oracle's own list of definitions, restated in the
+ * Numbering O1..O13 / Q1..Q2 is the oracle's own list of definitions, restated in the
  * comments of each function.
  */
 #include <math.h>
@@ -153,8 +153,12 @@ static int cmp_entry(const void *a, const void *b)
 /* O8 + O9: per row, the eligible ids sorted by O7, the first min(k, n_eligible) of them;
  * the remaining slots are (id 0, value -inf) ([SUPER] pad rule).  Slot j holds the entry
  * that exactly j others beat.  ids/vals are [R][k]; the argmax of a row is ids[r][0] (0 for
- * a row with no eligible logit).  Returns 0, or -1 if memory runs out. */
-int orc_topk(const float *logits, int R, int64_t V, int k, int32_t *ids, float *vals)
+ * a row with no eligible logit).  Returns 0, or -1 if memory runs out.
+ * O13 (idmap != NULL): column v of the logits is token idmap[v] (a subset head, O12); the
+ * entries are (logit, idmap[v]) and O7 orders them by that token id ([SUPER] 'What this
+ * changes': a level proposes over the subset, and what it proposes are vocabulary ids). */
+static int topk_of(const float *logits, int R, int64_t V, int k, const int32_t *idmap,
+                   int32_t *ids, float *vals)
 {
     struct entry *e = malloc(sizeof *e * (size_t)(V > 0 ? V : 1));
     if (!e)
@@ -165,7 +169,7 @@ int orc_topk(const float *logits, int R, int64_t V, int k, int32_t *ids, float *
         for (int64_t v = 0; v < V; v++)
             if (eligible(row[v])) {
                 e[n].l = row[v];
-                e[n].id = v;
+                e[n].id = idmap ? idmap[v] : v;
                 n++;
             }
         qsort(e, (size_t)n, sizeof *e, cmp_entry);
@@ -181,6 +185,40 @@ int orc_topk(const float *logits, int R, int64_t V, int k, int32_t *ids, float *
     }
     free(e);
     return 0;
+}
+
+int orc_topk(const float *logits, int R, int64_t V, int k, int32_t *ids, float *vals)
+{
+    return topk_of(logits, R, V, k, NULL, ids, vals);
+}
+
+int orc_topk_mapped(const float *logits, int R, int64_t V, int k, const int32_t *idmap,
+                    int32_t *ids, float *vals)
+{
+    return topk_of(logits, R, V, k, idmap, ids, vals);
+}
+
+/* ---------------------------------------------------------------- draft-vocabulary subset */
+
+/* O12: the subset head of a head for a list of token ids ([SUPER] 'What this changes': the
+ * head's FP8 rows of the draft vocabulary's ids are packed into a weight of their own, with
+ * the head's scales): row j is row ids[j], its es bytes per element copied as they are, and
+ * for per-row FP8 (scale != NULL) scale j is scale[ids[j]].  Reading where the page is
+ * silent: an id outside [0, V) gives a row of zero bytes and scale 0. */
+void orc_subset_rows(const void *w, const float *scale, int64_t V, int64_t H, int es,
+                     const int32_t *ids, int64_t n, void *out, float *out_scale)
+{
+    const size_t row = (size_t)H * (size_t)es;
+    for (int64_t j = 0; j < n; j++) {
+        const int64_t id = ids[j];
+        const int ok = id >= 0 && id < V;
+        if (ok)
+            memcpy((char *)out + (size_t)j * row, (const char *)w + (size_t)id * row, row);
+        else
+            memset((char *)out + (size_t)j * row, 0, row);
+        if (scale)
+            out_scale[j] = ok ? scale[id] : 0.0f;
+    }
 }
 
 /* ---------------------------------------------------------------- two-stage rescore */

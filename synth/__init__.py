@@ -24,6 +24,7 @@ BLOCK = 1 << 20
 STREAM_WEIGHTS = 0
 STREAM_ACTS = 1
 STREAM_PLANT = 2
+STREAM_IDS = 3
 
 # Workloads (shapes from the workload descriptions; seeds are this module's choice).
 CONFIGS = {
@@ -37,6 +38,9 @@ CONFIGS = {
                       x="normal", ks=[512], seed=404),
     "edge": dict(H=7168, V=163840, rows=[16], fmt="fp8_block32", w_std=0.02, x="edge_grid",
                  ks=[1, 22, 31, 32, 33, 512], seed=505),
+    # a draft-vocabulary subset: 49,152 of a 131,072-token head of width 4,096, FP8 rows
+    "subset_head": dict(H=4096, V=131072, n_draft=49152, rows=[1, 16], fmt="fp8_row",
+                        w_std=0.02, x="normal", ks=[1, 64, 512], seed=606),
 }
 
 # Edge workload planting (rows of the 16-row activation matrix).
@@ -152,6 +156,19 @@ def random_head(V, H, seed, std=1.0):
 
 def random_acts(R, H, seed, std=1.0):
     return to_bf16_bits(normal_f32(R * H, seed, STREAM_ACTS, std=std)).reshape(R, H)
+
+
+def token_ids(V, n, seed):
+    """n distinct token ids of [0, V), drawn uniformly and sorted (int32): the stand-in for a
+    draft vocabulary's id list."""
+    rng = np.random.default_rng([seed, STREAM_IDS, V, n])
+    return np.sort(rng.choice(V, size=n, replace=False)).astype(np.int32)
+
+
+def draft_ids(name):
+    """The draft vocabulary's token ids of a subset workload."""
+    c = CONFIGS[name]
+    return token_ids(c["V"], c["n_draft"], c["seed"])
 
 
 def logit_rows(R, V, seed, kind):

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     L = dh.lib()
     names = declared_functions()
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
-                          "dh_workspace_bytes", "dh_status_string"}
+                          "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
+                          "dh_topk_mapped", "dh_draft_mapped"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -173,3 +174,56 @@ def test_quantize_refusals(no_device):
     assert L.dh_quantize(dh.FP8_ROW, w.p, 64, 64, None, s.p, None) == 1
     assert L.dh_quantize(dh.FP8_BLOCK32, w.p, 64, 64, w.p, s.p, None) == 1   # overlap
     assert c.untouched() and s.untouched()
+
+
+def test_subset_refusals(no_device):
+    """dh_gather_rows, dh_topk_mapped and dh_draft_mapped refuse on the host."""
+    L = dh.lib()
+    V, H, n = 600, 64, 40
+    w, wd, s, blk = HostBuf(V * H), HostBuf(V * H * 2), HostBuf(V * 4), HostBuf(1024)
+    ids_in = HostBuf(n * 4, fill=0)
+    ow, os_ = HostBuf(n * H * 2), HostBuf(n * 4)
+    row = head(dh.FP8_ROW, V, H, w, s)
+    bf = head(dh.BF16, V, H, wd)
+    g = lambda h, i=ids_in, nn=n, o=ow, sc=os_: L.dh_gather_rows(
+        ctypes.byref(h), i.p if i else None, nn, o.p if o else None, sc.p if sc else None, None)
+    assert g(head(dh.FP8_BLOCK32, V, H, w, blk)) == 2     # 32x32 blocks cannot be split
+    assert g(row, nn=0) == 1
+    assert g(row, i=None) == 1 and g(row, o=None) == 1
+    assert g(row, sc=None) == 1                           # per-row FP8 needs the scale out
+    assert g(bf, sc=os_) == 1                             # bf16 has no scale
+    assert g(row, o=w) == 1                               # output overlaps the head
+    assert g(row, sc=ids_in) == 1                         # scale out overlaps the ids
+    assert L.dh_gather_rows(ctypes.byref(row), ids_in.p, n,
+                            ctypes.c_void_p(ow.a.ctypes.data + 8), os_.p, None) == 1
+    assert ow.untouched() and os_.untouched()
+
+    R, k = 2, 8
+    lg, ti, tv, am = HostBuf(R * n * 4), HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * 4)
+    idmap = HostBuf(n * 4, fill=0)
+    ws = HostBuf(dh.workspace_bytes(R, n, k))
+    t = lambda m=idmap, i=ti, kk=k: L.dh_topk_mapped(lg.p, R, n, kk, m.p if m else None,
+                                                     i.p, tv.p, am.p, ws.p, ws.a.size, None)
+    assert t(m=None) == 1
+    assert t(kk=n + 1) == 1
+    assert t(i=idmap) == 1                                # ids overlap the map
+    assert ti.untouched() and tv.untouched() and am.untouched()
+
+    sub = head(dh.FP8_ROW, n, H, HostBuf(n * H), HostBuf(n * 4))
+    x, ex, dr = HostBuf(R * H * 2), HostBuf(R * k * 4), HostBuf(R * 4)
+    dws = HostBuf(dh.workspace_bytes(R, n, k))
+
+    def d(m=idmap, dense=bf, exact=ex, i=ti):
+        return L.dh_draft_mapped(ctypes.byref(sub), m.p if m else None,
+                                 ctypes.byref(dense) if dense else None, x.p, R, k, i.p,
+                                 tv.p, dr.p, exact.p if exact else None, None, dws.p,
+                                 dws.a.size, None)
+
+    assert d(m=None) == 1
+    assert d(dense=head(dh.BF16, V, 96, HostBuf(V * 96 * 2))) == 1   # other width
+    assert d(dense=row) == 1                                         # dense not bf16
+    assert d(exact=None) == 1
+    assert d(i=idmap) == 1                                           # ids overlap the map
+    assert d(dense=None, exact=idmap) == 1
+    for b in (ti, tv, ex, dr):
+        assert b.untouched()

@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="main step only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--subset-only", action="store_true",
+                    help="only the draft-vocabulary subset comparison (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the projection "
@@ -139,6 +141,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.subset_only:
+        print(json.dumps({"subset_head": subset_sweep(dh, torch, args.calls)}), flush=True)
+        return
     name = "row_sweep"
     c = synth.CONFIGS[name]
     V, H, K = c["V"], c["H"], 64

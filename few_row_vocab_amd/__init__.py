@@ -4,9 +4,10 @@ The product is the C-ABI library libdh.so (include/dh.h) built from csrc/*.hip; 
 holds it, its build script and a thin Python binding (dh.py).
 """
 from . import dh
-from .dh import (BF16, FP8_BLOCK32, FP8_ROW, DHError, Head, draft, draft_mapped, gather_rows,
-                 gemv, quantize, rescore, topk, topk_mapped, workspace, workspace_bytes)
+from .dh import (BF16, FP8_BLOCK32, FP8_ROW, OUT_ADD_BF16, OUT_BF16, OUT_F32, DHError, Head,
+                 draft, draft_mapped, gather_rows, gemv, linear, quantize, rescore, topk,
+                 topk_mapped, workspace, workspace_bytes)
 
-__all__ = ["dh", "BF16", "FP8_BLOCK32", "FP8_ROW", "DHError", "Head", "draft", "draft_mapped",
-           "gather_rows", "gemv", "quantize", "rescore", "topk", "topk_mapped", "workspace",
-           "workspace_bytes"]
+__all__ = ["dh", "BF16", "FP8_BLOCK32", "FP8_ROW", "OUT_ADD_BF16", "OUT_BF16", "OUT_F32",
+           "DHError", "Head", "draft", "draft_mapped", "gather_rows", "gemv", "linear",
+           "quantize", "rescore", "topk", "topk_mapped", "workspace", "workspace_bytes"]

@@ -132,6 +132,28 @@ dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *l
     return device_status(dh::launch_gemv(*head, x, rows, logits, (hipStream_t)stream));
 }
 
+dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                    const uint16_t *residual, void *out, void *stream)
+{
+    DH_TRY(check_head(w));
+    DH_TRY(check_rows(rows));
+    if (mode != DH_OUT_F32 && mode != DH_OUT_BF16 && mode != DH_OUT_ADD_BF16)
+        return DH_ERR_INVALID;
+    const size_t ob = mode == DH_OUT_F32 ? 4 : 2;
+    if (!x || !out || !aligned(x, 16) || !aligned(out, ob))
+        return DH_ERR_INVALID;
+    if ((mode == DH_OUT_ADD_BF16) != (residual != nullptr) || (residual && !aligned(residual, 2)))
+        return DH_ERR_INVALID;
+    const Span so = span(out, (size_t)rows * (size_t)w->vocab * ob);
+    if (overlap(so, head_weight(*w)) || overlap(so, head_scale(*w)) ||
+        overlap(so, span(x, (size_t)rows * (size_t)w->hidden * 2)))
+        return DH_ERR_INVALID;
+    if (residual && (const void *)residual != out && overlap(so, span(residual, so.hi - so.lo)))
+        return DH_ERR_INVALID;
+    return device_status(
+        dh::launch_linear(*w, x, rows, mode, residual, out, (hipStream_t)stream));
+}
+
 size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k)
 {
     if (check_rows(rows) != DH_OK || vocab < 1 || vocab > DH_MAX_VOCAB ||

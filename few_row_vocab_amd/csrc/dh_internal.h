@@ -48,6 +48,9 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
 // hipError_t of its launches.
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream);
+// The same GEMV with an output mode (dh_out_mode): fp32, bf16, or bf16 of residual + sum.
+hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
+                         const uint16_t *residual, void *out, hipStream_t stream);
 // idmap: NULL, or the vocabulary id of each logit column (ids and argmax are mapped).
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,

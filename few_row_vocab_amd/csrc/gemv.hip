@@ -43,7 +43,10 @@ struct GemvArgs {
     const uint8_t *bscale;  // E8M0 [ceil(V/32)][H/32] (block format)
     const float *rscale;    // fp32 [V] (row format)
     const uint16_t *x;      // bf16 [R][H]
-    float *logits;          // fp32 [R][V]
+    float *logits;          // fp32 [R][V] (mode DH_OUT_F32)
+    uint16_t *out16;        // bf16 [R][V] (modes DH_OUT_BF16, DH_OUT_ADD_BF16)
+    const uint16_t *residual;   // bf16 [R][V] (mode DH_OUT_ADD_BF16; may equal out16)
+    int mode;               // dh_out_mode
     int64_t V;
     int H;
     int R;
@@ -81,6 +84,9 @@ __device__ inline void widen16(u32x4 q, float scale, bf16x8 &a0, bf16x8 &a1)
     a0 = p0.v;
     a1 = p1.v;
 }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // An E8M0 byte as the fp32 scale operand: the bit pattern b << 23, which is the power of
 // two 2^(b-127) for bytes 1..254.
@@ -276,7 +282,15 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
                 float s = stage[t * OUTS + c * 16 + i];
                 if (FMT == DH_FP8_ROW)
                     s *= a.rscale[v];
-                a.logits[(int64_t)c * V + v] = s;
+                const int64_t at = (int64_t)c * V + v;
+                if (a.mode == DH_OUT_F32) {
+                    a.logits[at] = s;
+                } else {
+                    // the sum, plus the residual for the add mode, rounded to bf16 once
+                    if (a.mode == DH_OUT_ADD_BF16)
+                        s += __uint_as_float((uint32_t)a.residual[at] << 16);
+                    a.out16[at] = bf16_bits(s);
+                }
             }
         }
     }
@@ -349,13 +363,22 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream)
 {
+    return launch_linear(head, x, rows, DH_OUT_F32, nullptr, logits, stream);
+}
+
+hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
+                         const uint16_t *residual, void *out, hipStream_t stream)
+{
     GemvArgs a;
     a.w = static_cast<const uint8_t *>(head.weight);
     a.bscale = head.format == DH_FP8_BLOCK32 ? static_cast<const uint8_t *>(head.scale)
                                              : nullptr;
     a.rscale = head.format == DH_FP8_ROW ? static_cast<const float *>(head.scale) : nullptr;
     a.x = x;
-    a.logits = logits;
+    a.logits = mode == DH_OUT_F32 ? static_cast<float *>(out) : nullptr;
+    a.out16 = mode == DH_OUT_F32 ? nullptr : static_cast<uint16_t *>(out);
+    a.residual = mode == DH_OUT_ADD_BF16 ? residual : nullptr;
+    a.mode = mode;
     a.V = head.vocab;
     a.H = (int)head.hidden;
     a.R = rows;

@@ -19,6 +19,10 @@ FP8_BLOCK32 = 1
 FP8_ROW = 2
 FORMATS = {"bf16": BF16, "fp8_block32": FP8_BLOCK32, "fp8_row": FP8_ROW}
 
+OUT_F32 = 0
+OUT_BF16 = 1
+OUT_ADD_BF16 = 2
+
 MAX_ROWS = 16
 MAX_K = 512
 MAX_HIDDEN = 8192
@@ -59,6 +63,7 @@ def lib():
         L.dh_draft.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
         L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
+        L.dh_linear.argtypes = [hp, vp, i32, i32, vp, vp, vp]
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_mapped.argtypes = [hp, vp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_workspace_bytes.argtypes = [i32, i64, i32]
@@ -66,7 +71,7 @@ def lib():
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
-                  L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped):
+                  L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear):
             f.restype = i32
         _lib = L
     return _lib
@@ -151,6 +156,23 @@ def gemv(head: Head, x, logits=None, stream=None):
     h = head._c()
     _check(lib().dh_gemv(ctypes.byref(h), _ptr(x), R, _ptr(logits), _stream(stream)))
     return logits
+
+
+def linear(w: Head, x, mode=OUT_F32, residual=None, out=None, stream=None):
+    """out [R][N] = x [R][K] (bf16) times the linear w [N][K]: float32 (OUT_F32), bf16
+    (OUT_BF16) or bf16 of residual + the sum (OUT_ADD_BF16; out may be residual)."""
+    _want(x, x.dtype if x.dtype in (torch.bfloat16, torch.int16) else torch.bfloat16, "x")
+    R = x.shape[0]
+    if out is None:
+        dt = torch.float32 if mode == OUT_F32 else torch.int16
+        out = torch.empty((R, w.vocab), dtype=dt, device=x.device)
+    _want(out, out.dtype, "out")
+    if residual is not None:
+        _want(residual, residual.dtype, "residual")
+    h = w._c()
+    _check(lib().dh_linear(ctypes.byref(h), _ptr(x), R, mode, _ptr(residual), _ptr(out),
+                           _stream(stream)))
+    return out
 
 
 def _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream):

@@ -88,6 +88,26 @@ typedef struct dh_head {
 dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *logits,
                   void *stream);
 
+/* Output modes of dh_linear.  [TFE] commit notes on the head's own GEMV: its few-row
+ * kernels write fp32, bf16, or the bf16 sum added to a bf16 row (the residual stream), and
+ * that add is rounded once. */
+typedef enum { DH_OUT_F32 = 0, DH_OUT_BF16 = 1, DH_OUT_ADD_BF16 = 2 } dh_out_mode;
+
+/* dh_linear -- one of the draft head's own linears through the same few-row GEMV: with
+ * s[r][n] = sum_k x[r][k] * w[n][k] (the weight as a dh_head: `vocab` = N output features,
+ * `hidden` = K input features, any format; [TFE] commit notes: the wo and w2 linears go
+ * through the own GEMV, FP8 with a row scale among the forms it loads), out[r][n] is
+ *   DH_OUT_F32:      s, float32 [rows][N];
+ *   DH_OUT_BF16:     bf16(s), bf16 bits [rows][N];
+ *   DH_OUT_ADD_BF16: bf16(residual[r][n] + s), bf16 bits [rows][N], one rounding to bf16
+ *                    of the fp32 sum.
+ * residual: device bf16 bits [rows][N] for DH_OUT_ADD_BF16 (else NULL); it may be `out`
+ * itself (in place) but must not overlap it otherwise.  Sums as dh_gemv (fp32, a fixed
+ * order independent of `rows`); bf16 rounding is to nearest even.  out: 4-byte aligned
+ * (float32) or 2-byte aligned (bf16).  Rows 1..DH_MAX_ROWS. */
+dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                    const uint16_t *residual, void *out, void *stream);
+
 /* dh_topk -- per row, the k best logits in order: entry u beats entry v iff u is eligible
  * and (v is not, or l_u > l_v, or l_u == l_v and u < v); NaN and -inf are not eligible, so
  * they are never returned; -0 == +0.  Slot j holds the entry that exactly j others beat.

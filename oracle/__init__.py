@@ -52,6 +52,11 @@ def lib():
         L.orc_subset_rows.restype = None
         L.orc_subset_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                       c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
+        L.orc_bf16_encode.restype = c.c_uint16
+        L.orc_bf16_encode.argtypes = [c.c_double]
+        L.orc_linear.restype = None
+        L.orc_linear.argtypes = [c.c_int, c.c_void_p, c.c_void_p, c.c_int64, c.c_int64,
+                                 c.c_void_p, c.c_int, c.c_int, c.c_void_p, c.c_void_p]
         L.orc_rescore.restype = None
         L.orc_rescore.argtypes = [c.c_void_p, c.c_int64, c.c_int64, c.c_void_p, c.c_int,
                                   c.c_void_p, c.c_void_p, c.c_int, c.c_void_p, c.c_void_p]
@@ -132,6 +137,42 @@ def gemv(fmt, w, scale, x, vids=None):
         nv = V
     out = np.empty((R, nv), np.float32)
     lib().orc_gemv(fmt, _p(w), _p(scale), V, H, _p(x), R, _p(vids), nv, _p(out))
+    return out
+
+
+def bf16_encode(d):
+    """O14a: bf16 bits of a real number (round to nearest even, one rounding)."""
+    return int(lib().orc_bf16_encode(float(d)))
+
+
+MODE_F32, MODE_BF16, MODE_ADD_BF16 = 0, 1, 2
+
+
+def linear(fmt, w, scale, x, mode, residual=None):
+    """O14.  w [N][K] in any storage format (as gemv), x bf16 bits [R][K]; mode 0 -> float32
+    [R][N], mode 1 -> bf16 bits [R][N], mode 2 -> bf16 bits of residual + the sum."""
+    w = np.ascontiguousarray(w)
+    N, K = w.shape
+    x = _c(x, np.uint16)
+    R = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x width != weight width")
+    if fmt == FMT_BF16:
+        w, scale = _c(w, np.uint16), None
+    elif fmt == FMT_FP8_BLOCK32:
+        w, scale = _c(w, np.uint8), _c(scale, np.uint8)
+    elif fmt == FMT_FP8_ROW:
+        w, scale = _c(w, np.uint8), _c(scale, np.float32)
+    else:
+        raise ValueError("format")
+    if mode == MODE_ADD_BF16:
+        residual = _c(residual, np.uint16)
+        if residual.shape != (R, N):
+            raise ValueError("residual shape")
+    else:
+        residual = None
+    out = np.empty((R, N), np.float32 if mode == MODE_F32 else np.uint16)
+    lib().orc_linear(fmt, _p(w), _p(scale), N, K, _p(x), R, mode, _p(residual), _p(out))
     return out
 
 

@@ -15,7 +15,7 @@
  * rounded once to float.  Build with -O2 -ffp-contract=off and no fast-math, so that the
  * compiler neither fuses nor reorders the sums and NaN/inf follow IEEE rules.
  *
- * Numbering O1..O13 / Q1..Q2 is the oracle's own list of definitions, restated in the
+ * Numbering O1..O14 / Q1..Q2 is the oracle's own list of definitions, restated in the
  * comments of each function.
  */
 #include <math.h>
@@ -106,6 +106,66 @@ void orc_gemv(int fmt, const void *w, const void *scale, int64_t V, int64_t H,
         }
         for (int r = 0; r < R; r++)
             out[(int64_t)r * nv + j] = (float)acc[r];
+    }
+}
+
+/* O14a: the bf16 encoding of a real number, rounded to nearest with ties to even: 8
+ * significant bits, float's exponent range, a quantum of 2^-133 below 2^-126 (subnormals),
+ * infinity once the rounded magnitude reaches 2^128; NaN encodes as 0x7fc0.  Taken straight
+ * from the double, so there is a single rounding. */
+uint16_t orc_bf16_encode(double d)
+{
+    if (isnan(d))
+        return 0x7fc0;
+    const uint16_t sign = signbit(d) ? 0x8000 : 0;
+    const double a = fabs(d);
+    if (isinf(a))
+        return sign | 0x7f80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                              /* a in [2^(e-1), 2^e) */
+    int q = e - 8;                             /* the quantum of 8 significant bits */
+    if (q < -133)
+        q = -133;
+    const double v = ldexp(nearbyint(ldexp(a, -q)), q);   /* to nearest, ties to even */
+    if (v >= ldexp(1.0, 128))
+        return sign | 0x7f80;
+    const float f = (float)v;                  /* exact: at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* O14: a linear of the head's own layers through the few-row GEMV ([TFE] commit notes on
+ * the own GEMV: fp32 output, bf16 output, or the sum added to a bf16 row, that add rounded
+ * once).  With s = sum over k of x[r][k] * w[n][k] in double, increasing k (as O5):
+ *   mode 0: out_f32[r][n] = float(s);
+ *   mode 1: out_bf16[r][n] = O14a(s);
+ *   mode 2: out_bf16[r][n] = O14a(residual[r][n] + s), the add in double.
+ * w is [N][K] in any storage format (O4); out is float [R][N] (mode 0) or bf16 bits. */
+void orc_linear(int fmt, const void *w, const void *scale, int64_t N, int64_t K,
+                const uint16_t *x, int R, int mode, const uint16_t *residual, void *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        double acc[64];
+        for (int r = 0; r < R; r++)
+            acc[r] = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double wv = weight_value(fmt, w, scale, K, n, k);
+            for (int r = 0; r < R; r++)
+                acc[r] += orc_bf16_value(x[(int64_t)r * K + k]) * wv;
+        }
+        for (int r = 0; r < R; r++) {
+            const int64_t at = (int64_t)r * N + n;
+            if (mode == 0)
+                ((float *)out)[at] = (float)acc[r];
+            else if (mode == 1)
+                ((uint16_t *)out)[at] = orc_bf16_encode(acc[r]);
+            else
+                ((uint16_t *)out)[at] = orc_bf16_encode(orc_bf16_value(residual[at]) + acc[r]);
+        }
     }
 }
 

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
-                          "dh_topk_mapped", "dh_draft_mapped"}
+                          "dh_topk_mapped", "dh_draft_mapped", "dh_linear"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -227,3 +227,22 @@ def test_subset_refusals(no_device):
     assert d(dense=None, exact=idmap) == 1
     for b in (ti, tv, ex, dr):
         assert b.untouched()
+
+
+def test_linear_refusals(no_device):
+    L = dh.lib()
+    N, K, R = 96, 64, 2
+    w, s, x = HostBuf(N * K), HostBuf(N * 4), HostBuf(R * K * 2)
+    out, res = HostBuf(R * N * 4), HostBuf(R * N * 2)
+    h = head(dh.FP8_ROW, N, K, w, s)
+    c = lambda mode, r=res, o=out, rows=R: L.dh_linear(ctypes.byref(h), x.p, rows, mode,
+                                                       r.p if r else None, o.p, None)
+    assert c(3, r=None) == 1                       # unknown mode
+    assert c(dh.OUT_ADD_BF16, r=None) == 1         # the add mode needs a residual
+    assert c(dh.OUT_BF16) == 1                     # only the add mode takes one
+    assert c(dh.OUT_F32, r=None, rows=17) == 2
+    assert c(dh.OUT_F32, r=None, o=w) == 1         # out overlaps the weight
+    part = ctypes.c_void_p(out.a.ctypes.data + 2)
+    assert L.dh_linear(ctypes.byref(h), x.p, R, dh.OUT_ADD_BF16, out.p, part, None) == 1
+    assert L.dh_linear(ctypes.byref(h), x.p, R, dh.OUT_F32, None, part, None) == 1  # misaligned
+    assert out.untouched() and res.untouched()

@@ -244,6 +244,7 @@ def main():
     if not args.quick:
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
         out["subset_head"] = subset_sweep(dh, torch, args.calls)
+        out["lowrank_two_stage"] = lowrank_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
@@ -382,6 +383,43 @@ def subset_sweep(dh, torch, n):
             f"({tf / ts:.2f}x)")
     log(f"subset gather: {gat:.1f} us ({gbytes / (gat * 1e-6) / 1e9:.0f} GB/s)")
     return res
+
+
+def lowrank_sweep(dh, torch, n):
+    """The two-stage head with a low-rank stage 1: bf16 factors of rank 512 (H=5120,
+    V=129280), 16 rows, the top 512 candidates rescored from the dense bf16 head; each
+    launch of dh_draft_lowrank and of its parts, back to back, over rotated factor copies."""
+    import synth
+    name = "lowrank"
+    c = synth.CONFIGS[name]
+    V, H, rk, k = c["V"], c["H"], c["rank"], c["ks"][0]
+    R = max(c["rows"])
+    dev = torch.device("cuda:0")
+    down, up = synth.lowrank_factors(name)
+    dn = torch.from_numpy(down.view(np.int16)).to(dev)
+    ups = [torch.from_numpy(up.view(np.int16)).to(dev) for _ in range(NCOPY)]
+    dense = dh.Head(dh.BF16, torch.from_numpy(synth.head_bf16(name).view(np.int16)).to(dev))
+    x = torch.from_numpy(synth.activations(name, R).view(np.int16)).to(dev)
+    hd = dh.Head(dh.BF16, dn)
+    hu = [dh.Head(dh.BF16, u) for u in ups]
+    ws = dh.workspace(R, V, k)
+    o = {"ids": torch.empty((R, k), dtype=torch.int32, device=dev),
+         "vals": torch.empty((R, k), dtype=torch.float32, device=dev),
+         "draft": torch.empty((R,), dtype=torch.int32, device=dev),
+         "exact": torch.empty((R, k), dtype=torch.float32, device=dev),
+         "t": torch.empty((R, rk), dtype=torch.int16, device=dev)}
+    lg = torch.empty((R, V), dtype=torch.float32, device=dev)
+    fd = lambda i: dh.draft_lowrank(hd, hu[i % NCOPY], x, k, dense=dense, ws=ws, out=o)
+    ft = lambda i: dh.linear(hd, x, dh.OUT_BF16, out=o["t"])
+    fu = lambda i: dh.gemv(hu[i % NCOPY], o["t"], lg)
+    d, td, tu = back_to_back_us(fd, n), back_to_back_us(ft, n), back_to_back_us(fu, n)
+    b = (rk * H * 2 + R * H * 2 + R * rk * 2) + (V * rk * 2 + R * V * 4) + R * k * H * 2
+    log(f"low-rank two-stage: draft {d:.1f} us back to back (down {td:.1f}, up {tu:.1f})")
+    return {"workload": f"rank {rk} bf16 factors, H={H}, V={V}, {R} rows, top {k} rescored "
+                        f"from the dense bf16 head",
+            "dh_draft_lowrank_us": d, "down_linear_us": td, "up_gemv_us": tu,
+            "up_gemv_GBps": round((V * rk * 2 + R * rk * 2 + R * V * 4) / (tu * 1e-6) / 1e9, 1),
+            "draft_GBps_upper_bytes": round(b / (d * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(w, x, V, H, R, K):

@@ -287,12 +287,14 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                                             draft, (hipStream_t)stream));
 }
 
-// dh_draft and dh_draft_mapped: with an id map the head is a subset head whose entry j is
-// vocabulary id idmap[j], and the dense head spans the whole vocabulary.
-static dh_status run_draft(const dh_head *head, const int32_t *idmap, const dh_head *dense,
-                           const uint16_t *x, int32_t rows, int32_t k, int32_t *ids,
-                           float *vals, int32_t *draft, float *exact, float *logits,
-                           void *workspace, size_t workspace_bytes, void *stream)
+// dh_draft, dh_draft_mapped and dh_draft_lowrank: with an id map the head is a subset head
+// whose entry j is vocabulary id idmap[j], and the dense head spans the whole vocabulary;
+// with `down` the stage-1 head is low rank: t = bf16(x down^T), and `head` projects t.
+static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t,
+                           const int32_t *idmap, const dh_head *dense, const uint16_t *x,
+                           int32_t rows, int32_t k, int32_t *ids, float *vals, int32_t *draft,
+                           float *exact, float *logits, void *workspace,
+                           size_t workspace_bytes, void *stream)
 {
     DH_TRY(check_head(head));
     DH_TRY(check_rows(rows));
@@ -301,10 +303,16 @@ static dh_status run_draft(const dh_head *head, const int32_t *idmap, const dh_h
     DH_TRY(check_k(k, head->vocab));
     if (!x || !aligned(x, 16) || !draft || !aligned(draft, 4) || (logits && !aligned(logits, 4)))
         return DH_ERR_INVALID;
+    if (down) {
+        DH_TRY(check_head(down));
+        if (down->vocab != head->hidden || !t || !aligned(t, 16))
+            return DH_ERR_INVALID;
+    }
+    const int64_t xw = down ? down->hidden : head->hidden;   // the width of x
     if (dense) {
         DH_TRY(check_head(dense));
         if (dense->format != DH_BF16 || (!idmap && dense->vocab != head->vocab) ||
-            dense->hidden != head->hidden || !exact)
+            dense->hidden != xw || !exact)
             return DH_ERR_INVALID;
     } else if (exact) {
         return DH_ERR_INVALID;
@@ -317,9 +325,10 @@ static dh_status run_draft(const dh_head *head, const int32_t *idmap, const dh_h
     float *L = logits ? logits : reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
     // The stage-1 outputs and the workspace must be clear of the inputs and of each other.
     const Span sl = span(L, lbytes), sw = span(workspace, tw.bytes);
-    const Span in[] = {head_weight(*head), head_scale(*head),
-                       span(x, (size_t)rows * (size_t)head->hidden * 2),
-                       dense ? head_weight(*dense) : Span{0, 0}};
+    const Span in[] = {head_weight(*head), head_scale(*head), span(x, (size_t)rows * xw * 2),
+                       dense ? head_weight(*dense) : Span{0, 0},
+                       down ? head_weight(*down) : Span{0, 0},
+                       down ? head_scale(*down) : Span{0, 0}};
     for (const Span &s : in)
         if (overlap(sl, s) || overlap(sw, s))
             return DH_ERR_INVALID;
@@ -339,8 +348,25 @@ static dh_status run_draft(const dh_head *head, const int32_t *idmap, const dh_h
                            {sl, sw, span(ids, (size_t)rows * k * 4),
                             span(vals, (size_t)rows * k * 4), span(draft, (size_t)rows * 4),
                             span(exact, exact ? (size_t)rows * k * 4 : 0)}));
+    if (down) {
+        // t is written by the first GEMV and read by the second: clear of everything else
+        const Span stt = span(t, (size_t)rows * (size_t)head->hidden * 2);
+        for (const Span &s : in)
+            if (overlap(stt, s))
+                return DH_ERR_INVALID;
+        const Span outs[] = {sl, sw, span(ids, (size_t)rows * k * 4),
+                             span(vals, (size_t)rows * k * 4), span(draft, (size_t)rows * 4),
+                             span(exact, exact ? (size_t)rows * k * 4 : 0)};
+        for (const Span &s : outs)
+            if (overlap(stt, s))
+                return DH_ERR_INVALID;
+    }
     const hipStream_t st = (hipStream_t)stream;
-    hipError_t e = dh::launch_gemv(*head, x, rows, L, st);
+    hipError_t e = hipSuccess;
+    if (down)
+        e = dh::launch_linear(*down, x, rows, DH_OUT_BF16, nullptr, t, st);
+    if (e == hipSuccess)
+        e = dh::launch_gemv(*head, down ? t : x, rows, L, st);
     if (e == hipSuccess)
         e = dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals, dense ? nullptr : draft,
                             workspace, st);
@@ -353,8 +379,8 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
                    int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
                    float *logits, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return run_draft(head, nullptr, dense, x, rows, k, ids, vals, draft, exact, logits,
-                   workspace, workspace_bytes, stream);
+    return run_draft(head, nullptr, nullptr, nullptr, dense, x, rows, k, ids, vals, draft,
+                     exact, logits, workspace, workspace_bytes, stream);
 }
 
 dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_head *dense,
@@ -364,8 +390,20 @@ dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_he
 {
     if (!idmap)
         return DH_ERR_INVALID;
-    return run_draft(head, idmap, dense, x, rows, k, ids, vals, draft, exact, logits, workspace,
-                   workspace_bytes, stream);
+    return run_draft(head, nullptr, nullptr, idmap, dense, x, rows, k, ids, vals, draft,
+                     exact, logits, workspace, workspace_bytes, stream);
+}
+
+dh_status dh_draft_lowrank(const dh_head *down, const dh_head *up, const dh_head *dense,
+                           const uint16_t *x, int32_t rows, int32_t k, uint16_t *t,
+                           int32_t *ids, float *vals, int32_t *draft, float *exact,
+                           float *logits, void *workspace, size_t workspace_bytes,
+                           void *stream)
+{
+    if (!down)
+        return DH_ERR_INVALID;
+    return run_draft(up, down, t, nullptr, dense, x, rows, k, ids, vals, draft, exact, logits,
+                     workspace, workspace_bytes, stream);
 }
 
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,

@@ -64,6 +64,8 @@ def lib():
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
         L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
         L.dh_linear.argtypes = [hp, vp, i32, i32, vp, vp, vp]
+        L.dh_draft_lowrank.argtypes = [hp, hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                       sz, vp]
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_mapped.argtypes = [hp, vp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_workspace_bytes.argtypes = [i32, i64, i32]
@@ -71,7 +73,8 @@ def lib():
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
-                  L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear):
+                  L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
+                  L.dh_draft_lowrank):
             f.restype = i32
         _lib = L
     return _lib
@@ -274,6 +277,32 @@ def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=F
         if idmap.numel() != head.vocab:
             raise ValueError(f"idmap: expected {head.vocab} ids, got {idmap.numel()}")
         _check(lib().dh_draft_mapped(ctypes.byref(h), _ptr(idmap), dref, *tail))
+    return o
+
+
+def draft_lowrank(down: Head, up: Head, x, k, dense: Optional[Head] = None, ws=None,
+                  keep_logits=False, out=None, stream=None):
+    """dh_draft_lowrank: t = bf16(x down^T), logits = t up^T, then the draft (dict with ids,
+    vals, draft, t (+ exact, logits))."""
+    R = x.shape[0]
+    dev = x.device
+    o = {} if out is None else out
+    o.setdefault("ids", torch.empty((R, k), dtype=torch.int32, device=dev))
+    o.setdefault("vals", torch.empty((R, k), dtype=torch.float32, device=dev))
+    o.setdefault("draft", torch.empty((R,), dtype=torch.int32, device=dev))
+    o.setdefault("t", torch.empty((R, down.vocab), dtype=torch.int16, device=dev))
+    if dense is not None:
+        o.setdefault("exact", torch.empty((R, k), dtype=torch.float32, device=dev))
+    if keep_logits:
+        o.setdefault("logits", torch.empty((R, up.vocab), dtype=torch.float32, device=dev))
+    _want(o["t"], o["t"].dtype if o["t"].dtype == torch.bfloat16 else torch.int16, "t")
+    ws = workspace(R, up.vocab, k, dev) if ws is None else ws
+    hd, hu = down._c(), up._c()
+    d = dense._c() if dense is not None else None
+    _check(lib().dh_draft_lowrank(
+        ctypes.byref(hd), ctypes.byref(hu), ctypes.byref(d) if d is not None else None,
+        _ptr(x), R, k, _ptr(o["t"]), _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
+        _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(), _stream(stream)))
     return o
 
 

@@ -163,6 +163,23 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream);
 
+/* dh_draft_lowrank -- dh_draft with a low-rank stage 1.  [TFE] two_stage commit note and
+ * 'Update': the two_stage head takes its top cand_k candidates from low-rank logits and
+ * drafts the argmax of their exact logits from a dense bf16 copy of the target's head.
+ *   t[r][j]      = bf16(sum_h x[r][h] * down[j][h])   (dh_linear, DH_OUT_BF16)
+ *   logits[r][v] = sum_j t[r][j] * up[v][j]           (dh_gemv, fp32)
+ * then dh_draft's top-k and argmax, and with `dense` its rescore from x.  down: a dh_head
+ * with `vocab` = the rank and `hidden` = H; up: `vocab` = V, `hidden` = the rank; any
+ * format each.  dense: bf16 [V][H] or NULL (one stage).  t: device bf16 bits [rows][rank],
+ * 16-byte aligned, written (the rank-r activations; the pages do not give their precision,
+ * and like every GEMM input on those pages they are bf16).  Other arguments, refusals and
+ * the workspace (dh_workspace_bytes(rows, V, k)) as dh_draft. */
+dh_status dh_draft_lowrank(const dh_head *down, const dh_head *up, const dh_head *dense,
+                           const uint16_t *x, int32_t rows, int32_t k, uint16_t *t,
+                           int32_t *ids, float *vals, int32_t *draft, float *exact,
+                           float *logits, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
 /* Draft-vocabulary subset heads.  [SUPER] 'What this changes': a draft head packs the FP8
  * rows of its draft vocabulary's ids into a weight of their own (keeping the head's scales)
  * and uploads their vocabulary ids; a level projects over that subset only, and the ids it

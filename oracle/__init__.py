@@ -223,6 +223,27 @@ def subset_rows(fmt, w, scale, ids):
     return out, out_s
 
 
+def draft_lowrank(down, up, x, k, dense_w=None, t=None):
+    """O15: O11 with a low-rank stage 1 ([TFE] two_stage commit note: the candidates come
+    from low-rank logits).  down = (fmt, w [rank][H], scale), up = (fmt, w [V][rank], scale):
+    t = O14 mode 1 of x through down (bf16 bits [R][rank]); logits = O5 of t through up;
+    then O8 and, with dense_w, O10 from x.  `t` given: the conditional form, which takes
+    that t (the GPU's) instead of its own.  Returns dict with t, logits, ids, vals, draft
+    (+ exact)."""
+    if t is None:
+        t = linear(down[0], down[1], down[2], x, MODE_BF16)
+    logits = gemv(up[0], up[1], up[2], t)
+    ids, vals = topk(logits, k)
+    out = {"t": t, "logits": logits, "ids": ids, "vals": vals}
+    if dense_w is None:
+        out["draft"] = ids[:, 0].copy()
+    else:
+        exact, d = rescore(dense_w, x, ids, vals > -np.inf)
+        out["exact"] = exact
+        out["draft"] = d
+    return out
+
+
 def draft_mapped(fmt, w, scale, idmap, x, k, dense_w=None):
     """O11 on a subset head (O12) whose row j is token idmap[j], with O13's top-k; the
     two-stage dense head spans the whole vocabulary."""

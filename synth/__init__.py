@@ -38,6 +38,9 @@ CONFIGS = {
                       x="normal", ks=[512], seed=404),
     "edge": dict(H=7168, V=163840, rows=[16], fmt="fp8_block32", w_std=0.02, x="edge_grid",
                  ks=[1, 22, 31, 32, 33, 512], seed=505),
+    # a low-rank stage 1 (rank 512, bf16 factors) with the dense bf16 head for the rescore
+    "lowrank": dict(H=5120, V=129280, rank=512, rows=[16], fmt="bf16", w_std=0.02,
+                    x="normal", ks=[512], seed=707),
     # a draft-vocabulary subset: 49,152 of a 131,072-token head of width 4,096, FP8 rows
     "subset_head": dict(H=4096, V=131072, n_draft=49152, rows=[1, 16], fmt="fp8_row",
                         w_std=0.02, x="normal", ks=[1, 64, 512], seed=606),
@@ -156,6 +159,16 @@ def random_head(V, H, seed, std=1.0):
 
 def random_acts(R, H, seed, std=1.0):
     return to_bf16_bits(normal_f32(R * H, seed, STREAM_ACTS, std=std)).reshape(R, H)
+
+
+def lowrank_factors(name):
+    """(down [rank][H], up [V][rank]) bf16 bits of a low-rank workload: down ~ N(0, 1/H), so
+    the rank-r activations of N(0, 1) rows are about N(0, 1), and up ~ N(0, w_std^2)."""
+    c = CONFIGS[name]
+    H, V, rk = c["H"], c["V"], c["rank"]
+    down = normal_bf16((rk, H), c["seed"] + 1, STREAM_WEIGHTS, 1.0 / np.sqrt(np.float32(H)))
+    up = normal_bf16((V, rk), c["seed"] + 2, STREAM_WEIGHTS, c["w_std"])
+    return down, up
 
 
 def token_ids(V, n, seed):

@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
-                          "dh_topk_mapped", "dh_draft_mapped", "dh_linear"}
+                          "dh_topk_mapped", "dh_draft_mapped", "dh_linear",
+                          "dh_draft_lowrank"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -246,3 +247,30 @@ def test_linear_refusals(no_device):
     assert L.dh_linear(ctypes.byref(h), x.p, R, dh.OUT_ADD_BF16, out.p, part, None) == 1
     assert L.dh_linear(ctypes.byref(h), x.p, R, dh.OUT_F32, None, part, None) == 1  # misaligned
     assert out.untouched() and res.untouched()
+
+
+def test_lowrank_refusals(no_device):
+    L = dh.lib()
+    H, rk, V, R, k = 128, 64, 700, 2, 8
+    wd, wu, wdense = HostBuf(rk * H * 2), HostBuf(V * rk * 2), HostBuf(V * H * 2)
+    x, t = HostBuf(R * H * 2), HostBuf(R * rk * 2)
+    ids, vals, ex, dr = HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * 4)
+    ws = HostBuf(dh.workspace_bytes(R, V, k))
+    down, up = head(dh.BF16, rk, H, wd), head(dh.BF16, V, rk, wu)
+    dense = head(dh.BF16, V, H, wdense)
+
+    def c(dn=down, u=up, d=dense, tt=t, exact=ex):
+        return L.dh_draft_lowrank(ctypes.byref(dn) if dn else None, ctypes.byref(u),
+                                  ctypes.byref(d) if d else None, x.p, R, k,
+                                  tt.p if tt else None, ids.p, vals.p, dr.p,
+                                  exact.p if exact else None, None, ws.p, ws.a.size, None)
+
+    assert c(dn=None) == 1
+    assert c(tt=None) == 1                                     # t is required
+    assert c(u=head(dh.BF16, V, 96, wu)) == 1                  # up width != rank
+    assert c(d=head(dh.BF16, V, rk, wdense)) == 1              # dense width != H
+    assert c(tt=x) == 1                                        # t overlaps x
+    assert c(tt=ids) == 1                                      # t overlaps an output
+    assert c(d=None) == 1                                      # one stage with `exact`
+    for b in (ids, vals, ex, dr, t):
+        assert b.untouched()

@@ -337,7 +337,7 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
 def subset_sweep(dh, torch, n):
     """The draft-vocabulary subset head against the whole head it is gathered from: an FP8
     head with a row scale, H=4096, V=131072, and 49,152 of its rows with their token ids;
-    dh_draft on the whole head and dh_draft_mapped on the subset, top-64, 1 and 16 rows,
+    dh_draft on the whole head and dh_draft_mapped on the subset, top-64, 1, 16 and 32 rows,
     back to back over rotated copies (each subset copy is 201 MB, so three of them do not
     fit the 256 MB Infinity Cache), plus the gather itself."""
     import synth
@@ -346,7 +346,7 @@ def subset_sweep(dh, torch, n):
     V, H, nd, K = c["V"], c["H"], c["n_draft"], 64
     dev = torch.device("cuda:0")
     wd = torch.from_numpy(synth.head_bf16(name).view(np.int16)).to(dev)
-    x16 = torch.from_numpy(synth.activations(name, 16).view(np.int16)).to(dev)
+    x32 = torch.from_numpy(synth.activations(name, 32).view(np.int16)).to(dev)
     im = torch.from_numpy(synth.draft_ids(name)).to(dev)
     fulls, subs = [], []
     for i in range(NCOPY):
@@ -362,8 +362,8 @@ def subset_sweep(dh, torch, n):
                        f"sorted token ids; top-{K}",
            "gather_us": gat, "gather_bytes": gbytes,
            "gather_GBps": round(gbytes / (gat * 1e-6) / 1e9, 1), "rows": []}
-    for R in (1, 16):
-        x = x16[:R].contiguous()
+    for R in (1, 16, 32):
+        x = x32[:R].contiguous()
         ws_f, ws_s = dh.workspace(R, V, K), dh.workspace(R, nd, K)
         mk = lambda: {"ids": torch.empty((R, K), dtype=torch.int32, device=dev),
                       "vals": torch.empty((R, K), dtype=torch.float32, device=dev),

@@ -96,6 +96,17 @@ dh_status check_rows(int32_t rows)
     return DH_OK;
 }
 
+// A GEMV of more than 16 rows keeps 32 rows of activations in registers: H is limited.
+dh_status check_gemv_rows(int32_t rows, int64_t hidden)
+{
+    const dh_status st = check_rows(rows);
+    if (st != DH_OK)
+        return st;
+    if (rows > 16 && hidden > DH_MAX_HIDDEN_WIDE)
+        return DH_ERR_UNSUPPORTED;
+    return DH_OK;
+}
+
 dh_status check_k(int32_t k, int64_t vocab)
 {
     if (k < 1 || k > vocab)
@@ -122,7 +133,7 @@ dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *l
                   void *stream)
 {
     DH_TRY(check_head(head));
-    DH_TRY(check_rows(rows));
+    DH_TRY(check_gemv_rows(rows, head->hidden));
     if (!x || !logits || !aligned(x, 16) || !aligned(logits, 4))
         return DH_ERR_INVALID;
     const Span out = span(logits, (size_t)rows * (size_t)head->vocab * sizeof(float));
@@ -136,7 +147,7 @@ dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t m
                     const uint16_t *residual, void *out, void *stream)
 {
     DH_TRY(check_head(w));
-    DH_TRY(check_rows(rows));
+    DH_TRY(check_gemv_rows(rows, w->hidden));
     if (mode != DH_OUT_F32 && mode != DH_OUT_BF16 && mode != DH_OUT_ADD_BF16)
         return DH_ERR_INVALID;
     const size_t ob = mode == DH_OUT_F32 ? 4 : 2;
@@ -297,7 +308,7 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
                            size_t workspace_bytes, void *stream)
 {
     DH_TRY(check_head(head));
-    DH_TRY(check_rows(rows));
+    DH_TRY(check_gemv_rows(rows, head->hidden));
     if (head->vocab > DH_MAX_VOCAB)
         return DH_ERR_UNSUPPORTED;
     DH_TRY(check_k(k, head->vocab));
@@ -305,6 +316,7 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
         return DH_ERR_INVALID;
     if (down) {
         DH_TRY(check_head(down));
+        DH_TRY(check_gemv_rows(rows, down->hidden));
         if (down->vocab != head->hidden || !t || !aligned(t, 16))
             return DH_ERR_INVALID;
     }
@@ -432,8 +444,9 @@ const char *dh_status_string(int32_t status)
     case DH_OK: return "ok";
     case DH_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad format, "
                                 "bad size, or overlapping buffers)";
-    case DH_ERR_UNSUPPORTED: return "size outside the implemented limits (rows <= 16, "
-                                    "k <= 512, hidden <= 8192, vocab <= 262144)";
+    case DH_ERR_UNSUPPORTED: return "size outside the implemented limits (rows <= 32, "
+                                    "k <= 512, hidden <= 8192 (4096 above 16 rows), "
+                                    "vocab <= 262144)";
     case DH_ERR_WORKSPACE: return "workspace missing, misaligned or too small "
                                   "(see dh_workspace_bytes)";
     case DH_ERR_DEVICE: return "the HIP runtime reported an error at launch";

@@ -33,6 +33,11 @@ namespace dh {
 namespace {
 
 constexpr int kMaxWaves = 16;
+// 17..32 activation rows: two 16-row MFMA column blocks.  Their activations double the VGPRs a
+// wave holds, so such launches run half the waves (256 VGPRs each), each wave doing the work
+// of two waves of the 16-row launch with separate sums (so a row's sums are the same bits
+// as in a 16-row call), and take H <= 4096.
+constexpr int kMaxWaves2 = kMaxWaves / 2;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 constexpr int kCachePolicy = 0;          // plain loads: the non-temporal hint measured ~15% slower
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
@@ -96,46 +101,54 @@ __device__ inline float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23)
 // blocks split evenly over the waves), so no load needs a guard.
 // TR: 16-row MFMA groups per tile (a tile is 16 * TR head rows, inside one 32-row block
 // of scales); two groups double the bytes in flight and halve the barriers per byte.
-template <int FMT, int KBW, bool FULL, int TR>
-__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
+// NB: 16-row blocks of activation rows (1: up to 16 rows; 2: up to 32).  Each weight tile
+// is widened once and multiplied by every block.  A wave covers NB "virtual waves" of KBW
+// blocks each, the split of the 16-row launch, and keeps one sum per virtual wave.
+template <int FMT, int KBW, bool FULL, int TR, int NB>
+__global__ __launch_bounds__(NB == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(GemvArgs a)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
     constexpr int ES = FMT == DH_BF16 ? 2 : 1;   // bytes per weight element
     constexpr int TILE = 16 * TR;                // head rows per tile
-    constexpr int OUTS = TILE * 16;              // (head row, activation row) sums per tile
-    __shared__ float red[2][kMaxWaves][4 * TR][kWave];
-    extern __shared__ float stage[];             // [tile of this block][group][c][i]
+    constexpr int OUTS = TILE * 16 * NB;         // (head row, activation row) sums per tile
+    constexpr int KW = NB * KBW;                 // 64-column blocks of one wave
+    __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
+    extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
+    const int nvw = (a.nkb + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
     const int rr = lane & 15;
     const int g = lane >> 4;
     const int H = a.H;
     const int64_t V = a.V;
 
     // This wave's H-slice of the activations: the B operands of every tile.
-    bf16x8 xb[KBW][2];
+    bf16x8 xb[NB][KW][2];
 #pragma unroll
-    for (int kb = 0; kb < KBW; kb++) {
-        const int blk = wave * KBW + kb;
-        const int k0 = blk * 64 + 16 * g;
-        Pack8 p0, p1;
-        p0.q = u32x4{0u, 0u, 0u, 0u};
-        p1.q = u32x4{0u, 0u, 0u, 0u};
-        if (rr < a.R && (FULL || (blk < a.nkb && k0 < H))) {
-            const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)rr * H + k0);
-            p0.q = px[0];
-            p1.q = px[1];
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int kb = 0; kb < KW; kb++) {
+            const int blk = wave * KW + kb;
+            const int k0 = blk * 64 + 16 * g;
+            const int row = 16 * nb + rr;
+            Pack8 p0, p1;
+            p0.q = u32x4{0u, 0u, 0u, 0u};
+            p1.q = u32x4{0u, 0u, 0u, 0u};
+            if (row < a.R && (FULL || (blk < a.nkb && k0 < H))) {
+                const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)row * H + k0);
+                p0.q = px[0];
+                p1.q = px[1];
+            }
+            xb[nb][kb][0] = p0.v;
+            xb[nb][kb][1] = p1.v;
         }
-        xb[kb][0] = p0.v;
-        xb[kb][1] = p1.v;
-    }
 
     // One register slot per (group, 64-column block).  A slot is refilled with the next
     // tile's block as soon as its current contents have been widened, so a whole tile of
     // loads stays in flight (through the reduction below) with a single set of registers.
-    u32x4 raw[TR][KBW][RQ];
+    u32x4 raw[TR][KW][RQ];
 
     // Buffer loads: descriptors (SGPRs) are rebased on each tile, one per 16-row group, and
     // bounded by the group's existing rows, so rows past V read as zeros (a descriptor of
@@ -143,10 +156,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     // is the same for every tile, and a block adds a constant offset.  No load sits under
     // a branch, so the wait before each block is a fixed count of younger loads.
     const uint32_t wrow = (uint32_t)H * ES;
-    const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KBW * 64 + 16 * g) * ES;
-    const uint32_t sbase = (uint32_t)(2 * wave * KBW);
+    const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KW * 64 + 16 * g) * ES;
+    const uint32_t sbase = (uint32_t)(2 * wave * KW);
     auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], int kb) {
-        const int blk = wave * KBW + kb;
+        const int blk = wave * KW + kb;
         if (FULL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
 #pragma unroll
             for (int r = 0; r < TR; r++)
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
                     raw[r][kb][q] = u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // E8M0 scales of a tile: lane i loads byte i of this wave's 2 * KBW scale bytes (one
+    // E8M0 scales of a tile: lane i loads byte i of this wave's 2 * KW scale bytes (one
     // load per tile instead of one per block); a block's scale is then read from lane
     // 2 * kb (lanes with g < 2) or 2 * kb + 1 (the second 32 columns).  Bytes past the row
     // read as 0, which only meet zero codes.
@@ -195,7 +208,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         rsrcs(tile, true, wr, sr);
         sbytes = load_scales(sr);
 #pragma unroll
-        for (int kb = 0; kb < KBW; kb++)
+        for (int kb = 0; kb < KW; kb++)
             load_block(wr, kb);
     }
     int buf = 0, it = 0;
@@ -206,12 +219,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
         rsrcs(more ? next : tile, more, wr, sr);
         const uint32_t sbytes_next = load_scales(sr);
 
-        f32x4 acc[TR];
+        f32x4 acc[NB][NB][TR];                   // [act block][virtual wave][group]
 #pragma unroll
-        for (int r = 0; r < TR; r++)
-            acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-        for (int kb = 0; kb < KBW; kb++) {
+            for (int u = 0; u < NB; u++)
+#pragma unroll
+                for (int r = 0; r < TR; r++)
+                    acc[nb][u][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KW; kb++) {
             bf16x8 a0[TR], a1[TR];
 #pragma unroll
             for (int r = 0; r < TR; r++) {
@@ -235,31 +252,41 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
             // keep the refill here: the scheduler would otherwise sink every load below the
             // last MFMA, and the pipeline would drain once per tile
             __builtin_amdgcn_sched_barrier(0);
+            const int u = kb / KBW;              // the virtual wave of this block
 #pragma unroll
-            for (int r = 0; r < TR; r++) {
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[r], xb[kb][0], acc[r], 0, 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[r], xb[kb][1], acc[r], 0, 0, 0);
-            }
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int r = 0; r < TR; r++) {
+                    acc[nb][u][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a0[r], xb[nb][kb][0], acc[nb][u][r], 0, 0, 0);
+                    acc[nb][u][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a1[r], xb[nb][kb][1], acc[nb][u][r], 0, 0, 0);
+                }
         }
 
-        // acc[r][j] of lane l is the partial sum of head row 16r + 4*(l/16) + j of the tile
-        // for activation row l%16 over this wave's H-slice.  The waves' partials are summed
-        // in wave order and kept in LDS until the end, so the loop issues no stores.
+        // acc[nb][u][r][j] of lane l is the partial sum of head row 16r + 4*(l/16) + j of
+        // the tile for activation row 16nb + l%16 over virtual wave NB*wave + u's H-slice.
+        // The partials are summed in virtual-wave order and kept in LDS until the end, so
+        // the loop issues no stores.
 #pragma unroll
-        for (int r = 0; r < TR; r++)
+        for (int nb = 0; nb < NB; nb++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                red[buf][wave][4 * r + j][lane] = acc[r][j];
+            for (int u = 0; u < NB; u++)
+#pragma unroll
+                for (int r = 0; r < TR; r++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        red[buf][NB * wave + u][nb][4 * r + j][lane] = acc[nb][u][r][j];
         __syncthreads();
         for (int o = threadIdx.x; o < OUTS; o += blockDim.x) {
-            const int r = o >> 8;                  // row group
-            const int c = (o >> 4) & 15;           // activation row
+            const int r = o / (256 * NB);          // row group
+            const int c = (o >> 4) % (16 * NB);    // activation row
             const int i = o & 15;                  // head row within the group
-            const int src = c + 16 * (i >> 2);
+            const int src = (c & 15) + 16 * (i >> 2);
             const int j = 4 * r + (i & 3);
             float s = 0.f;
-            for (int w = 0; w < nw; w++)
-                s += red[buf][w][j][src];
+            for (int w = 0; w < nvw; w++)
+                s += red[buf][w][c >> 4][j][src];
             stage[it * OUTS + o] = s;
         }
         buf ^= 1;
@@ -296,14 +323,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a)
     }
 }
 
-template <int FMT, int KBW, bool FULL, int TR>
+template <int FMT, int KBW, bool FULL, int TR, int NB>
 hipError_t run(GemvArgs a, hipStream_t stream)
 {
     static int occ_cache[kMaxWaves + 1];
     static int lds_set[kMaxDevices];               // per device: the LDS limit has been raised
-    const int nw = (a.nkb + KBW - 1) / KBW;
+    const int nw = (a.nkb + NB * KBW - 1) / (NB * KBW);
     const int block = nw * kWave;
-    auto kern = gemv_kernel<FMT, KBW, FULL, TR>;
+    auto kern = gemv_kernel<FMT, KBW, FULL, TR, NB>;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -321,7 +348,7 @@ hipError_t run(GemvArgs a, hipStream_t stream)
     const int occ = occupancy(kern, block, occ_cache[nw]);
     int64_t grid = (int64_t)device_cus() * occ;
     // each block keeps its tiles' logits in LDS: at most kMaxStageBytes of them
-    const int64_t max_per = kMaxStageBytes / (TR * 256 * (int)sizeof(float));
+    const int64_t max_per = kMaxStageBytes / (TR * 256 * NB * (int)sizeof(float));
     const int64_t min_grid = (a.ntiles + max_per - 1) / max_per;
     if (grid < min_grid)
         grid = min_grid;
@@ -329,31 +356,40 @@ hipError_t run(GemvArgs a, hipStream_t stream)
         grid = a.ntiles;
     const int64_t per = (a.ntiles + grid - 1) / grid;
     return launch(kern, dim3((unsigned)grid), dim3(block),
-                  (size_t)per * TR * 256 * sizeof(float), stream, a);
+                  (size_t)per * TR * 256 * NB * sizeof(float), stream, a);
 }
 
-template <int FMT, int KBW>
+template <int FMT, int KBW, int NB>
 hipError_t run_kbw(const GemvArgs &a, hipStream_t stream)
 {
     constexpr int TR = 1;   // two groups measured slower: the loop is not latency-bound
-    if (a.H % 64 == 0 && a.nkb % KBW == 0)
-        return run<FMT, KBW, true, TR>(a, stream);
-    return run<FMT, KBW, false, TR>(a, stream);
+    if (a.H % 64 == 0 && a.nkb % (NB * KBW) == 0)
+        return run<FMT, KBW, true, TR, NB>(a, stream);
+    return run<FMT, KBW, false, TR, NB>(a, stream);
 }
 
 template <int FMT>
 hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
 {
-    const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;
+    const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;   // the 16-row split, for any R
+    if (a.R > 16) {
+        switch (kbw) {
+        case 1: return run_kbw<FMT, 1, 2>(a, stream);
+        case 2: return run_kbw<FMT, 2, 2>(a, stream);
+        case 3: return run_kbw<FMT, 3, 2>(a, stream);
+        case 4: return run_kbw<FMT, 4, 2>(a, stream);
+        default: return hipErrorInvalidValue;        // H > 4096 with more than 16 rows
+        }
+    }
     switch (kbw) {
-    case 1: return run_kbw<FMT, 1>(a, stream);
-    case 2: return run_kbw<FMT, 2>(a, stream);
-    case 3: return run_kbw<FMT, 3>(a, stream);
-    case 4: return run_kbw<FMT, 4>(a, stream);
-    case 5: return run_kbw<FMT, 5>(a, stream);
-    case 6: return run_kbw<FMT, 6>(a, stream);
-    case 7: return run_kbw<FMT, 7>(a, stream);
-    case 8: return run_kbw<FMT, 8>(a, stream);
+    case 1: return run_kbw<FMT, 1, 1>(a, stream);
+    case 2: return run_kbw<FMT, 2, 1>(a, stream);
+    case 3: return run_kbw<FMT, 3, 1>(a, stream);
+    case 4: return run_kbw<FMT, 4, 1>(a, stream);
+    case 5: return run_kbw<FMT, 5, 1>(a, stream);
+    case 6: return run_kbw<FMT, 6, 1>(a, stream);
+    case 7: return run_kbw<FMT, 7, 1>(a, stream);
+    case 8: return run_kbw<FMT, 8, 1>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -23,7 +23,8 @@ OUT_F32 = 0
 OUT_BF16 = 1
 OUT_ADD_BF16 = 2
 
-MAX_ROWS = 16
+MAX_ROWS = 32
+MAX_HIDDEN_WIDE = 4096
 MAX_K = 512
 MAX_HIDDEN = 8192
 MAX_VOCAB = 262144

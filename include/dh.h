@@ -2,7 +2,7 @@
  * dh.h -- C ABI of the few-row draft-head vocabulary projection for MI355X (gfx950).
  *
  * A speculative-decoding draft head ends in a projection of its last hidden rows onto the
- * vocabulary: a GEMV of 1..16 bf16 activation rows against a [V][H] head, fp32 logits, a
+ * vocabulary: a GEMV of 1..32 bf16 activation rows against a [V][H] head, fp32 logits, a
  * per-row top-k and argmax, and optionally a rescore of the top-k candidates against a dense
  * bf16 head.  Sources (web pages on one inference engine, cited by title and section):
  *   [TFE]   "dsv41 Zig: the TFE draft head (TF_DS_DRAFTER=eagle), off by default"
@@ -71,9 +71,13 @@ typedef struct dh_head {
 } dh_head;
 
 /* Limits of this implementation (refused with DH_ERR_UNSUPPORTED beyond them).
- * Rows: [TFE] commit notes -- the head's own GEMV takes up to 16 rows.
+ * Rows: [TFE] commit notes -- the head's own GEMV takes up to 16 rows; [SUPER] commit notes
+ * on 32-row windows -- calls of 17 to 32 rows take the few-row forms too, each giving the same
+ * bits as the 16-row form.  A GEMV of more than 16 rows needs H <= DH_MAX_HIDDEN_WIDE (the
+ * activations of 32 rows are held in registers).
  * k: [TFE] 'Update' -- the candidate count runs from 1 to 512. */
-#define DH_MAX_ROWS 16
+#define DH_MAX_ROWS 32
+#define DH_MAX_HIDDEN_WIDE 4096    /* GEMV calls with more than 16 rows */
 #define DH_MAX_K 512
 #define DH_MAX_HIDDEN 8192
 #define DH_MAX_VOCAB 262144        /* dh_topk / dh_draft */
@@ -83,7 +87,7 @@ typedef struct dh_head {
  * [TFE] commit notes: the own GEMV for up to 16 rows with fp32 output; 'What this changes':
  * fp32 sums.  x: device bf16 bits [rows][H], 16-byte aligned.  logits: device float32
  * [rows][V].  Summation order is fixed by the kernel and independent of `rows`, so a row's
- * logits are bitwise the same in a 1-row and a 16-row call.  NaN and infinities propagate
+ * logits are bitwise the same in a 1-row, a 16-row and a 32-row call.  NaN and infinities propagate
  * as in IEEE arithmetic. */
 dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *logits,
                   void *stream);

@@ -42,7 +42,7 @@ CONFIGS = {
     "lowrank": dict(H=5120, V=129280, rank=512, rows=[16], fmt="bf16", w_std=0.02,
                     x="normal", ks=[512], seed=707),
     # a draft-vocabulary subset: 49,152 of a 131,072-token head of width 4,096, FP8 rows
-    "subset_head": dict(H=4096, V=131072, n_draft=49152, rows=[1, 16], fmt="fp8_row",
+    "subset_head": dict(H=4096, V=131072, n_draft=49152, rows=[1, 16, 32], fmt="fp8_row",
                         w_std=0.02, x="normal", ks=[1, 64, 512], seed=606),
 }
 

@@ -40,7 +40,8 @@ def test_status_strings():
 def test_workspace_bytes_limits():
     assert dh.workspace_bytes(16, 163840, 512) > 16 * 163840 * 4
     assert dh.workspace_bytes(0, 1000, 8) == 0
-    assert dh.workspace_bytes(17, 1000, 8) == 0
+    assert dh.workspace_bytes(33, 1000, 8) == 0
+    assert dh.workspace_bytes(32, 1000, 8) > dh.workspace_bytes(16, 1000, 8)
     assert dh.workspace_bytes(1, 1000, 0) == 0
     assert dh.workspace_bytes(1, 1000, 513) == 0
     assert dh.workspace_bytes(1, 10, 11) == 0
@@ -92,7 +93,8 @@ def test_gemv_refusals_leave_outputs_untouched(no_device):
     w, s, x, out = HostBuf(V * H), HostBuf(4 * H // 32), HostBuf(16 * H * 2), HostBuf(16 * V * 4)
     ok = head(dh.FP8_BLOCK32, V, H, w, s)
     cases = [
-        (ok, x, 0, out, 1), (ok, x, 17, out, 2), (ok, None, 1, out, 1), (ok, x, 1, None, 1),
+        (ok, x, 0, out, 1), (ok, x, 33, out, 2), (ok, None, 1, out, 1), (ok, x, 1, None, 1),
+        (head(dh.FP8_BLOCK32, V, 4160, w, s), x, 17, out, 2),     # > 16 rows needs H <= 4096
         (head(7, V, H, w, s), x, 1, out, 1),                       # bad format
         (head(dh.FP8_BLOCK32, V, 48, w, s), x, 1, out, 1),         # H % 32
         (head(dh.FP8_BLOCK32, V, 8224, w, s), x, 1, out, 2),       # H > 8192
@@ -127,7 +129,7 @@ def test_topk_refusals_leave_outputs_untouched(no_device):
     assert call(kk=0) == 1
     assert call(kk=513) == 2
     assert call(kk=V + 1) == 1
-    assert call(rows=0) == 1 and call(rows=17) == 2
+    assert call(rows=0) == 1 and call(rows=33) == 2
     assert call(vocab=dh.MAX_VOCAB + 1) == 2
     assert call(wsb=64) == 3
     assert call(wsp=ctypes.c_void_p(ws.a.ctypes.data + 16)) == 3      # misaligned workspace
@@ -161,7 +163,7 @@ def test_rescore_and_draft_refusals(no_device):
     assert draft(d=stage1) == 1                         # dense head not bf16
     assert draft(kk=513) == 2
     assert draft(wsb=100) == 3
-    assert draft(rows=17) == 2
+    assert draft(rows=33) == 2
     for b in (ids, vals, ex, dr):
         assert b.untouched()
 
@@ -241,7 +243,7 @@ def test_linear_refusals(no_device):
     assert c(3, r=None) == 1                       # unknown mode
     assert c(dh.OUT_ADD_BF16, r=None) == 1         # the add mode needs a residual
     assert c(dh.OUT_BF16) == 1                     # only the add mode takes one
-    assert c(dh.OUT_F32, r=None, rows=17) == 2
+    assert c(dh.OUT_F32, r=None, rows=33) == 2
     assert c(dh.OUT_F32, r=None, o=w) == 1         # out overlaps the weight
     part = ctypes.c_void_p(out.a.ctypes.data + 2)
     assert L.dh_linear(ctypes.byref(h), x.p, R, dh.OUT_ADD_BF16, out.p, part, None) == 1

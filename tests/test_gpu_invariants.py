@@ -83,7 +83,7 @@ def test_refusals_on_device_buffers_leave_outputs_untouched():
     out = torch.full((R, V), 7.0, device="cuda")
     h = head._c()
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    assert L.dh_gemv(ctypes.byref(h), ctypes.c_void_p(x.data_ptr()), 17, ctypes.c_void_p(out.data_ptr()), st) == 2
+    assert L.dh_gemv(ctypes.byref(h), ctypes.c_void_p(x.data_ptr()), 33, ctypes.c_void_p(out.data_ptr()), st) == 2
     ids = torch.full((R, k), 5, dtype=torch.int32, device="cuda")
     vals = torch.full((R, k), 5.0, device="cuda")
     ws = dh.workspace(R, V, k)

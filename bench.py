@@ -326,6 +326,17 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
     s = stats_us(timed(lambda i: dh.rescore(dense[0], xd, o["ids"], exact=o["exact"],
                                             draft=o["draft"]), n))
     b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
+    # the top-k with the softmax statistics (probabilities of the kept entries, each row's
+    # log-sum-exp) against the plain top-k, on the FP8 head's 16-row logits, top-64
+    lg16 = torch.empty((16, V), dtype=torch.float32, device=xd.device)
+    dh.gemv(heads[0], xd, lg16)
+    ws64 = dh.workspace(16, V, K)
+    res["topk_softmax"] = {
+        "rows": 16, "k": K,
+        "dh_topk_us": back_to_back_us(lambda i: dh.topk(lg16, K, ws=ws64), n),
+        "dh_topk_softmax_us": back_to_back_us(lambda i: dh.topk_softmax(lg16, K, ws=ws64), n)}
+    log(f"top-64 of 16 rows: {res['topk_softmax']['dh_topk_us']:.1f} us, with softmax "
+        f"statistics {res['topk_softmax']['dh_topk_softmax_us']:.1f} us")
     res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
                         "dh_topk_us": t, "dh_rescore_us": s, "dh_draft_back_to_back_us": dbb,
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}

@@ -211,6 +211,27 @@ dh_status dh_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k, i
                                          workspace, (hipStream_t)stream));
 }
 
+dh_status dh_topk_softmax(const float *logits, int32_t rows, int64_t vocab, int32_t k,
+                          int32_t *ids, float *vals, int32_t *argmax, float *probs, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    DH_TRY(check_topk(logits, rows, vocab, k, ids, vals, argmax, workspace, workspace_bytes));
+    if (!probs || !lse || !aligned(probs, 4) || !aligned(lse, 4))
+        return DH_ERR_INVALID;
+    const Span sp = span(probs, (size_t)rows * k * 4), sl = span(lse, (size_t)rows * 4);
+    const Span others[] = {span(logits, (size_t)rows * (size_t)vocab * sizeof(float)),
+                           span(ids, (size_t)rows * k * 4), span(vals, (size_t)rows * k * 4),
+                           span(argmax, argmax ? (size_t)rows * 4 : 0),
+                           span(workspace, dh::topk_ws_layout(rows, vocab, k).bytes)};
+    if (overlap(sp, sl))
+        return DH_ERR_INVALID;
+    for (const Span &o : others)
+        if (overlap(sp, o) || overlap(sl, o))
+            return DH_ERR_INVALID;
+    return device_status(dh::launch_topk(logits, rows, vocab, k, nullptr, ids, vals, argmax,
+                                         workspace, (hipStream_t)stream, probs, lse));
+}
+
 // The id map of a subset head is an input: no output may overlap it.
 static dh_status check_idmap(const int32_t *idmap, int64_t vocab, std::initializer_list<Span> outs)
 {

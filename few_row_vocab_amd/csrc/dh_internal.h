@@ -38,9 +38,10 @@ inline int64_t topk_chunks(int64_t vocab, int k)
 }
 
 // Workspace layout of the top-k (offsets in bytes, each 256-byte aligned): the chunk lists
-// of 64-bit keys, [rows][chunks][k].
+// of 64-bit keys, [rows][chunks][k], then the chunks' softmax statistics [rows][chunks]
+// (float2: the largest eligible logit and the sum of exp(l - it)).
 struct TopkWs {
-    size_t val_off, id_off, cnt_off, bytes;
+    size_t val_off, id_off, cnt_off, stats_off, bytes;
 };
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
 
@@ -52,9 +53,12 @@ hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
                          const uint16_t *residual, void *out, hipStream_t stream);
 // idmap: NULL, or the vocabulary id of each logit column (ids and argmax are mapped).
+// probs, lse: NULL, or the softmax probability of each kept entry [rows][k] and each row's
+// log-sum-exp [rows] (both or neither).
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                       void *ws, hipStream_t stream);
+                       void *ws, hipStream_t stream, float *probs = nullptr,
+                       float *lse = nullptr);
 
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,

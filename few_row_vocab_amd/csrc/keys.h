@@ -1,5 +1,5 @@
-// Device helpers shared by the top-k kernels and the GEMV's candidate epilogue: the 64-bit
-// ordering keys of logits and the one-wave scan and bin search of a radix-select round.
+// Device helpers of the top-k kernels: the 64-bit ordering keys of logits and the one-wave
+// scan and bin search of a radix-select round.
 //
 // Ordering (from "nemotron: Super's MTP drafts on the draft vocabulary's FP8 rows ...",
 // commit note on the few-row top-k, and "dsv41 Zig: the TFE draft head

@@ -23,6 +23,11 @@
 //    survivor's slot is the number of survivors that beat it (the pages' rank-by-count
 //    order).  Values come back from the images (zeros, whose sign the image drops, are
 //    read from the logits, so -0 stays -0).
+// Softmax statistics (STATS, for dh_topk_softmax): pass 1 also writes each chunk's largest
+// eligible logit m_c and s_c = sum over its eligible logits of exp(l - m_c) (1 for l == m_c,
+// so +inf entries count 1 each); the merge combines them in chunk order into the row's m and
+// z = sum_c s_c exp(m_c - m), and gives each kept entry exp(l - m) / z and the row
+// log(z) + m.  Sums are in fp32 in a fixed order (deterministic).
 // These kernels are short chains of dependent steps, so the design counts barriers and LDS
 // round trips: every thread issues all of its global loads before using any, keys stay in
 // registers, a select round costs one barrier (every wave scans the round's histogram
@@ -53,8 +58,33 @@ template <int NT>
 struct SelectLds {
     uint32_t hist[kHistWords];
     uint64_t wmin[NT / 64], wmax[NT / 64];         // per-wave extremes of the non-zero keys
+    float smax[NT / 64], ssum[NT / 64];            // per-wave softmax statistics (STATS)
     uint32_t fill;                                 // survivors placed so far
 };
+
+__device__ inline bool eligible(float f) { return !__builtin_isnan(f) && f != -__builtin_inff(); }
+
+// exp(l - m) of an eligible l below or at the maximum m; 1 when l == m (also for +inf).
+__device__ inline float rel_exp(float l, float m) { return l == m ? 1.0f : expf(l - m); }
+
+__device__ inline float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float w = __shfl_xor(v, o);
+        v = w > v ? w : v;
+    }
+    return v;
+}
+
+// A butterfly over the wave's lanes: a fixed association order, so the sum is reproducible.
+__device__ inline float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
 
 template <int NT>
 __device__ inline void clear_select(SelectLds<NT> &sh)
@@ -147,10 +177,10 @@ __device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds<N
 }
 
 // Pass 1: one workgroup of NT threads per (chunk of NT * kP1PerThread logits, row); thread
-// t holds entries base + j*NT + t.
-template <int NT>
+// t holds entries base + j*NT + t.  STATS: the chunk's (m_c, s_c) to stats[row][chunk].
+template <int NT, bool STATS>
 __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V, int k,
-                                                 int nchunks, uint64_t *cand)
+                                                 int nchunks, uint64_t *cand, float2 *stats)
 {
     __shared__ __align__(16) SelectLds<NT> sh;
     constexpr int PER = kP1PerThread;
@@ -174,9 +204,44 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         const uint32_t im = id < V ? order_key(__uint_as_float(u[j])) : 0u;
         key[j] = im ? entry_key(im, (uint32_t)id) : 0ull;
     }
+    float lmax = -__builtin_inff();
+    if constexpr (STATS) {
+#pragma unroll
+        for (int j = 0; j < PER; j++) {
+            const float f = __uint_as_float(u[j]);
+            if (key[j] != 0 && f > lmax)
+                lmax = f;
+        }
+        lmax = wave_max(lmax);
+        if ((threadIdx.x & 63) == 0)
+            sh.smax[threadIdx.x >> 6] = lmax;
+    }
     __syncthreads();
+    if constexpr (STATS) {
+        // the chunk's maximum, then this wave's sum; select_top's first barrier publishes it
+        lmax = sh.smax[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; w++)
+            lmax = sh.smax[w] > lmax ? sh.smax[w] : lmax;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < PER; j++)
+            if (key[j] != 0)
+                s += rel_exp(__uint_as_float(u[j]), lmax);
+        s = wave_sum(s);
+        if ((threadIdx.x & 63) == 0)
+            sh.ssum[threadIdx.x >> 6] = s;
+    }
     uint32_t n;
     const uint64_t P = select_top<false, PER, NT>(key, (uint32_t)k, sh, n);
+    if constexpr (STATS) {
+        if (threadIdx.x == 0) {
+            float s = 0.f;
+            for (int w = 0; w < NT / 64; w++)
+                s += sh.ssum[w];
+            stats[(int64_t)r * nchunks + c] = float2{lmax, s};
+        }
+    }
     const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
 
     // survivors in any order (the merge takes the lists as sets)
@@ -215,15 +280,19 @@ constexpr int kRangedMinK = 8;
 // Pass 2: one workgroup per row; a thread holds PER of the row's nchunks * k list slots
 // (PER * kMergeThreads >= nchunks * k).  The lists hold the chunks' top values, which share
 // their leading bits, so for more than a few winners the select ranges over [min, max].
-template <int PER, bool RANGED>
+// STATS: the row's softmax statistics from the chunks' (m_c, s_c): probs[r][slot] and lse[r].
+template <int PER, bool RANGED, bool STATS>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits, int64_t V,
                                                             int k, int nchunks,
                                                             const uint64_t *cand,
                                                             const int32_t *idmap, int32_t *ids,
-                                                            float *vals, int32_t *argmax)
+                                                            float *vals, int32_t *argmax,
+                                                            const float2 *stats, float *probs,
+                                                            float *lse)
 {
     __shared__ __align__(16) SelectLds<kMergeThreads> sh;
     __shared__ __align__(16) uint64_t sel[DH_MAX_K];
+    __shared__ float row_m, row_z;
     const int r = blockIdx.x;
     const int slots = nchunks * k;
     const uint64_t *src = cand + (int64_t)r * slots;
@@ -241,6 +310,27 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
     clear_select<kMergeThreads>(sh);
     if constexpr (RANGED)
         publish_min_max<PER, kMergeThreads>(key, sh);
+    if constexpr (STATS) {
+        // wave 0: m = max_c m_c, then z = sum_c s_c exp(m_c - m), chunks c = lane, lane + 64,
+        // ... summed in that order per lane, then across lanes by a butterfly
+        if (threadIdx.x < 64) {
+            const float2 *st = stats + (int64_t)r * nchunks;
+            float m = -__builtin_inff();
+            for (int c = threadIdx.x; c < nchunks; c += 64)
+                m = st[c].x > m ? st[c].x : m;
+            m = wave_max(m);
+            float z = 0.f;
+            for (int c = threadIdx.x; c < nchunks; c += 64)
+                if (st[c].y > 0.f)
+                    z += st[c].y * rel_exp(st[c].x, m);
+            z = wave_sum(z);
+            if (threadIdx.x == 0) {
+                row_m = m;
+                row_z = z;
+                lse[r] = z > 0.f ? m + logf(z) : -__builtin_inff();
+            }
+        }
+    }
     __syncthreads();
     uint32_t n;
     const uint64_t P = select_top<RANGED, PER, kMergeThreads>(key, (uint32_t)k, sh, n);
@@ -327,13 +417,18 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         // a subset head's entry id is vocabulary id idmap[id]
         const int32_t out = idmap ? idmap[id] : (int32_t)id;
         rid[rank] = out;
-        rval[rank] = image_value(x, logits + (int64_t)r * V + id);
+        const float v = image_value(x, logits + (int64_t)r * V + id);
+        rval[rank] = v;
+        if constexpr (STATS)
+            probs[(int64_t)r * k + rank] = rel_exp(v, row_m) / row_z;
         if (rank == 0 && argmax)
             argmax[r] = out;
     }
     for (int p = kk + i; p < k; p += kMergeThreads) {
         rid[p] = 0;
         rval[p] = -__builtin_inff();
+        if constexpr (STATS)
+            probs[(int64_t)r * k + p] = 0.f;
     }
     if (kk == 0 && argmax && i == 0)
         argmax[r] = 0;
@@ -349,44 +444,69 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
     w.val_off = 0;   // the chunk lists hold keys that carry both the value and the id
     w.id_off = 0;
     w.cnt_off = 0;
-    w.bytes = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
+    w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
+    w.bytes = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
     return w;
+}
+
+template <int PER, bool STATS>
+hipError_t launch_merge2(const float *logits, int rows, int64_t vocab, int k, int nc,
+                         const uint64_t *cand, const int32_t *idmap, int32_t *ids, float *vals,
+                         int32_t *argmax, const float2 *stats, float *probs, float *lse,
+                         hipStream_t stream)
+{
+    if (k > kRangedMinK)
+        return launch(topk_merge<PER, true, STATS>, dim3(rows), dim3(kMergeThreads), 0, stream,
+                      logits, vocab, k, nc, cand, idmap, ids, vals, argmax, stats, probs, lse);
+    return launch(topk_merge<PER, false, STATS>, dim3(rows), dim3(kMergeThreads), 0, stream,
+                  logits, vocab, k, nc, cand, idmap, ids, vals, argmax, stats, probs, lse);
 }
 
 template <int PER>
 hipError_t launch_merge(const float *logits, int rows, int64_t vocab, int k, int nc,
                         const uint64_t *cand, const int32_t *idmap, int32_t *ids, float *vals,
-                        int32_t *argmax, hipStream_t stream)
+                        int32_t *argmax, const float2 *stats, float *probs, float *lse,
+                        hipStream_t stream)
 {
-    if (k > kRangedMinK)
-        return launch(topk_merge<PER, true>, dim3(rows), dim3(kMergeThreads), 0, stream,
-                      logits, vocab, k, nc, cand, idmap, ids, vals, argmax);
-    return launch(topk_merge<PER, false>, dim3(rows), dim3(kMergeThreads), 0, stream, logits,
-                  vocab, k, nc, cand, idmap, ids, vals, argmax);
+    if (probs)
+        return launch_merge2<PER, true>(logits, rows, vocab, k, nc, cand, idmap, ids, vals,
+                                        argmax, stats, probs, lse, stream);
+    return launch_merge2<PER, false>(logits, rows, vocab, k, nc, cand, idmap, ids, vals, argmax,
+                                     nullptr, nullptr, nullptr, stream);
+}
+
+template <int NT>
+hipError_t launch_pass1(const float *logits, int rows, int64_t vocab, int k, int nc,
+                        uint64_t *cand, float2 *stats, hipStream_t stream)
+{
+    const dim3 g1(nc, rows);
+    if (stats)
+        return launch(topk_pass1<NT, true>, g1, dim3(NT), 0, stream, logits, vocab, k, nc, cand,
+                      stats);
+    return launch(topk_pass1<NT, false>, g1, dim3(NT), 0, stream, logits, vocab, k, nc, cand,
+                  stats);
 }
 
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                       void *ws, hipStream_t stream)
+                       void *ws, hipStream_t stream, float *probs, float *lse)
 {
     const TopkWs w = topk_ws_layout(rows, vocab, k);
     const int chunk = topk_chunk(vocab, k);
     const int nc = (int)topk_chunks(vocab, k);
     uint64_t *cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.val_off);
+    float2 *stats = probs ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + w.stats_off)
+                          : nullptr;
     hipError_t e;
-    const dim3 g1(nc, rows);
     switch (chunk) {
     case 2048:
-        e = launch(topk_pass1<2048 / kP1PerThread>, g1, dim3(2048 / kP1PerThread), 0, stream,
-                   logits, vocab, k, nc, cand);
+        e = launch_pass1<2048 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
         break;
     case 4096:
-        e = launch(topk_pass1<4096 / kP1PerThread>, g1, dim3(4096 / kP1PerThread), 0, stream,
-                   logits, vocab, k, nc, cand);
+        e = launch_pass1<4096 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
         break;
     default:
-        e = launch(topk_pass1<8192 / kP1PerThread>, g1, dim3(8192 / kP1PerThread), 0, stream,
-                   logits, vocab, k, nc, cand);
+        e = launch_pass1<8192 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
         break;
     }
     if (e != hipSuccess)
@@ -395,18 +515,18 @@ hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
     const int64_t slots = (int64_t)nc * k;         // <= kMergeSlots by the chunk choice
     if (slots <= kMergeThreads)
         return launch_merge<1>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stream);
+                               stats, probs, lse, stream);
     if (slots <= 2 * kMergeThreads)
         return launch_merge<2>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stream);
+                               stats, probs, lse, stream);
     if (slots <= 4 * kMergeThreads)
         return launch_merge<4>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stream);
+                               stats, probs, lse, stream);
     if (slots <= 8 * kMergeThreads)
         return launch_merge<8>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stream);
+                               stats, probs, lse, stream);
     return launch_merge<16>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                            stream);
+                            stats, probs, lse, stream);
 }
 
 }  // namespace dh

@@ -65,6 +65,7 @@ def lib():
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
         L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
         L.dh_linear.argtypes = [hp, vp, i32, i32, vp, vp, vp]
+        L.dh_topk_softmax.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_lowrank.argtypes = [hp, hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -75,7 +76,7 @@ def lib():
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
-                  L.dh_draft_lowrank):
+                  L.dh_draft_lowrank, L.dh_topk_softmax):
             f.restype = i32
         _lib = L
     return _lib
@@ -211,6 +212,24 @@ def topk_mapped(logits, k, idmap, ws=None, ids=None, vals=None, argmax=None,
                 with_argmax=True, stream=None):
     """topk over a subset head's logits; ids and argmax are vocabulary ids idmap[j]."""
     return _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream)
+
+
+def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
+    """(ids, vals, argmax, probs fp32 [R][k], lse fp32 [R]): dh_topk plus each row's softmax
+    statistics (probs[:, 0] is the top-1's confidence)."""
+    _want(logits, torch.float32, "logits")
+    R, V = logits.shape
+    dev = logits.device
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
+    vals = torch.empty((R, k), dtype=torch.float32, device=dev)
+    probs = torch.empty((R, k), dtype=torch.float32, device=dev)
+    lse = torch.empty((R,), dtype=torch.float32, device=dev)
+    argmax = torch.empty((R,), dtype=torch.int32, device=dev) if with_argmax else None
+    ws = workspace(R, V, k, dev) if ws is None else ws
+    _check(lib().dh_topk_softmax(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
+                                 _ptr(probs), _ptr(lse), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+    return ids, vals, argmax, probs, lse
 
 
 def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):

@@ -128,6 +128,20 @@ dh_status dh_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k, i
                   float *vals, int32_t *argmax, void *workspace, size_t workspace_bytes,
                   void *stream);
 
+/* dh_topk_softmax -- dh_topk plus the softmax statistics of each row, in the same two
+ * passes over the logits.  [TFE] commit notes: the head's row kernels include a top-1 with a
+ * confidence; the pages do not define it, and the reading here is the softmax probability.
+ * Over a row's eligible logits (NaN and -inf excluded), with m the largest:
+ *   z = sum_v exp(l_v - m), an entry equal to m counting 1 (so every +inf counts 1 and the
+ *   finite entries 0 when m = +inf);  lse[r] = m + ln z (-inf when the row has no eligible
+ *   logit, +inf when m = +inf);  probs[r][j] = exp(vals[r][j] - m) / z (0 for pads).
+ * probs[r][0] is the top-1's confidence.  fp32 arithmetic, sums in a fixed order
+ * (reproducible).  probs: device float32 [rows][k]; lse: device float32 [rows].  Other
+ * arguments, workspace and refusals as dh_topk. */
+dh_status dh_topk_softmax(const float *logits, int32_t rows, int64_t vocab, int32_t k,
+                          int32_t *ids, float *vals, int32_t *argmax, float *probs, float *lse,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* dh_rescore -- the exact logits of candidate tokens from a dense bf16 head and the
  * candidate that wins among them.  [TFE] two_stage commit note and 'Update': the draft is
  * the argmax of the candidates' exact logits from a dense bf16 copy of the target's head,

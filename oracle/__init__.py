@@ -49,6 +49,9 @@ def lib():
         L.orc_topk_mapped.restype = c.c_int
         L.orc_topk_mapped.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
                                       c.c_void_p, c.c_void_p]
+        L.orc_topk_softmax.restype = c.c_int
+        L.orc_topk_softmax.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
+                                       c.c_void_p, c.c_void_p, c.c_void_p]
         L.orc_subset_rows.restype = None
         L.orc_subset_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                       c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
@@ -185,6 +188,20 @@ def topk(logits, k):
     if lib().orc_topk(_p(logits), R, V, k, _p(ids), _p(vals)) != 0:
         raise MemoryError("oracle top-k")
     return ids, vals
+
+
+def topk_softmax(logits, k):
+    """O8 + O16: (ids int32 [R][k], vals float32 [R][k], probs float32 [R][k], lse float32
+    [R]); probs[:, 0] is the top-1's confidence."""
+    logits = _c(logits, np.float32)
+    R, V = logits.shape
+    ids = np.empty((R, k), np.int32)
+    vals = np.empty((R, k), np.float32)
+    probs = np.empty((R, k), np.float32)
+    lse = np.empty((R,), np.float32)
+    if lib().orc_topk_softmax(_p(logits), R, V, k, _p(ids), _p(vals), _p(probs), _p(lse)) != 0:
+        raise MemoryError("oracle top-k")
+    return ids, vals, probs, lse
 
 
 def topk_mapped(logits, k, idmap):

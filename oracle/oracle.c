@@ -15,7 +15,7 @@
  * rounded once to float.  Build with -O2 -ffp-contract=off and no fast-math, so that the
  * compiler neither fuses nor reorders the sums and NaN/inf follow IEEE rules.
  *
- * Numbering O1..O14 / Q1..Q2 is the oracle's own list of definitions, restated in the
+ * Numbering O1..O16 / Q1..Q2 is the oracle's own list of definitions, restated in the
  * comments of each function.
  */
 #include <math.h>
@@ -256,6 +256,42 @@ int orc_topk_mapped(const float *logits, int R, int64_t V, int k, const int32_t 
                     int32_t *ids, float *vals)
 {
     return topk_of(logits, R, V, k, idmap, ids, vals);
+}
+
+/* O16: the softmax statistics of a row ([TFE] commit notes: a top-1 with a confidence, which
+ * the pages do not define; read as the softmax probability).  Over the row's eligible logits
+ * (O6), with m the largest: z = sum over them of exp(l - m), an entry equal to m counting 1
+ * (so with m = +inf each +inf counts 1 and finite entries 0); lse = m + ln z, -inf for a row
+ * with no eligible logit; the probability of a kept entry of value l is exp(l - m) / z (1 / z
+ * for l == m) and 0 for a pad.  In double, summed in increasing v, rounded once to float.
+ * ids/vals as O8; probs [R][k]; lse [R].  Returns 0, or -1 if memory runs out. */
+int orc_topk_softmax(const float *logits, int R, int64_t V, int k, int32_t *ids, float *vals,
+                     float *probs, float *lse)
+{
+    if (topk_of(logits, R, V, k, NULL, ids, vals) != 0)
+        return -1;
+    for (int r = 0; r < R; r++) {
+        const float *row = logits + (int64_t)r * V;
+        double m = -INFINITY;
+        int any = 0;
+        for (int64_t v = 0; v < V; v++)
+            if (eligible(row[v])) {
+                any = 1;
+                if (row[v] > m)
+                    m = row[v];
+            }
+        double z = 0.0;
+        for (int64_t v = 0; v < V; v++)
+            if (eligible(row[v]))
+                z += (double)row[v] == m ? 1.0 : exp((double)row[v] - m);
+        lse[r] = !any ? -INFINITY : (float)(m + log(z));
+        for (int j = 0; j < k; j++) {
+            const float l = vals[(int64_t)r * k + j];
+            probs[(int64_t)r * k + j] =
+                !eligible(l) ? 0.0f : (float)(((double)l == m ? 1.0 : exp((double)l - m)) / z);
+        }
+    }
+    return 0;
 }
 
 /* ---------------------------------------------------------------- draft-vocabulary subset */

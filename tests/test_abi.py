@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
                           "dh_topk_mapped", "dh_draft_mapped", "dh_linear",
-                          "dh_draft_lowrank"}
+                          "dh_draft_lowrank", "dh_topk_softmax"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -275,4 +275,22 @@ def test_lowrank_refusals(no_device):
     assert c(tt=ids) == 1                                      # t overlaps an output
     assert c(d=None) == 1                                      # one stage with `exact`
     for b in (ids, vals, ex, dr, t):
+        assert b.untouched()
+
+
+def test_topk_softmax_refusals(no_device):
+    L = dh.lib()
+    R, V, k = 2, 1000, 8
+    lg, ids, vals = HostBuf(R * V * 4), HostBuf(R * k * 4), HostBuf(R * k * 4)
+    probs, lse = HostBuf(R * k * 4), HostBuf(R * 4)
+    ws = HostBuf(dh.workspace_bytes(R, V, k))
+    c = lambda pr=probs, ls=lse: L.dh_topk_softmax(lg.p, R, V, k, ids.p, vals.p, None,
+                                                   pr.p if pr else None, ls.p if ls else None,
+                                                   ws.p, ws.a.size, None)
+    assert c(pr=None) == 1 and c(ls=None) == 1
+    assert c(ls=ids) == 1                       # lse overlaps ids
+    assert c(pr=vals) == 1                      # probs overlap vals
+    assert c(ls=probs) == 1                     # lse overlaps probs
+    assert c(ls=lg) == 1                        # lse overlaps the logits
+    for b in (ids, vals, probs, lse):
         assert b.untouched()

@@ -68,12 +68,12 @@ def measured_traffic():
 
 
 def gemv_kernel_name(fmt_code, H):
-    """The template instance the library launches for this head width (its rule for the
-    per-wave K blocks and the unguarded tile loop), as rocprofv3 names it."""
+    """The template instance the library launches for this head width and up to 16 rows (its
+    rule for the per-wave K blocks and the unguarded tile loop), as rocprofv3 names it."""
     nkb = (H + 63) // 64
     kbw = -(-nkb // 16)
     full = H % 64 == 0 and nkb % kbw == 0
-    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1>"
+    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1, 1>"
 
 
 def copy_calibration():
@@ -122,8 +122,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="main step only (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--subset-only", action="store_true",
-                    help="only the draft-vocabulary subset comparison (for profiling)")
+    ap.add_argument("--only", choices=["subset", "lowrank"],
+                    help="only the draft-vocabulary subset comparison or the low-rank "
+                         "two-stage head (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the projection "
@@ -141,8 +142,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.subset_only:
+    if args.only == "subset":
         print(json.dumps({"subset_head": subset_sweep(dh, torch, args.calls)}), flush=True)
+        return
+    if args.only == "lowrank":
+        print(json.dumps({"lowrank_two_stage": lowrank_sweep(dh, torch, args.calls)}),
+              flush=True)
         return
     name = "row_sweep"
     c = synth.CONFIGS[name]

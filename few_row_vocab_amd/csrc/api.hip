@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "dh_internal.h"
+#include "topk.h"
 
 namespace dh {
 

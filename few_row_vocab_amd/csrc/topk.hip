@@ -33,6 +33,7 @@
 // registers, a select round costs one barrier (every wave scans the round's histogram
 // itself), and survivors are placed through an LDS counter rather than a block scan.
 #include "dh_internal.h"
+#include "topk.h"
 #include "keys.h"
 #include "launch.h"
 

@@ -342,6 +342,21 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
         "dh_topk_softmax_us": back_to_back_us(lambda i: dh.topk_softmax(lg16, K, ws=ws64), n)}
     log(f"top-64 of 16 rows: {res['topk_softmax']['dh_topk_us']:.1f} us, with softmax "
         f"statistics {res['topk_softmax']['dh_topk_softmax_us']:.1f} us")
+    # the keyed pick from the top-k lists (temperature 0.8, top-p 0.95), 16 rows
+    pos16 = torch.arange(16, dtype=torch.int64, device=xd.device)
+    i64, v64, _ = dh.topk(lg16, K, ws=ws64)
+    i512, v512, _ = dh.topk(lg16, 512)
+    tok16 = torch.empty((16,), dtype=torch.int32, device=xd.device)
+    kept16 = torch.empty((16,), dtype=torch.int32, device=xd.device)
+    res["sample"] = {
+        "rows": 16, "temperature": 0.8, "top_p": 0.95,
+        "dh_sample_k64_us": back_to_back_us(
+            lambda i: dh.sample(i64, v64, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16), n),
+        "dh_sample_k512_us": back_to_back_us(
+            lambda i: dh.sample(i512, v512, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16),
+            n)}
+    log(f"keyed pick of 16 rows: {res['sample']['dh_sample_k64_us']:.1f} us from 64 "
+        f"candidates, {res['sample']['dh_sample_k512_us']:.1f} us from 512")
     res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
                         "dh_topk_us": t, "dh_rescore_us": s, "dh_draft_back_to_back_us": dbb,
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}

@@ -6,9 +6,9 @@ holds it, its build script and a thin Python binding (dh.py).
 from . import dh
 from .dh import (BF16, FP8_BLOCK32, FP8_ROW, OUT_ADD_BF16, OUT_BF16, OUT_F32, DHError, Head,
                  draft, draft_lowrank, draft_mapped, gather_rows, gemv, linear, quantize,
-                 rescore, topk, topk_mapped, topk_softmax, workspace, workspace_bytes)
+                 rescore, sample, topk, topk_mapped, topk_softmax, workspace, workspace_bytes)
 
 __all__ = ["dh", "BF16", "FP8_BLOCK32", "FP8_ROW", "OUT_ADD_BF16", "OUT_BF16", "OUT_F32",
            "DHError", "Head", "draft", "draft_lowrank", "draft_mapped", "gather_rows", "gemv",
-           "linear", "quantize", "rescore", "topk", "topk_mapped", "topk_softmax", "workspace",
-           "workspace_bytes"]
+           "linear", "quantize", "rescore", "sample", "topk", "topk_mapped", "topk_softmax",
+           "workspace", "workspace_bytes"]

@@ -440,6 +440,33 @@ dh_status dh_draft_lowrank(const dh_head *down, const dh_head *up, const dh_head
                      workspace, workspace_bytes, stream);
 }
 
+dh_status dh_sample(const int32_t *ids, const float *vals, int32_t rows, int32_t k,
+                    double temperature, double top_p, double min_p, uint64_t seed,
+                    const int64_t *positions, int32_t *token, int32_t *kept, void *stream)
+{
+    DH_TRY(check_rows(rows));
+    if (k < 1)
+        return DH_ERR_INVALID;
+    if (k > DH_MAX_K)
+        return DH_ERR_UNSUPPORTED;
+    if (!(temperature >= 0.0) || !(temperature < __builtin_inf()) || !(top_p > 0.0) ||
+        !(top_p <= 1.0) || !(min_p >= 0.0) || !(min_p <= 1.0))
+        return DH_ERR_INVALID;
+    if (!ids || !vals || !positions || !token || !aligned(ids, 4) || !aligned(vals, 4) ||
+        !aligned(positions, 8) || !aligned(token, 4) || (kept && !aligned(kept, 4)))
+        return DH_ERR_INVALID;
+    const Span st = span(token, (size_t)rows * 4), sk = span(kept, kept ? (size_t)rows * 4 : 0);
+    const Span in[] = {span(ids, (size_t)rows * k * 4), span(vals, (size_t)rows * k * 4),
+                       span(positions, (size_t)rows * 8)};
+    for (const Span &i : in)
+        if (overlap(st, i) || overlap(sk, i))
+            return DH_ERR_INVALID;
+    if (overlap(st, sk))
+        return DH_ERR_INVALID;
+    return device_status(dh::launch_sample(ids, vals, rows, k, temperature, top_p, min_p, seed,
+                                           positions, token, kept, (hipStream_t)stream));
+}
+
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream)
 {

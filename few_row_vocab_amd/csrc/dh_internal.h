@@ -28,6 +28,9 @@ hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           float *exact, int32_t *draft, hipStream_t stream);
 hipError_t launch_gather_rows(const dh_head &head, const int32_t *ids, int64_t n, void *weight,
                               float *scale, hipStream_t stream);
+hipError_t launch_sample(const int32_t *ids, const float *vals, int rows, int k, double T,
+                         double top_p, double min_p, uint64_t seed, const int64_t *pos,
+                         int32_t *token, int32_t *kept, hipStream_t stream);
 hipError_t launch_quantize(int format, const uint16_t *w, int64_t vocab, int64_t hidden,
                            uint8_t *codes, void *scale, hipStream_t stream);
 

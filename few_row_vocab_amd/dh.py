@@ -66,6 +66,8 @@ def lib():
         L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
         L.dh_linear.argtypes = [hp, vp, i32, i32, vp, vp, vp]
         L.dh_topk_softmax.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dh_sample.argtypes = [vp, vp, i32, i32, c.c_double, c.c_double, c.c_double,
+                                c.c_uint64, vp, vp, vp, vp]
         L.dh_draft_lowrank.argtypes = [hp, hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                        sz, vp]
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -76,7 +78,7 @@ def lib():
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
-                  L.dh_draft_lowrank, L.dh_topk_softmax):
+                  L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample):
             f.restype = i32
         _lib = L
     return _lib
@@ -230,6 +232,24 @@ def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
                                  _ptr(probs), _ptr(lse), _ptr(ws), ws.numel(),
                                  _stream(stream)))
     return ids, vals, argmax, probs, lse
+
+
+def sample(ids, vals, positions, temperature=1.0, top_p=1.0, min_p=0.0, seed=0,
+           with_kept=True, token=None, kept=None, stream=None):
+    """dh_sample: (token int32 [R], kept int32 [R] or None) keyed by seed, positions (int64
+    [R]) and the candidates' token ids."""
+    _want(ids, torch.int32, "ids")
+    _want(vals, torch.float32, "vals")
+    _want(positions, torch.int64, "positions")
+    R, k = ids.shape
+    if token is None:
+        token = torch.empty((R,), dtype=torch.int32, device=ids.device)
+    if kept is None and with_kept:
+        kept = torch.empty((R,), dtype=torch.int32, device=ids.device)
+    _check(lib().dh_sample(_ptr(ids), _ptr(vals), R, k, float(temperature), float(top_p),
+                           float(min_p), int(seed) & (2**64 - 1), _ptr(positions), _ptr(token),
+                           _ptr(kept), _stream(stream)))
+    return token, kept
 
 
 def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):

@@ -10,6 +10,7 @@
  *            stream's text is covered, same replies"
  *   [METAL] "dsv41 metal: the DSpark drafter on an FP8 head, a concurrent propose and
  *            resident buffers"
+ *   [DSV]   "DeepSeek-V4.1: performance hooks and host checks"
  *
  * Conventions for every entry point:
  *  - Pointers named as device pointers must point to device memory of the current HIP
@@ -197,6 +198,27 @@ dh_status dh_draft_lowrank(const dh_head *down, const dh_head *up, const dh_head
                            int32_t *ids, float *vals, int32_t *draft, float *exact,
                            float *logits, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/* dh_sample -- a keyed pick from each row's top-k candidates.  [DSV] commit notes on the
+ * serving module's sampler: a window's choices come from the candidates, their nucleus
+ * statistics and a pick keyed by seed, position and token id, so a drafted token equals the
+ * serial one.  The pages define no formula; the reading implemented:
+ *   over the eligible candidates j in list order (vals[r][j] > -inf; v_0 the first),
+ *   q_j = exp((v_j - v_0) / temperature) (1 when v_j == v_0);
+ *   nucleus: j is kept while the sum of q before it is below top_p * sum(q) (j = 0 always),
+ *   min-p: and q_j >= min_p;
+ *   the pick is the kept j maximising (v_j - v_0) / temperature - ln(-ln u_j), the lower id
+ *   on a tie, with u_j in (0, 1) the first word w of Philox4x64-10 (Salmon et al., SC 2011)
+ *   with key (seed, 0) and counter (positions[r], ids[r][j], 0, 0), as (w >> 11 + 1/2) * 2^-53
+ *   (Gumbel-max: the pick has probability q_j / sum of the kept q).
+ * temperature == 0 picks ids[r][0].  A row without an eligible candidate gives token 0.
+ * Arithmetic in double.  ids, vals: device [rows][k], a dh_topk list (descending, pads
+ * last).  positions: device int64 [rows].  token: device int32 [rows]; kept: device int32
+ * [rows] (the number of candidates the filters kept) or NULL.  temperature >= 0 and finite,
+ * 0 < top_p <= 1, 0 <= min_p <= 1, else DH_ERR_INVALID. */
+dh_status dh_sample(const int32_t *ids, const float *vals, int32_t rows, int32_t k,
+                    double temperature, double top_p, double min_p, uint64_t seed,
+                    const int64_t *positions, int32_t *token, int32_t *kept, void *stream);
 
 /* Draft-vocabulary subset heads.  [SUPER] 'What this changes': a draft head packs the FP8
  * rows of its draft vocabulary's ids into a weight of their own (keeping the head's scales)

@@ -52,6 +52,14 @@ def lib():
         L.orc_topk_softmax.restype = c.c_int
         L.orc_topk_softmax.argtypes = [c.c_void_p, c.c_int, c.c_int64, c.c_int, c.c_void_p,
                                        c.c_void_p, c.c_void_p, c.c_void_p]
+        L.orc_philox4x64.restype = None
+        L.orc_philox4x64.argtypes = [c.c_void_p, c.c_void_p, c.c_void_p]
+        L.orc_keyed_uniform.restype = c.c_double
+        L.orc_keyed_uniform.argtypes = [c.c_uint64, c.c_int64, c.c_int32]
+        L.orc_sample.restype = None
+        L.orc_sample.argtypes = [c.c_void_p, c.c_void_p, c.c_int, c.c_int, c.c_double,
+                                 c.c_double, c.c_double, c.c_uint64, c.c_void_p, c.c_void_p,
+                                 c.c_void_p, c.c_void_p]
         L.orc_subset_rows.restype = None
         L.orc_subset_rows.argtypes = [c.c_void_p, c.c_void_p, c.c_int64, c.c_int64, c.c_int,
                                       c.c_void_p, c.c_int64, c.c_void_p, c.c_void_p]
@@ -202,6 +210,34 @@ def topk_softmax(logits, k):
     if lib().orc_topk_softmax(_p(logits), R, V, k, _p(ids), _p(vals), _p(probs), _p(lse)) != 0:
         raise MemoryError("oracle top-k")
     return ids, vals, probs, lse
+
+
+def philox4x64(ctr, key):
+    """Philox4x64-10 of counter (4 x uint64) and key (2 x uint64): 4 x uint64."""
+    c = np.ascontiguousarray(ctr, np.uint64)
+    kk = np.ascontiguousarray(key, np.uint64)
+    out = np.empty(4, np.uint64)
+    lib().orc_philox4x64(_p(c), _p(kk), _p(out))
+    return out
+
+
+def keyed_uniform(seed, position, token):
+    return float(lib().orc_keyed_uniform(int(seed), int(position), int(token)))
+
+
+def sample(ids, vals, T, top_p, min_p, seed, pos):
+    """O17: the keyed pick over top-k lists (ids int32 [R][k], vals float32 [R][k]); pos int64
+    [R].  -> (token int32 [R], kept int32 [R], score float64 [R][k])."""
+    ids = _c(ids, np.int32)
+    vals = _c(vals, np.float32)
+    R, k = ids.shape
+    pos = _c(np.asarray(pos, np.int64), np.int64)
+    token = np.empty(R, np.int32)
+    kept = np.empty(R, np.int32)
+    score = np.empty((R, k), np.float64)
+    lib().orc_sample(_p(ids), _p(vals), R, k, float(T), float(top_p), float(min_p),
+                     int(seed), _p(pos), _p(token), _p(kept), _p(score))
+    return token, kept, score
 
 
 def topk_mapped(logits, k, idmap):

@@ -10,12 +10,13 @@
  *           text is covered, same replies"
  *  [METAL] "dsv41 metal: the DSpark drafter on an FP8 head, a concurrent propose and
  *           resident buffers"
+ *  [DSV]   "DeepSeek-V4.1: performance hooks and host checks"
  *
  * Floating point: every dot product is accumulated in IEEE double, in increasing h, and
  * rounded once to float.  Build with -O2 -ffp-contract=off and no fast-math, so that the
  * compiler neither fuses nor reorders the sums and NaN/inf follow IEEE rules.
  *
- * Numbering O1..O16 / Q1..Q2 is the oracle's own list of definitions, restated in the
+ * Numbering O1..O17 / Q1..Q2 is the oracle's own list of definitions, restated in the
  * comments of each function.
  */
 #include <math.h>
@@ -292,6 +293,114 @@ int orc_topk_softmax(const float *logits, int R, int64_t V, int k, int32_t *ids,
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------- keyed sampling */
+
+/* Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel
+ * random numbers: as easy as 1, 2, 3", SC 2011), from its definition: ten rounds; a round
+ * multiplies counter words 0 and 2 by the two round constants into 128-bit products and
+ * makes the new counter (hi(c2*M1) ^ c1 ^ k0, lo(c2*M1), hi(c0*M0) ^ c3 ^ k1, lo(c0*M0)); the
+ * key is bumped by the two Weyl constants between rounds. */
+static void mul128(uint64_t a, uint64_t b, uint64_t *hi, uint64_t *lo)
+{
+    const unsigned __int128 p = (unsigned __int128)a * b;
+    *hi = (uint64_t)(p >> 64);
+    *lo = (uint64_t)p;
+}
+
+void orc_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4])
+{
+    uint64_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; round++) {
+        if (round) {
+            k0 += 0x9E3779B97F4A7C15ull;
+            k1 += 0xBB67AE8584CAA73Bull;
+        }
+        uint64_t h0, l0, h1, l1;
+        mul128(0xD2E7470EE14C6C93ull, c[0], &h0, &l0);
+        mul128(0xCA5A826395121157ull, c[2], &h1, &l1);
+        const uint64_t n0 = h1 ^ c[1] ^ k0, n2 = h0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = l1;
+        c[2] = n2;
+        c[3] = l0;
+    }
+    for (int i = 0; i < 4; i++)
+        out[i] = c[i];
+}
+
+/* The uniform of (seed, position, token id): the first word of Philox4x64-10 with key
+ * (seed, 0) and counter (position, id, 0, 0), as (w >> 11 + 1/2) * 2^-53, in (0, 1). */
+double orc_keyed_uniform(uint64_t seed, int64_t position, int32_t id)
+{
+    const uint64_t ctr[4] = {(uint64_t)position, (uint64_t)(uint32_t)id, 0, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t w[4];
+    orc_philox4x64(ctr, key, w);
+    return ((double)(w[0] >> 11) + 0.5) * 0x1p-53;
+}
+
+/* O17: the keyed pick over a row's top-k candidates ([DSV] commit notes on the serving
+ * module's sampler: a window's choices come from the candidates, their nucleus statistics
+ * and a pick keyed by seed, position and token id, so a drafted token equals the serial
+ * one).  The pages define
+ * no formula; the reading: for the eligible candidates j (value v_j > -inf, in the list's
+ * order, v_0 the largest) q_j = exp((v_j - v_0) / T) (1 for v_j == v_0); the nucleus keeps
+ * j while the mass before it is below top_p * sum(q) (j = 0 always), and min-p drops q_j <
+ * min_p; among the kept, the pick maximises (v_j - v_0) / T - ln(-ln u(seed, pos, id_j))
+ * (Gumbel-max: the pick has probability q_j / sum of the kept q), the lower id on a tie.
+ * T == 0 picks ids[0].  All in double.  token[r] = 0 and kept[r] = 0 for a row with no
+ * eligible candidate; score[r][j] is each candidate's score (-inf when not kept). */
+void orc_sample(const int32_t *ids, const float *vals, int R, int k, double T, double top_p,
+                double min_p, uint64_t seed, const int64_t *pos, int32_t *token, int32_t *kept,
+                double *score)
+{
+    double *q = malloc(sizeof *q * (size_t)(k > 0 ? k : 1));
+    for (int r = 0; r < R; r++) {
+        const int32_t *ri = ids + (int64_t)r * k;
+        const float *rv = vals + (int64_t)r * k;
+        double *rs = score + (int64_t)r * k;
+        int n = 0;
+        while (n < k && rv[n] > -INFINITY)
+            n++;
+        for (int j = 0; j < k; j++)
+            rs[j] = -INFINITY;
+        if (n == 0) {
+            token[r] = 0;
+            kept[r] = 0;
+            continue;
+        }
+        if (T == 0.0) {
+            token[r] = ri[0];
+            kept[r] = 1;
+            rs[0] = 0.0;
+            continue;
+        }
+        const double v0 = rv[0];
+        double z = 0.0;
+        for (int j = 0; j < n; j++) {
+            q[j] = (double)rv[j] == v0 ? 1.0 : exp(((double)rv[j] - v0) / T);
+            z += q[j];
+        }
+        double before = 0.0;
+        int m = 0, best = -1;
+        for (int j = 0; j < n; j++) {
+            const int keep = j == 0 || (before < top_p * z && q[j] >= min_p);
+            before += q[j];
+            if (!keep)
+                continue;
+            m++;
+            const double d = (double)rv[j] == v0 ? 0.0 : ((double)rv[j] - v0) / T;
+            rs[j] = d - log(-log(orc_keyed_uniform(seed, pos[r], ri[j])));
+            if (best < 0 || rs[j] > rs[best] || (rs[j] == rs[best] && ri[j] < ri[best]))
+                best = j;
+        }
+        token[r] = ri[best];
+        kept[r] = m;
+    }
+    free(q);
 }
 
 /* ---------------------------------------------------------------- draft-vocabulary subset */

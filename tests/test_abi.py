@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
                           "dh_topk_mapped", "dh_draft_mapped", "dh_linear",
-                          "dh_draft_lowrank", "dh_topk_softmax"}
+                          "dh_draft_lowrank", "dh_topk_softmax", "dh_sample"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -294,3 +294,17 @@ def test_topk_softmax_refusals(no_device):
     assert c(ls=lg) == 1                        # lse overlaps the logits
     for b in (ids, vals, probs, lse):
         assert b.untouched()
+
+
+def test_sample_refusals(no_device):
+    L = dh.lib()
+    R, k = 2, 8
+    ids, vals, pos, tok, kept = (HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * 8),
+                                 HostBuf(R * 4), HostBuf(R * 4))
+    c = lambda T=1.0, p=1.0, m=0.0, rows=R, kk=k, t=tok: L.dh_sample(
+        ids.p, vals.p, rows, kk, T, p, m, 1, pos.p, t.p, kept.p, None)
+    assert c(T=-1.0) == 1 and c(T=float("nan")) == 1 and c(T=float("inf")) == 1
+    assert c(p=0.0) == 1 and c(p=1.01) == 1 and c(m=-0.5) == 1 and c(m=2.0) == 1
+    assert c(rows=0) == 1 and c(rows=33) == 2 and c(kk=0) == 1 and c(kk=513) == 2
+    assert c(t=ids) == 1                          # token overlaps the candidates
+    assert tok.untouched() and kept.untouched()

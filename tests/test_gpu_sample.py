@@ -1,0 +1,89 @@
+"""GPU parity of dh_sample (the keyed pick from the top-k candidates) against the oracle's
+O17, through the C ABI.
+
+The pick is an argmax decided in double on both sides (the kernel's precision); the two
+sides' exp and log may differ in the last bit, so a row is compared exactly when its best
+and second-best oracle scores differ by more than 1e-9, and otherwise the GPU's pick must be
+one of the candidates within 1e-9 of the best.  The kept counts must be equal except where
+the nucleus boundary sits within 1e-12 (relative) of a candidate's cumulative mass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from few_row_vocab_amd import dh
+from gpu_util import dev, host, need_gpu, say
+from test_gpu_core import _planted
+
+pytestmark = pytest.mark.gpu
+
+
+def check_picks(ids, vals, T, top_p, min_p, seed, pos, tok, kept):
+    ot, ok, sc = oracle.sample(ids, vals, T, top_p, min_p, seed, pos)
+    for r in range(ids.shape[0]):
+        s = sc[r]
+        fin = np.isfinite(s)
+        if T == 0 or fin.sum() <= 1:
+            assert tok[r] == ot[r], (r, tok[r], ot[r])
+        else:
+            order = np.sort(s[fin])[::-1]
+            if order[0] - order[1] > 1e-9:
+                assert tok[r] == ot[r], (r, tok[r], ot[r])
+            else:
+                near = ids[r][fin & (s >= order[0] - 1e-9)]
+                assert tok[r] in near
+        if kept[r] != ok[r]:
+            v = vals[r].astype(np.float64)
+            q = np.where(v > -np.inf, np.exp((v - v[0]) / T), 0.0)
+            cum = np.cumsum(q)
+            assert np.min(np.abs(cum - top_p * q.sum())) <= 1e-12 * q.sum(), (r, kept[r], ok[r])
+
+
+@pytest.mark.parametrize("k", [1, 8, 64, 512])
+@pytest.mark.parametrize("T,top_p,min_p", [(1.0, 1.0, 0.0), (0.6, 0.9, 0.0), (1.5, 0.95, 0.02),
+                                           (0.0, 1.0, 0.0), (0.05, 1.0, 0.0)])
+def test_sample_vs_oracle(k, T, top_p, min_p):
+    need_gpu()
+    V = 20000
+    logits = _planted(16, V, seed=k * 31 + int(T * 10))
+    ids, vals, _ = dh.topk(dev(logits), k)
+    pos = np.arange(16, dtype=np.int64) * 977 + 5
+    seed = 0x9E3779B97F4A7C15 ^ k
+    tok, kept = dh.sample(ids, vals, dev(pos), temperature=T, top_p=top_p, min_p=min_p,
+                          seed=seed)
+    torch.cuda.synchronize()
+    check_picks(host(ids), host(vals), T, top_p, min_p, seed, pos, host(tok), host(kept))
+
+
+def test_sample_many_seeds_law():
+    """Many seeds on the GPU: the picks follow the oracle's (and the reading's) law."""
+    need_gpu()
+    vals = np.array([[2.0, 1.6, 1.5, 0.9, 0.3, -0.4, -1.0, -np.inf]], np.float32)
+    ids = np.array([[40, 7, 19, 3, 88, 51, 12, 0]], np.int32)
+    R = 32
+    vd, idd = dev(np.repeat(vals, R, 0)), dev(np.repeat(ids, R, 0))
+    pos = dev(np.arange(R, dtype=np.int64))
+    picks = []
+    for s in range(100):
+        tok, _ = dh.sample(idd, vd, pos, temperature=0.8, top_p=0.9, seed=s)
+        picks.append(host(tok))
+    torch.cuda.synchronize()
+    picks = np.concatenate(picks)
+    ot = np.concatenate([oracle.sample(np.repeat(ids, R, 0), np.repeat(vals, R, 0), 0.8, 0.9,
+                                       0.0, s, np.arange(R))[0] for s in range(100)])
+    assert np.mean(picks == ot) > 0.999
+    say(f"pick frequencies: {[int(np.sum(picks == i)) for i in ids[0]]}")
+
+
+def test_sample_refusals():
+    need_gpu()
+    R, k = 2, 8
+    ids = dev(np.zeros((R, k), np.int32))
+    vals = dev(np.zeros((R, k), np.float32))
+    pos = dev(np.zeros(R, np.int64))
+    for kw in ({"temperature": -1.0}, {"temperature": float("inf")}, {"top_p": 0.0},
+               {"top_p": 1.5}, {"min_p": -0.1}, {"min_p": 1.1}):
+        with pytest.raises(dh.DHError):
+            dh.sample(ids, vals, pos, **kw)

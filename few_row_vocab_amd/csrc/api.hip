@@ -397,8 +397,8 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     }
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;
-    if (down)
-        e = dh::launch_linear(*down, x, rows, DH_OUT_BF16, nullptr, t, st);
+    if (down)   // nothing else is live in the checked workspace yet: it may hold partials
+        e = dh::launch_linear(*down, x, rows, DH_OUT_BF16, nullptr, t, st, workspace, need);
     if (e == hipSuccess)
         e = dh::launch_gemv(*head, down ? t : x, rows, L, st);
     if (e == hipSuccess)

@@ -20,8 +20,12 @@ constexpr int kWave = 64;
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream);
 // The same GEMV with an output mode (dh_out_mode): fp32, bf16, or bf16 of residual + sum.
+// scratch: optional device memory; with a few tiles and linear_split_bytes of it, the work
+// is split over more workgroups with bit-identical results.
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
-                         const uint16_t *residual, void *out, hipStream_t stream);
+                         const uint16_t *residual, void *out, hipStream_t stream,
+                         void *scratch = nullptr, size_t scratch_bytes = 0);
+size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
 
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,

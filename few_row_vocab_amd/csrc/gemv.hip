@@ -97,6 +97,22 @@ __device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16
 // two 2^(b-127) for bytes 1..254.
 __device__ inline float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23); }
 
+// The output of one (activation row c, head row v) sum s: the row scale, then the mode.
+__device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
+{
+    if (a.rscale)
+        s *= a.rscale[v];
+    const int64_t at = (int64_t)c * a.V + v;
+    if (a.mode == DH_OUT_F32) {
+        a.logits[at] = s;
+    } else {
+        // the sum, plus the residual for the add mode, rounded to bf16 once
+        if (a.mode == DH_OUT_ADD_BF16)
+            s += __uint_as_float((uint32_t)a.residual[at] << 16);
+        a.out16[at] = bf16_bits(s);
+    }
+}
+
 // FULL: every wave's 64-column blocks lie inside the row (H a multiple of 64 and the
 // blocks split evenly over the waves), so no load needs a guard.
 // TR: 16-row MFMA groups per tile (a tile is 16 * TR head rows, inside one 32-row block
@@ -308,22 +324,113 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
         for (int o = lane; o < per_tile; o += kWave) {
             const int c = o >> 4, i = o & 15;
             const int64_t v = v0 + i;
-            if (v < V) {
-                float s = stage[t * OUTS + c * 16 + i];
-                if (FMT == DH_FP8_ROW)
-                    s *= a.rscale[v];
-                const int64_t at = (int64_t)c * V + v;
-                if (a.mode == DH_OUT_F32) {
-                    a.logits[at] = s;
-                } else {
-                    // the sum, plus the residual for the add mode, rounded to bf16 once
-                    if (a.mode == DH_OUT_ADD_BF16)
-                        s += __uint_as_float((uint32_t)a.residual[at] << 16);
-                    a.out16[at] = bf16_bits(s);
-                }
+            if (v < V)
+                write_out(a, c, v, stage[t * OUTS + c * 16 + i]);
+        }
+    }
+}
+
+// Few tiles (a linear with few output rows): the streaming kernel would leave most compute
+// units idle, so the work is split by virtual wave instead.  One wave per (tile, virtual
+// wave v) computes the same MFMA chain over the same kbw blocks as virtual wave v of the
+// streaming kernel and stores its 16 x 16 (or 16 x 32) partial to part[v][c][head row];
+// gemv_reduce then adds the partials in virtual-wave order, starting from 0, exactly as the
+// streaming kernel's reduction does -- the same sums, the same bits.
+constexpr int kSplitMaxKbw = 8;
+
+template <int FMT, int NB>
+__global__ __launch_bounds__(kWave) void gemv_split(GemvArgs a, int kbw, float *part)
+{
+    constexpr int RQ = FMT == DH_BF16 ? 2 : 1;
+    constexpr int ES = FMT == DH_BF16 ? 2 : 1;
+    const int lane = threadIdx.x, rr = lane & 15, g = lane >> 4;
+    const int tile = blockIdx.x, vw = blockIdx.y;
+    const int H = a.H;
+    const int64_t V = a.V;
+    const int64_t v0 = (int64_t)tile * 16;
+    const int64_t rows = V - v0 < 16 ? V - v0 : 16;
+    const uint32_t wrow = (uint32_t)H * ES;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.w + v0 * wrow), (short)0, (int)(rows * wrow), kRsrcWord3);
+    // every load first (a block past the row or an activation row past R is zero)
+    u32x4 raw[kSplitMaxKbw][RQ];
+    Pack8 xq[NB][kSplitMaxKbw][2];
+    uint32_t sb[kSplitMaxKbw];
+#pragma unroll
+    for (int kb = 0; kb < kSplitMaxKbw; kb++) {
+        const int blk = vw * kbw + kb;
+        const int k0 = blk * 64 + 16 * g;
+        const bool in = kb < kbw && blk < a.nkb && k0 < H;
+#pragma unroll
+        for (int q = 0; q < RQ; q++)
+            raw[kb][q] = in ? __builtin_amdgcn_raw_buffer_load_b128(
+                                  wr, (uint32_t)rr * wrow + (uint32_t)k0 * ES + 16 * q, 0, 0)
+                            : u32x4{0u, 0u, 0u, 0u};
+        sb[kb] = FMT == DH_FP8_BLOCK32 && in
+                     ? a.bscale[(v0 >> 5) * (H >> 5) + 2 * blk + (g >= 2 ? 1 : 0)]
+                     : 0u;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            const int row = 16 * nb + rr;
+            xq[nb][kb][0].q = u32x4{0u, 0u, 0u, 0u};
+            xq[nb][kb][1].q = u32x4{0u, 0u, 0u, 0u};
+            if (in && row < a.R) {
+                const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)row * H + k0);
+                xq[nb][kb][0].q = px[0];
+                xq[nb][kb][1].q = px[1];
             }
         }
     }
+    f32x4 acc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+        acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < kSplitMaxKbw; kb++) {
+        if (kb >= kbw)
+            break;
+        bf16x8 a0, a1;
+        if constexpr (FMT == DH_BF16) {
+            Pack8 p0, p1;
+            p0.q = raw[kb][0];
+            p1.q = raw[kb][RQ - 1];
+            a0 = p0.v;
+            a1 = p1.v;
+        } else {
+            widen16(raw[kb][0], FMT == DH_FP8_BLOCK32 ? e8m0_scale(sb[kb]) : 1.0f, a0, a1);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xq[nb][kb][0].v, acc[nb], 0, 0, 0);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xq[nb][kb][1].v, acc[nb], 0, 0, 0);
+        }
+    }
+    // acc[nb][j]: head row 4 * (lane / 16) + j, activation row 16 nb + lane % 16
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        const int c = 16 * nb + rr;
+        if (c >= a.R)
+            continue;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t v = v0 + 4 * g + j;
+            if (v < V)
+                part[((int64_t)vw * a.R + c) * V + v] = acc[nb][j];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const float *part)
+{
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= (int64_t)a.R * a.V)
+        return;
+    const int c = (int)(n / a.V);
+    const int64_t v = n - (int64_t)c * a.V;
+    float s = 0.f;
+    for (int w = 0; w < nvw; w++)
+        s += part[((int64_t)w * a.R + c) * a.V + v];
+    write_out(a, c, v, s);
 }
 
 template <int FMT, int KBW, bool FULL, int TR, int NB, int VW>
@@ -411,8 +518,33 @@ hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *
     return launch_linear(head, x, rows, DH_OUT_F32, nullptr, logits, stream);
 }
 
+size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows)
+{
+    const int nkb = (int)((hidden + 63) / 64);
+    const int kbw = (nkb + kMaxWaves - 1) / kMaxWaves;
+    const int nvw = (nkb + kbw - 1) / kbw;
+    return (size_t)nvw * (size_t)rows * (size_t)vocab * sizeof(float);
+}
+
+template <int FMT>
+hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
+{
+    const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;
+    const int nvw = (a.nkb + kbw - 1) / kbw;
+    const int ntiles = (int)((a.V + 15) / 16);
+    hipError_t e = a.R > 16
+        ? launch(gemv_split<FMT, 2>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part)
+        : launch(gemv_split<FMT, 1>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part);
+    if (e != hipSuccess)
+        return e;
+    const int64_t n = (int64_t)a.R * a.V;
+    return launch(gemv_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, nvw,
+                  (const float *)part);
+}
+
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
-                         const uint16_t *residual, void *out, hipStream_t stream)
+                         const uint16_t *residual, void *out, hipStream_t stream,
+                         void *scratch, size_t scratch_bytes)
 {
     GemvArgs a;
     a.w = static_cast<const uint8_t *>(head.weight);
@@ -429,6 +561,18 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
     a.R = rows;
     a.ntiles = 0;   // set per tile height by run()
     a.nkb = (int)((head.hidden + 63) / 64);
+    // few tiles and room for the partials: split by virtual wave (the same bits)
+    const int64_t ntiles = (a.V + 15) / 16;
+    if (scratch && ntiles <= device_cus() / 2 && (a.nkb + kMaxWaves - 1) / kMaxWaves <= kSplitMaxKbw &&
+        scratch_bytes >= linear_split_bytes(a.V, head.hidden, rows)) {
+        float *part = static_cast<float *>(scratch);
+        switch (head.format) {
+        case DH_BF16: return run_split<DH_BF16>(a, part, stream);
+        case DH_FP8_BLOCK32: return run_split<DH_FP8_BLOCK32>(a, part, stream);
+        case DH_FP8_ROW: return run_split<DH_FP8_ROW>(a, part, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (head.format) {
     case DH_BF16: return run_fmt<DH_BF16>(a, stream);
     case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32>(a, stream);

@@ -107,6 +107,30 @@ def _want(t, dtype, name):
         raise ValueError(f"{name}: expected a contiguous tensor")
 
 
+def _shaped(t, shape, dtypes, name):
+    """A caller's tensor must match what the library will read or write through its pointer:
+    the C ABI takes bare pointers and cannot check sizes itself."""
+    if t is None:
+        return None
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: expected {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    _want(t, t.dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+BF16_BITS = (torch.bfloat16, torch.int16)
+
+
+def _ws_bytes(ws):
+    if ws.dtype != torch.uint8:
+        raise TypeError("workspace: expected a uint8 tensor")
+    _want(ws, torch.uint8, "workspace")
+    return ws.numel()
+
+
 def _bits16(t):
     """bf16 tensors are passed as their bit patterns."""
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
@@ -136,9 +160,16 @@ class Head:
         elif w.dtype != torch.uint8:
             raise TypeError("FP8 head: weight must be uint8 E4M3 codes")
         _want(w, w.dtype, "weight")
-        if self.scale is not None:
-            _want(self.scale, self.scale.dtype, "scale")
-        return _Head(self.format, w.shape[0], w.shape[1], w.data_ptr(),
+        if w.dim() != 2:
+            raise ValueError("weight: expected [V][H]")
+        V, H = w.shape
+        if self.format == FP8_ROW:
+            _shaped(self.scale, (V,), torch.float32, "scale")
+        elif self.format == FP8_BLOCK32:
+            _shaped(self.scale, ((V + 31) // 32, H // 32), torch.uint8, "scale")
+        elif self.scale is not None:
+            raise ValueError("a bf16 head has no scale")
+        return _Head(self.format, V, H, w.data_ptr(),
                      None if self.scale is None else self.scale.data_ptr())
 
 
@@ -155,11 +186,11 @@ def workspace(rows, vocab, k, device="cuda"):
 
 def gemv(head: Head, x, logits=None, stream=None):
     """logits [R][V] fp32 = x [R][H] (bf16) times the head."""
-    _want(x, x.dtype if x.dtype in (torch.bfloat16, torch.int16) else torch.bfloat16, "x")
     R = x.shape[0]
+    _shaped(x, (R, head.hidden), BF16_BITS, "x")
     if logits is None:
         logits = torch.empty((R, head.vocab), dtype=torch.float32, device=x.device)
-    _want(logits, torch.float32, "logits")
+    _shaped(logits, (R, head.vocab), torch.float32, "logits")
     h = head._c()
     _check(lib().dh_gemv(ctypes.byref(h), _ptr(x), R, _ptr(logits), _stream(stream)))
     return logits
@@ -168,14 +199,13 @@ def gemv(head: Head, x, logits=None, stream=None):
 def linear(w: Head, x, mode=OUT_F32, residual=None, out=None, stream=None):
     """out [R][N] = x [R][K] (bf16) times the linear w [N][K]: float32 (OUT_F32), bf16
     (OUT_BF16) or bf16 of residual + the sum (OUT_ADD_BF16; out may be residual)."""
-    _want(x, x.dtype if x.dtype in (torch.bfloat16, torch.int16) else torch.bfloat16, "x")
     R = x.shape[0]
+    _shaped(x, (R, w.hidden), BF16_BITS, "x")
     if out is None:
         dt = torch.float32 if mode == OUT_F32 else torch.int16
         out = torch.empty((R, w.vocab), dtype=dt, device=x.device)
-    _want(out, out.dtype, "out")
-    if residual is not None:
-        _want(residual, residual.dtype, "residual")
+    _shaped(out, (R, w.vocab), torch.float32 if mode == OUT_F32 else BF16_BITS, "out")
+    _shaped(residual, (R, w.vocab), BF16_BITS, "residual")
     h = w._c()
     _check(lib().dh_linear(ctypes.byref(h), _ptr(x), R, mode, _ptr(residual), _ptr(out),
                            _stream(stream)))
@@ -190,16 +220,19 @@ def _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream):
     vals = torch.empty((R, k), dtype=torch.float32, device=dev) if vals is None else vals
     if with_argmax and argmax is None:
         argmax = torch.empty((R,), dtype=torch.int32, device=dev)
+    _shaped(ids, (R, k), torch.int32, "ids")
+    _shaped(vals, (R, k), torch.float32, "vals")
+    _shaped(argmax, (R,), torch.int32, "argmax")
     ws = workspace(R, V, k, dev) if ws is None else ws
     if idmap is None:
         st = lib().dh_topk(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
-                           _ptr(ws), ws.numel(), _stream(stream))
+                           _ptr(ws), _ws_bytes(ws), _stream(stream))
     else:
         _want(idmap, torch.int32, "idmap")
         if idmap.numel() != V:
             raise ValueError(f"idmap: expected {V} ids, got {idmap.numel()}")
         st = lib().dh_topk_mapped(_ptr(logits), R, V, k, _ptr(idmap), _ptr(ids), _ptr(vals),
-                                  _ptr(argmax), _ptr(ws), ws.numel(), _stream(stream))
+                                  _ptr(argmax), _ptr(ws), _ws_bytes(ws), _stream(stream))
     _check(st)
     return ids, vals, argmax
 
@@ -229,7 +262,7 @@ def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
     argmax = torch.empty((R,), dtype=torch.int32, device=dev) if with_argmax else None
     ws = workspace(R, V, k, dev) if ws is None else ws
     _check(lib().dh_topk_softmax(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
-                                 _ptr(probs), _ptr(lse), _ptr(ws), ws.numel(),
+                                 _ptr(probs), _ptr(lse), _ptr(ws), _ws_bytes(ws),
                                  _stream(stream)))
     return ids, vals, argmax, probs, lse
 
@@ -239,13 +272,15 @@ def sample(ids, vals, positions, temperature=1.0, top_p=1.0, min_p=0.0, seed=0,
     """dh_sample: (token int32 [R], kept int32 [R] or None) keyed by seed, positions (int64
     [R]) and the candidates' token ids."""
     _want(ids, torch.int32, "ids")
-    _want(vals, torch.float32, "vals")
-    _want(positions, torch.int64, "positions")
     R, k = ids.shape
+    _shaped(vals, (R, k), torch.float32, "vals")
+    _shaped(positions, (R,), torch.int64, "positions")
     if token is None:
         token = torch.empty((R,), dtype=torch.int32, device=ids.device)
     if kept is None and with_kept:
         kept = torch.empty((R,), dtype=torch.int32, device=ids.device)
+    _shaped(token, (R,), torch.int32, "token")
+    _shaped(kept, (R,), torch.int32, "kept")
     _check(lib().dh_sample(_ptr(ids), _ptr(vals), R, k, float(temperature), float(top_p),
                            float(min_p), int(seed) & (2**64 - 1), _ptr(positions), _ptr(token),
                            _ptr(kept), _stream(stream)))
@@ -281,13 +316,24 @@ def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
     """(exact fp32 [R][cand_k], draft int32 [R])."""
     _want(cand_ids, torch.int32, "cand_ids")
     R, ck = cand_ids.shape
+    _shaped(x, (R, dense.hidden), BF16_BITS, "x")
     dev = x.device
     exact = torch.empty((R, ck), dtype=torch.float32, device=dev) if exact is None else exact
     draft = torch.empty((R,), dtype=torch.int32, device=dev) if draft is None else draft
+    _shaped(exact, (R, ck), torch.float32, "exact")
+    _shaped(draft, (R,), torch.int32, "draft")
     h = dense._c()
     _check(lib().dh_rescore(ctypes.byref(h), _ptr(x), R, _ptr(cand_ids), ck, _ptr(exact),
                             _ptr(draft), _stream(stream)))
     return exact, draft
+
+
+def _check_outs(o, R, k, vocab):
+    _shaped(o["ids"], (R, k), torch.int32, "ids")
+    _shaped(o["vals"], (R, k), torch.float32, "vals")
+    _shaped(o["draft"], (R,), torch.int32, "draft")
+    _shaped(o.get("exact"), (R, k), torch.float32, "exact")
+    _shaped(o.get("logits"), (R, vocab), torch.float32, "logits")
 
 
 def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=False,
@@ -304,11 +350,14 @@ def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=F
         o.setdefault("exact", torch.empty((R, k), dtype=torch.float32, device=dev))
     if keep_logits:
         o.setdefault("logits", torch.empty((R, head.vocab), dtype=torch.float32, device=dev))
+    _shaped(x, (R, head.hidden), BF16_BITS, "x")
+    _check_outs(o, R, k, head.vocab)
     ws = workspace(R, head.vocab, k, dev) if ws is None else ws
     h = head._c()
     d = dense._c() if dense is not None else None
     tail = (_ptr(x), R, k, _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
-            _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), _ws_bytes(ws),
+            _stream(stream))
     dref = ctypes.byref(d) if d is not None else None
     if idmap is None:
         _check(lib().dh_draft(ctypes.byref(h), dref, *tail))
@@ -335,14 +384,16 @@ def draft_lowrank(down: Head, up: Head, x, k, dense: Optional[Head] = None, ws=N
         o.setdefault("exact", torch.empty((R, k), dtype=torch.float32, device=dev))
     if keep_logits:
         o.setdefault("logits", torch.empty((R, up.vocab), dtype=torch.float32, device=dev))
-    _want(o["t"], o["t"].dtype if o["t"].dtype == torch.bfloat16 else torch.int16, "t")
+    _shaped(x, (R, down.hidden), BF16_BITS, "x")
+    _shaped(o["t"], (R, down.vocab), BF16_BITS, "t")
+    _check_outs(o, R, k, up.vocab)
     ws = workspace(R, up.vocab, k, dev) if ws is None else ws
     hd, hu = down._c(), up._c()
     d = dense._c() if dense is not None else None
     _check(lib().dh_draft_lowrank(
         ctypes.byref(hd), ctypes.byref(hu), ctypes.byref(d) if d is not None else None,
         _ptr(x), R, k, _ptr(o["t"]), _ptr(o["ids"]), _ptr(o["vals"]), _ptr(o["draft"]),
-        _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(o.get("exact")), _ptr(o.get("logits")), _ptr(ws), _ws_bytes(ws), _stream(stream)))
     return o
 
 

@@ -54,6 +54,22 @@ __device__ inline uint32_t wave_scan(uint32_t v)
     return v;
 }
 
+// Reserves `mine` consecutive slots per lane from an LDS counter with one atomic per wave
+// (a lane's slots follow those of the lanes below it); returns the lane's first slot.  All
+// 64 lanes must take part.
+__device__ inline uint32_t wave_reserve(uint32_t mine, uint32_t *fill)
+{
+    const uint32_t incl = wave_scan(mine);
+    const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0;
+    if (total != 0) {
+        if ((threadIdx.x & 63) == 63)
+            base = atomicAdd(fill, total);
+        base = __builtin_amdgcn_readlane(base, 63);
+    }
+    return base + incl - mine;
+}
+
 // The smallest and largest of the non-zero 64-bit keys over the 64 lanes of a wave (the same
 // DPP pattern as wave_scan; masked lanes keep the identity).  An all-zero wave gives
 // (~0, 0).

@@ -31,7 +31,8 @@
 // These kernels are short chains of dependent steps, so the design counts barriers and LDS
 // round trips: every thread issues all of its global loads before using any, keys stay in
 // registers, a select round costs one barrier (every wave scans the round's histogram
-// itself), and survivors are placed through an LDS counter rather than a block scan.
+// itself), and survivors are placed through an LDS counter (one atomic per wave) rather
+// than a block scan.
 #include "dh_internal.h"
 #include "topk.h"
 #include "keys.h"
@@ -251,8 +252,8 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
     for (int j = 0; j < PER; j++)
         mine += key[j] != 0 && key[j] >= P;
     uint64_t *out = cand + ((int64_t)r * nchunks + c) * k;
+    uint32_t at = wave_reserve(mine, &sh.fill);
     if (mine) {
-        uint32_t at = atomicAdd(&sh.fill, mine);
 #pragma unroll
         for (int j = 0; j < PER; j++)
             if (key[j] != 0 && key[j] >= P && at < (uint32_t)k)   // exactly `kept` survive
@@ -270,6 +271,56 @@ __device__ inline uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size,
     const bool lower = (i & stride) == 0, desc = (i & size) == 0;
     const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
     return lower == desc ? hi : lo;
+}
+
+// The key of lane l ^ S, through the cheapest cross-lane path for the stride: DPP quad
+// permutes for 1 and 2 (no LDS), ds_swizzle's xor mode within 32 lanes for 4..16, a
+// bpermute for 32.
+template <int S>
+__device__ inline uint32_t lane_xor(uint32_t v)
+{
+    if constexpr (S == 1)
+        return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
+    else if constexpr (S == 2)
+        return __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);   // quad_perm 2,3,0,1
+    else if constexpr (S <= 16)
+        return __builtin_amdgcn_ds_swizzle(v, 0x1F | (S << 10));           // and 31, xor S
+    else
+        return __shfl_xor(v, S);
+}
+
+template <int SIZE, int S>
+__device__ inline uint64_t bitonic(uint64_t x, int l)
+{
+    const uint64_t y = ((uint64_t)lane_xor<S>((uint32_t)(x >> 32)) << 32) |
+                       lane_xor<S>((uint32_t)x);
+    return bitonic_step(x, y, l, SIZE, S);
+}
+
+// Sorts the 64 keys of a wave in descending order (lane 0 the largest).
+__device__ inline uint64_t wave_sort_desc(uint64_t x, int l)
+{
+    x = bitonic<2, 1>(x, l);
+    x = bitonic<4, 2>(x, l);
+    x = bitonic<4, 1>(x, l);
+    x = bitonic<8, 4>(x, l);
+    x = bitonic<8, 2>(x, l);
+    x = bitonic<8, 1>(x, l);
+    x = bitonic<16, 8>(x, l);
+    x = bitonic<16, 4>(x, l);
+    x = bitonic<16, 2>(x, l);
+    x = bitonic<16, 1>(x, l);
+    x = bitonic<32, 16>(x, l);
+    x = bitonic<32, 8>(x, l);
+    x = bitonic<32, 4>(x, l);
+    x = bitonic<32, 2>(x, l);
+    x = bitonic<32, 1>(x, l);
+    x = bitonic<64, 32>(x, l);
+    x = bitonic<64, 16>(x, l);
+    x = bitonic<64, 8>(x, l);
+    x = bitonic<64, 4>(x, l);
+    x = bitonic<64, 2>(x, l);
+    return bitonic<64, 1>(x, l);
 }
 
 // Up to this many survivors the merge ranks by counting; above, by sorted runs of 64.
@@ -342,8 +393,8 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
 #pragma unroll
     for (int j = 0; j < PER; j++)
         mine += key[j] != 0 && key[j] >= P;
+    uint32_t at = wave_reserve(mine, &sh.fill);
     if (mine) {
-        uint32_t at = atomicAdd(&sh.fill, mine);
 #pragma unroll
         for (int j = 0; j < PER; j++)
             if (key[j] != 0 && key[j] >= P && at < (uint32_t)kk)   // exactly kk survive
@@ -377,10 +428,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         const int nruns = (kk + 63) >> 6;
         const int w = i >> 6, l = i & 63;
         if (w < nruns) {
-            x = i < kk ? sel[i] : 0ull;
-            for (int size = 2; size <= 64; size <<= 1)
-                for (int stride = size >> 1; stride > 0; stride >>= 1)
-                    x = bitonic_step(x, __shfl_xor(x, stride), l, size, stride);
+            x = wave_sort_desc(i < kk ? sel[i] : 0ull, l);
         }
         __syncthreads();
         if (w < nruns)
@@ -396,17 +444,24 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
                 lo[q] = 0;
                 hi[q] = q < nruns && q != w ? 64 : 0;
             }
+            // every run's probe is read each step, without a branch, so the step's eight LDS
+            // reads are in flight together (a settled or absent run reads a slot it ignores)
 #pragma unroll
-            for (int step = 0; step < 7; step++)
+            for (int step = 0; step < 7; step++) {
+                int mid[kMaxRuns];
+                uint64_t y[kMaxRuns];
 #pragma unroll
-                for (int q = 0; q < kMaxRuns; q++)
-                    if (lo[q] < hi[q]) {
-                        const int mid = (lo[q] + hi[q]) >> 1;
-                        if (sel[64 * q + mid] > x)
-                            lo[q] = mid + 1;
-                        else
-                            hi[q] = mid;
-                    }
+                for (int q = 0; q < kMaxRuns; q++) {
+                    mid[q] = (lo[q] + hi[q]) >> 1;
+                    y[q] = sel[64 * q + (mid[q] & 63)];
+                }
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++) {
+                    const bool open = lo[q] < hi[q], above = y[q] > x;
+                    lo[q] = open && above ? mid[q] + 1 : lo[q];
+                    hi[q] = open && !above ? mid[q] : hi[q];
+                }
+            }
             rank = (uint32_t)l;
 #pragma unroll
             for (int q = 0; q < kMaxRuns; q++)

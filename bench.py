@@ -72,8 +72,9 @@ def gemv_kernel_name(fmt_code, H):
     rule for the per-wave K blocks and the unguarded tile loop), as rocprofv3 names it."""
     nkb = (H + 63) // 64
     kbw = -(-nkb // 16)
-    full = H % 64 == 0 and nkb % kbw == 0
-    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1, 1>"
+    vw = 2 if fmt_code == 0 and kbw == 5 else 1        # bf16 tiles of 5 blocks: 8 waves
+    full = H % 64 == 0 and nkb % (vw * kbw) == 0
+    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1, 1, {vw}>"
 
 
 def copy_calibration():

@@ -34,7 +34,7 @@ inline int64_t topk_chunks(int64_t vocab, int k)
 // of 64-bit keys, [rows][chunks][k], then the chunks' softmax statistics [rows][chunks]
 // (float2: the largest eligible logit and the sum of exp(l - it)).
 struct TopkWs {
-    size_t val_off, id_off, cnt_off, stats_off, bytes;
+    size_t keys_off, stats_off, bytes;
 };
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
 

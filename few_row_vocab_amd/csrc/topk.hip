@@ -497,9 +497,7 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const size_t nc = (size_t)topk_chunks(vocab, k);
     TopkWs w;
-    w.val_off = 0;   // the chunk lists hold keys that carry both the value and the id
-    w.id_off = 0;
-    w.cnt_off = 0;
+    w.keys_off = 0;   // the chunk lists hold keys that carry both the value and the id
     w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
     w.bytes = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
     return w;
@@ -550,7 +548,7 @@ hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
     const TopkWs w = topk_ws_layout(rows, vocab, k);
     const int chunk = topk_chunk(vocab, k);
     const int nc = (int)topk_chunks(vocab, k);
-    uint64_t *cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.val_off);
+    uint64_t *cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.keys_off);
     float2 *stats = probs ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + w.stats_off)
                           : nullptr;
     hipError_t e;

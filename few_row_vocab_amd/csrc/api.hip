@@ -370,8 +370,14 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
         return DH_ERR_INVALID;
     DH_TRY(check_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft, workspace,
                       tw.bytes));
-    if (dense)
+    if (dense) {
         DH_TRY(check_rescore(dense, x, rows, ids, k, exact, draft));
+        // the rescore reads the stage-1 values while it writes `exact` and then `draft`
+        const Span sv = span(vals, (size_t)rows * k * 4);
+        if (overlap(sv, span(exact, (size_t)rows * k * 4)) ||
+            overlap(sv, span(draft, (size_t)rows * 4)))
+            return DH_ERR_INVALID;
+    }
     for (const Span &s : in) {
         if (overlap(span(ids, (size_t)rows * k * 4), s) ||
             overlap(span(vals, (size_t)rows * k * 4), s) || overlap(span(draft, (size_t)rows * 4), s))

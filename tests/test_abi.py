@@ -157,6 +157,7 @@ def test_rescore_and_draft_refusals(no_device):
                           ids.p, vals.p, dr.p, exact.p if exact else None, None, ws.p,
                           ws.a.size if wsb is None else wsb, None)
 
+    assert draft(exact=vals) == 1                       # exact overlaps the stage-1 values
     assert draft(exact=None) == 1                       # two-stage needs `exact`
     assert draft(d=None) == 1                           # one-stage must not pass `exact`
     assert draft(d=head(dh.BF16, V - 1, H, wd)) == 1   # dense head of another size

@@ -36,7 +36,7 @@ constexpr int kMaxWaves = 16;
 // 17..32 activation rows: two 16-row MFMA column blocks.  Their activations double the VGPRs a
 // wave holds, so such launches run half the waves (256 VGPRs each), each wave doing the work
 // of two waves of the 16-row launch with separate sums (so a row's sums are the same bits
-// as in a 16-row call), and take H <= 4096.
+// as in a 16-row call), for H <= 4096; wider heads take two 16-row launches.
 constexpr int kMaxWaves2 = kMaxWaves / 2;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 constexpr int kCachePolicy = 0;          // plain loads: the non-temporal hint measured ~15% slower
@@ -488,7 +488,20 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
         case 2: return run_kbw<FMT, 2, 2>(a, stream);
         case 3: return run_kbw<FMT, 3, 2>(a, stream);
         case 4: return run_kbw<FMT, 4, 2>(a, stream);
-        default: return hipErrorInvalidValue;        // H > 4096 with more than 16 rows
+        default: {
+            // H > 4096: 32 rows of activations do not fit the registers, so rows 0..15 and
+            // 16.. take a launch each (the weights are read twice; every row keeps its bits)
+            GemvArgs lo = a, hi = a;
+            lo.R = 16;
+            hi.R = a.R - 16;
+            hi.x = a.x + (int64_t)16 * a.H;
+            const int64_t skip = (int64_t)16 * a.V;
+            hi.logits = a.logits ? a.logits + skip : nullptr;
+            hi.out16 = a.out16 ? a.out16 + skip : nullptr;
+            hi.residual = a.residual ? a.residual + skip : nullptr;
+            const hipError_t e = run_fmt<FMT>(lo, stream);
+            return e != hipSuccess ? e : run_fmt<FMT>(hi, stream);
+        }
         }
     }
     switch (kbw) {

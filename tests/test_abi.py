@@ -94,7 +94,6 @@ def test_gemv_refusals_leave_outputs_untouched(no_device):
     ok = head(dh.FP8_BLOCK32, V, H, w, s)
     cases = [
         (ok, x, 0, out, 1), (ok, x, 33, out, 2), (ok, None, 1, out, 1), (ok, x, 1, None, 1),
-        (head(dh.FP8_BLOCK32, V, 4160, w, s), x, 17, out, 2),     # > 16 rows needs H <= 4096
         (head(7, V, H, w, s), x, 1, out, 1),                       # bad format
         (head(dh.FP8_BLOCK32, V, 48, w, s), x, 1, out, 1),         # H % 32
         (head(dh.FP8_BLOCK32, V, 8224, w, s), x, 1, out, 2),       # H > 8192

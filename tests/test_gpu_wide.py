@@ -1,11 +1,11 @@
 """GPU parity of 17..32-row calls (two 16-row MFMA column blocks per weight tile) through the
 C ABI, for the three weight formats.
 
- * logits within tolerance of the oracle, over tiles, ragged tails and H up to the 4096 limit;
+ * logits within tolerance of the oracle, over tiles, ragged tails and H up to 4096 (one pass);
  * the pages' bit-equality across row counts: each row of a 17..32-row call equals the same
    row of a 1-row and of a 16-row call bit for bit;
  * dh_linear's output modes, dh_draft (top-k of 32 rows) and the subset head at 32 rows;
- * H above 4096 with more than 16 rows is refused.
+ * above H = 4096 (two 16-row launches) the same parity and bit equality.
 """
 import numpy as np
 import pytest
@@ -102,17 +102,24 @@ def test_wide_subset_draft():
     assert np.array_equal(host(out["ids"]), oi)
 
 
-def test_wide_refusals():
+@pytest.mark.parametrize("fmt", ["bf16", "block"])
+def test_wide_rows_on_a_wide_head(fmt):
+    """Above H = 4096 a 17..32-row call takes two 16-row launches: parity, and every row the
+    same bits as in a 16-row call."""
     need_gpu()
-    V, H, R = 300, 4160, 17
+    V, H, R = 3001, 5120, 25
     w = synth.random_head(V, H, seed=95, std=0.02)
-    gh, _ = make_heads("row", w)
-    xd = dev_u16(synth.random_acts(R, H, seed=96))
-    out = torch.full((R, V), 3.0, device="cuda")
-    with pytest.raises(dh.DHError) as e:
-        dh.gemv(gh, xd, out)
-    assert e.value.status == 2
-    with pytest.raises(dh.DHError):
-        dh.linear(gh, xd, dh.OUT_F32, out=out)
+    x = synth.random_acts(R, H, seed=96)
+    gh, (ow, osc) = make_heads(fmt, w)
+    xd = dev_u16(x)
+    wide = dh.gemv(gh, xd)
+    lo = dh.gemv(gh, xd[:16].contiguous())
+    hi = dh.gemv(gh, xd[16:].contiguous())
+    res = dev_u16(synth.random_acts(R, V, seed=97, std=0.5))
+    add = dh.linear(gh, xd, dh.OUT_ADD_BF16, residual=res)
     torch.cuda.synchronize()
-    assert bool((out == 3.0).all())
+    g = host(wide)
+    check_logits(g, oracle.gemv(FMTS[fmt][1], ow, osc, x))
+    assert np.array_equal(g.view(np.uint32), np.concatenate([host(lo), host(hi)]).view(np.uint32))
+    resf = (host(res).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(host(add).view(np.uint16), torch_bf16(resf + g))

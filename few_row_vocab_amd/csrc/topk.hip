@@ -64,8 +64,6 @@ struct SelectLds {
     uint32_t fill;                                 // survivors placed so far
 };
 
-__device__ inline bool eligible(float f) { return !__builtin_isnan(f) && f != -__builtin_inff(); }
-
 // exp(l - m) of an eligible l below or at the maximum m; 1 when l == m (also for +inf).
 __device__ inline float rel_exp(float l, float m) { return l == m ? 1.0f : expf(l - m); }
 

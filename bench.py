@@ -272,6 +272,30 @@ def back_to_back_us(fn, n, warm=3):
     return round(a.elapsed_time(b) * 1e3 / n, 2)
 
 
+def graph_us(fn, n, replays=5):
+    """Mean time of one call inside a HIP graph of n captured calls (no host launch cost):
+    for kernels shorter than the binding's own per-call host time."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    g, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return round(a.elapsed_time(b) * 1e3 / (n * replays), 2)
+
+
 def timed(fn, n, warm=3):
     import torch
     for _ in range(warm):
@@ -349,15 +373,18 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
     i512, v512, _ = dh.topk(lg16, 512)
     tok16 = torch.empty((16,), dtype=torch.int32, device=xd.device)
     kept16 = torch.empty((16,), dtype=torch.int32, device=xd.device)
+    f64 = lambda i: dh.sample(i64, v64, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16)
+    f512 = lambda i: dh.sample(i512, v512, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16)
     res["sample"] = {
         "rows": 16, "temperature": 0.8, "top_p": 0.95,
-        "dh_sample_k64_us": back_to_back_us(
-            lambda i: dh.sample(i64, v64, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16), n),
-        "dh_sample_k512_us": back_to_back_us(
-            lambda i: dh.sample(i512, v512, pos16, 0.8, 0.95, seed=i, token=tok16, kept=kept16),
-            n)}
-    log(f"keyed pick of 16 rows: {res['sample']['dh_sample_k64_us']:.1f} us from 64 "
-        f"candidates, {res['sample']['dh_sample_k512_us']:.1f} us from 512")
+        "dh_sample_k64_us": back_to_back_us(f64, n),
+        "dh_sample_k512_us": back_to_back_us(f512, n),
+        "dh_sample_k64_graph_us": graph_us(f64, n),
+        "dh_sample_k512_graph_us": graph_us(f512, n)}
+    sm = res["sample"]
+    log(f"keyed pick of 16 rows: {sm['dh_sample_k64_us']:.1f} us from 64 candidates, "
+        f"{sm['dh_sample_k512_us']:.1f} us from 512 (host-launched back to back); in a graph "
+        f"{sm['dh_sample_k64_graph_us']:.1f} and {sm['dh_sample_k512_graph_us']:.1f} us")
     res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
                         "dh_topk_us": t, "dh_rescore_us": s, "dh_draft_back_to_back_us": dbb,
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}

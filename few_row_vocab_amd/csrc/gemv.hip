@@ -427,9 +427,16 @@ __global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const fl
         return;
     const int c = (int)(n / a.V);
     const int64_t v = n - (int64_t)c * a.V;
+    // nvw <= kMaxWaves: every partial's load is in flight before the first add
+    float p[kMaxWaves];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; w++)
+        p[w] = w < nvw ? part[((int64_t)w * a.R + c) * a.V + v] : 0.f;
     float s = 0.f;
-    for (int w = 0; w < nvw; w++)
-        s += part[((int64_t)w * a.R + c) * a.V + v];
+#pragma unroll
+    for (int w = 0; w < kMaxWaves; w++)
+        if (w < nvw)
+            s += p[w];
     write_out(a, c, v, s);
 }
 

@@ -1,8 +1,9 @@
 """Benchmark of the few-row draft-head vocabulary projection on one MI355X.
 
 One step = one pass of the whole projection over one batch: dh_draft on the FP8 E4M3 head
-with E8M0 32x32 block scales (H=5120, V=129280, 16 activation rows): the GEMV (fp32 logits
-kept) then the top-64 and argmax.  Inputs are resident in HBM before timing;
+with E8M0 32x32 block scales (H=5120, V=129280, one activation row; --rows 5, 10, 15 or 16
+takes the row-sweep workload's head and rows instead): the GEMV (fp32 logits kept) then the
+top-64 and argmax.  Inputs are resident in HBM before timing;
 three copies of the FP8 head are rotated so that no step finds the head in the 256 MB
 Infinity Cache.
 
@@ -30,7 +31,11 @@ PEAK_HBM_GBPS = 8000.0
 NCOPY = 3
 # HBM traffic of the GEMV launch, from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
 # calibrated on a plain copy kernel; valid only for the kernel source it was taken on.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_fp8_block32_R16_H5120_V129280_traffic.txt")
+def traffic_file(rows):
+    return os.path.join(ROOT, "profiles", f"gemv_fp8_block32_R{rows}_H5120_V129280_traffic.txt")
+
+
+
 KERNEL_SOURCES = [os.path.join(ROOT, "few_row_vocab_amd", "csrc", f)
                   for f in ("gemv.hip", "dh_internal.h", "launch.h")]
 
@@ -53,11 +58,12 @@ def gemv_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Bytes per GEMV launch from the committed counter summary, or None when there is
-    none or when the kernel's source has changed since the counters were taken."""
+def measured_traffic(rows):
+    """Bytes per GEMV launch from the committed counter summary for this row count, or None
+    when there is none or when the kernel's source has changed since the counters were
+    taken."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(rows)).read()
     except OSError:
         return None
     src = re.search(r"^source_hash:\s*(\S+)", text, re.M)
@@ -121,6 +127,9 @@ def main():
     ap.add_argument("--calls", type=int, default=50, help="timed calls per sweep entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="main step only (for profiling)")
+    ap.add_argument("--rows", type=int, default=1, choices=[1, 5, 10, 15, 16],
+                    help="activation rows of the timed step: 1 is the one-row FP8 block "
+                         "workload, the others the row-sweep workload's first rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--only", choices=["subset", "lowrank"],
@@ -150,10 +159,10 @@ def main():
         print(json.dumps({"lowrank_two_stage": lowrank_sweep(dh, torch, args.calls)}),
               flush=True)
         return
-    name = "row_sweep"
+    R = args.rows
+    name = "fp8_block_1row" if R == 1 else "row_sweep"
     c = synth.CONFIGS[name]
     V, H, K = c["V"], c["H"], 64
-    R = 16
 
     t0 = time.time()
     w = synth.head_bf16(name)
@@ -240,20 +249,29 @@ def main():
                    "head_copies_rotated": NCOPY, "step_bytes": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic(R),
                      "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H),
                      "kernel_us": round(gemv_avg_ms * 1e3, 2),
                      "algorithmic_bytes": step_bytes, "kernel_source": gemv_source_hash()},
         "quantize_fp8_block32_ms": round(quant_ms, 3),
     }
 
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
     if not args.quick:
+        # the row sweep has a workload of its own (its head and 16 activation rows)
+        del heads, logits, ids, vals, am, ws, out_bufs, wd, xd
+        torch.cuda.empty_cache()
+        sw = "row_sweep"
+        wd = torch.from_numpy(synth.head_bf16(sw).view(np.int16)).to(dev)
+        xd = torch.from_numpy(synth.activations(sw, 16).view(np.int16)).to(dev)
+        heads = [dh.Head(dh.FP8_BLOCK32, *dh.quantize(wd, dh.FP8_BLOCK32)) for _ in range(NCOPY)]
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
+        del heads, wd, xd
+        torch.cuda.empty_cache()
         out["subset_head"] = subset_sweep(dh, torch, args.calls)
         out["lowrank_two_stage"] = lowrank_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
     print(json.dumps(out), flush=True)
 
 
@@ -483,7 +501,7 @@ def lowrank_sweep(dh, torch, n):
 
 def cpu_baseline(w, x, V, H, R, K):
     """The oracle as it stands (C, double precision, OpenMP over vocabulary rows) on the
-    host's cores: the whole step (GEMV of all 16 rows over the full FP8 head, then the
+    host's cores: the whole step (GEMV of the step's rows over the full FP8 head, then the
     top-k) repeated until about 10 s have passed, plus one GEMV on a single thread over
     the first 8192 vocabulary rows.  The FP8 codes come from the oracle's own quantizer
     (not timed)."""
@@ -492,7 +510,7 @@ def cpu_baseline(w, x, V, H, R, K):
     codes, scales = oracle.quant_block32(w)
     tq = time.time() - t0
     times = []
-    while not times or (sum(times) < 10.0 and len(times) < 20):
+    while not times or (sum(times) < 10.0 and len(times) < 400):
         t0 = time.time()
         lg = oracle.gemv(oracle.FMT_FP8_BLOCK32, codes, scales, x)
         oracle.topk(lg, K)
@@ -522,9 +540,9 @@ def cpu_baseline(w, x, V, H, R, K):
             "quantize_seconds": round(tq, 3),
             "single_thread": {"value": round(b1 / d1 / 1e9, 4), "unit": "GB/s",
                               "seconds": round(d1, 3),
-                              "sample": f"GEMV only, first {S} vocabulary rows, {R} rows"},
+                              "sample": f"GEMV only, first {S} vocabulary rows, {R} activation row(s)"},
             "sample": f"the full step (GEMV over all {V} vocabulary rows of the FP8 block "
-                      f"head for {R} rows, then top-{K}), {len(times)} times, median; GB/s "
+                      f"head for {R} activation row(s), then top-{K}), {len(times)} times, median; GB/s "
                       f"over the step's algorithmic bytes"}
 
 

@@ -46,13 +46,23 @@ Span span(const void *p, size_t bytes) { return Span{(uintptr_t)p, (uintptr_t)p 
 
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
-size_t elem_bytes(int format) { return format == DH_BF16 ? 2 : 1; }
+size_t elem_bytes(int format) { return (format & ~DH_TILED) == DH_BF16 ? 2 : 1; }
+
+// The storage format without the layout modifier.
+int base_format(int format) { return format & ~DH_TILED; }
+
+bool known_format(int format)
+{
+    const int f = base_format(format);
+    return (format & ~(DH_TILED | 3)) == 0 &&
+           (f == DH_BF16 || f == DH_FP8_BLOCK32 || f == DH_FP8_ROW);
+}
 
 size_t scale_bytes(const dh_head &h)
 {
-    if (h.format == DH_FP8_BLOCK32)
+    if (base_format(h.format) == DH_FP8_BLOCK32)
         return (size_t)((h.vocab + 31) / 32) * (size_t)(h.hidden / 32);
-    if (h.format == DH_FP8_ROW)
+    if (base_format(h.format) == DH_FP8_ROW)
         return (size_t)h.vocab * sizeof(float);
     return 0;
 }
@@ -61,7 +71,7 @@ dh_status check_head(const dh_head *h)
 {
     if (!h || !h->weight)
         return DH_ERR_INVALID;
-    if (h->format != DH_BF16 && h->format != DH_FP8_BLOCK32 && h->format != DH_FP8_ROW)
+    if (!known_format(h->format))
         return DH_ERR_INVALID;
     if (h->vocab < 1 || h->hidden < 32 || h->hidden % 32 != 0)
         return DH_ERR_INVALID;
@@ -69,20 +79,31 @@ dh_status check_head(const dh_head *h)
         return DH_ERR_UNSUPPORTED;
     if (!aligned(h->weight, 16))
         return DH_ERR_INVALID;
-    if (h->format == DH_BF16) {
+    if (base_format(h->format) == DH_BF16) {
         if (h->scale)
             return DH_ERR_INVALID;
     } else {
         if (!h->scale)
             return DH_ERR_INVALID;
-        if (h->format == DH_FP8_ROW && !aligned(h->scale, 4))
+        if (base_format(h->format) == DH_FP8_ROW && !aligned(h->scale, 4))
             return DH_ERR_INVALID;
     }
     return DH_OK;
 }
 
+// A head whose weight must be row-major (a rescore's dense head, a gather's source).
+dh_status check_row_major(const dh_head *h)
+{
+    const dh_status st = check_head(h);
+    if (st != DH_OK)
+        return st;
+    return (h->format & DH_TILED) ? DH_ERR_INVALID : DH_OK;
+}
+
 Span head_weight(const dh_head &h)
 {
+    if (h.format & DH_TILED)
+        return span(h.weight, dh::tiled_bytes(h.format, h.vocab, h.hidden));
     return span(h.weight, (size_t)h.vocab * (size_t)h.hidden * elem_bytes(h.format));
 }
 
@@ -256,7 +277,7 @@ dh_status dh_topk_mapped(const float *logits, int32_t rows, int64_t vocab, int32
 dh_status dh_gather_rows(const dh_head *head, const int32_t *ids, int64_t n, void *weight,
                          void *scale, void *stream)
 {
-    DH_TRY(check_head(head));
+    DH_TRY(check_row_major(head));
     if (head->format == DH_FP8_BLOCK32)
         return DH_ERR_UNSUPPORTED;
     if (n < 1)
@@ -285,7 +306,7 @@ static dh_status check_rescore(const dh_head *dense, const uint16_t *x, int32_t 
                                const int32_t *cand_ids, int32_t cand_k, float *exact,
                                int32_t *draft)
 {
-    DH_TRY(check_head(dense));
+    DH_TRY(check_row_major(dense));
     if (dense->format != DH_BF16)
         return DH_ERR_INVALID;
     DH_TRY(check_rows(rows));
@@ -466,6 +487,25 @@ dh_status dh_sample(const int32_t *ids, const float *vals, int32_t rows, int32_t
         return DH_ERR_INVALID;
     return device_status(dh::launch_sample(ids, vals, rows, k, temperature, top_p, min_p, seed,
                                            positions, token, kept, (hipStream_t)stream));
+}
+
+dh_status dh_tile_head(const dh_head *head, void *tiled, void *stream)
+{
+    DH_TRY(check_row_major(head));
+    if (!tiled || !aligned(tiled, 16))
+        return DH_ERR_INVALID;
+    const Span st = span(tiled, dh::tiled_bytes(head->format, head->vocab, head->hidden));
+    if (overlap(st, head_weight(*head)) || overlap(st, head_scale(*head)))
+        return DH_ERR_INVALID;
+    return device_status(dh::launch_tile_head(*head, tiled, (hipStream_t)stream));
+}
+
+size_t dh_tiled_bytes(int32_t format, int64_t vocab, int64_t hidden)
+{
+    if (!known_format(format) || vocab < 1 || hidden < 32 || hidden % 32 != 0 ||
+        hidden > DH_MAX_HIDDEN || vocab > ((int64_t)1 << 25))
+        return 0;
+    return dh::tiled_bytes(format, vocab, hidden);
 }
 
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,

@@ -35,6 +35,9 @@ hipError_t launch_gather_rows(const dh_head &head, const int32_t *ids, int64_t n
 hipError_t launch_sample(const int32_t *ids, const float *vals, int rows, int k, double T,
                          double top_p, double min_p, uint64_t seed, const int64_t *pos,
                          int32_t *token, int32_t *kept, hipStream_t stream);
+// The tiled copy of a row-major head's weight (dh.h, DH_TILED), and its size in bytes.
+hipError_t launch_tile_head(const dh_head &head, void *tiled, hipStream_t stream);
+size_t tiled_bytes(int format, int64_t vocab, int64_t hidden);
 hipError_t launch_quantize(int format, const uint16_t *w, int64_t vocab, int64_t hidden,
                            uint8_t *codes, void *scale, hipStream_t stream);
 

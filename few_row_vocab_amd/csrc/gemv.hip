@@ -39,7 +39,11 @@ constexpr int kMaxWaves = 16;
 // as in a 16-row call), for H <= 4096; wider heads take two 16-row launches.
 constexpr int kMaxWaves2 = kMaxWaves / 2;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
-constexpr int kCachePolicy = 0;          // plain loads: the non-temporal hint measured ~15% slower
+// Row-major heads: plain loads.  A wave's load covers 16 rows x 64 bytes there, and with the
+// non-temporal hint such part-line reads measured ~15% slower.  Tiled heads: every load reads
+// 1 KiB of whole lines, and there the non-temporal hint streams ~11% faster than plain loads.
+constexpr int kCachePolicy = 0;
+constexpr int kCacheNT = 2;              // gfx950 cache policy bit 1: non-temporal
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
 constexpr int kMaxDevices = 64;
 
@@ -57,6 +61,7 @@ struct GemvArgs {
     int R;
     int ntiles;
     int nkb;                // number of 64-column blocks, ceil(H / 64)
+    int tile_bytes;         // tiled layout: bytes of one 16-row tile, nkb * 1024 * (bytes/weight)
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -123,7 +128,11 @@ __device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
 // waves of KBW blocks each); a wave covers VW of them with a sum apiece, and the reduction
 // adds the virtual waves' sums in order, so VW changes neither a result nor its bits -- only
 // how many waves share the work (VW = 2: 8 waves of up to 256 VGPRs).
-template <int FMT, int KBW, bool FULL, int TR, int NB, int VW>
+// TL: the head is tiled (DH_TILED): a tile's 64-column block is RQ KiB in which lane l's
+// 16 bytes sit at 16 l, so a wave's load reads 1 KiB of whole lines, with the non-temporal
+// hint; rows past V and columns past H are zeros in the tiled copy.  The lanes receive the
+// same bytes as from the row-major head, so the sums and their bits are the same.
+template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL>
 __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(GemvArgs a)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
@@ -174,18 +183,22 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // length 0 makes the loads after the last tile empty); a lane's offset within a group
     // is the same for every tile, and a block adds a constant offset.  No load sits under
     // a branch, so the wait before each block is a fixed count of younger loads.
+    static_assert(!TL || TR == 1, "a tiled tile is one 16-row group");
     const uint32_t wrow = (uint32_t)H * ES;
-    const uint32_t woff = (uint32_t)rr * wrow + (uint32_t)(wave * KW * 64 + 16 * g) * ES;
+    const uint32_t woff = TL ? (uint32_t)(16 * lane + wave * KW * RQ * 1024)
+                             : (uint32_t)rr * wrow + (uint32_t)(wave * KW * 64 + 16 * g) * ES;
     const uint32_t sbase = (uint32_t)(2 * wave * KW);
     auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], int kb) {
         const int blk = wave * KW + kb;
-        if (FULL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
+        // tiled: blocks past the tile read as zeros through the descriptor's bound
+        if (FULL || TL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
 #pragma unroll
             for (int r = 0; r < TR; r++)
 #pragma unroll
                 for (int q = 0; q < RQ; q++)
                     raw[r][kb][q] = __builtin_amdgcn_raw_buffer_load_b128(
-                        wr[r], woff, kb * 64 * ES + 16 * q, kCachePolicy);
+                        wr[r], woff, TL ? (kb * RQ + q) * 1024 : kb * 64 * ES + 16 * q,
+                        TL ? kCacheNT : kCachePolicy);
         } else {
 #pragma unroll
             for (int r = 0; r < TR; r++)
@@ -207,11 +220,18 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
                      __amdgpu_buffer_rsrc_t &sr) {
 #pragma unroll
         for (int r = 0; r < TR; r++) {
-            const int64_t v0 = (int64_t)tile * TILE + 16 * r;
-            int64_t rows = V - v0 < 16 ? V - v0 : 16;
-            rows = rows < 0 || !live ? 0 : rows;
-            wr[r] = __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + (rows ? v0 : 0) * wrow),
-                                                      (short)0, (int)(rows * wrow), kRsrcWord3);
+            if constexpr (TL) {
+                wr[r] = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(a.w + (int64_t)tile * a.tile_bytes), (short)0,
+                    live ? a.tile_bytes : 0, kRsrcWord3);
+            } else {
+                const int64_t v0 = (int64_t)tile * TILE + 16 * r;
+                int64_t rows = V - v0 < 16 ? V - v0 : 16;
+                rows = rows < 0 || !live ? 0 : rows;
+                wr[r] = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(a.w + (rows ? v0 : 0) * wrow), (short)0, (int)(rows * wrow),
+                    kRsrcWord3);
+            }
         }
         const uint8_t *p = FMT == DH_FP8_BLOCK32
                                ? a.bscale + (((int64_t)tile * TILE) >> 5) * (H >> 5)
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
 // streaming kernel's reduction does -- the same sums, the same bits.
 constexpr int kSplitMaxKbw = 8;
 
-template <int FMT, int NB>
+template <int FMT, int NB, bool TL>
 __global__ __launch_bounds__(kWave) void gemv_split(GemvArgs a, int kbw, float *part)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;
@@ -350,8 +370,11 @@ __global__ __launch_bounds__(kWave) void gemv_split(GemvArgs a, int kbw, float *
     const int64_t v0 = (int64_t)tile * 16;
     const int64_t rows = V - v0 < 16 ? V - v0 : 16;
     const uint32_t wrow = (uint32_t)H * ES;
-    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.w + v0 * wrow), (short)0, (int)(rows * wrow), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wr =
+        TL ? __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + (int64_t)tile * a.tile_bytes),
+                                               (short)0, a.tile_bytes, kRsrcWord3)
+           : __builtin_amdgcn_make_buffer_rsrc((void *)(a.w + v0 * wrow), (short)0,
+                                               (int)(rows * wrow), kRsrcWord3);
     // every load first (a block past the row or an activation row past R is zero)
     u32x4 raw[kSplitMaxKbw][RQ];
     Pack8 xq[NB][kSplitMaxKbw][2];
@@ -364,7 +387,10 @@ __global__ __launch_bounds__(kWave) void gemv_split(GemvArgs a, int kbw, float *
 #pragma unroll
         for (int q = 0; q < RQ; q++)
             raw[kb][q] = in ? __builtin_amdgcn_raw_buffer_load_b128(
-                                  wr, (uint32_t)rr * wrow + (uint32_t)k0 * ES + 16 * q, 0, 0)
+                                  wr,
+                                  TL ? (uint32_t)((blk * RQ + q) * 1024 + 16 * lane)
+                                     : (uint32_t)rr * wrow + (uint32_t)k0 * ES + 16 * q,
+                                  0, TL ? kCacheNT : kCachePolicy)
                             : u32x4{0u, 0u, 0u, 0u};
         sb[kb] = FMT == DH_FP8_BLOCK32 && in
                      ? a.bscale[(v0 >> 5) * (H >> 5) + 2 * blk + (g >= 2 ? 1 : 0)]
@@ -440,14 +466,14 @@ __global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const fl
     write_out(a, c, v, s);
 }
 
-template <int FMT, int KBW, bool FULL, int TR, int NB, int VW>
+template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL>
 hipError_t run(GemvArgs a, hipStream_t stream)
 {
     static int occ_cache[kMaxWaves + 1];
     static int lds_set[kMaxDevices];               // per device: the LDS limit has been raised
     const int nw = (a.nkb + VW * KBW - 1) / (VW * KBW);
     const int block = nw * kWave;
-    auto kern = gemv_kernel<FMT, KBW, FULL, TR, NB, VW>;
+    auto kern = gemv_kernel<FMT, KBW, FULL, TR, NB, VW, TL>;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -476,25 +502,25 @@ hipError_t run(GemvArgs a, hipStream_t stream)
                   (size_t)per * TR * 256 * NB * sizeof(float), stream, a);
 }
 
-template <int FMT, int KBW, int NB, int VW = NB>
+template <int FMT, int KBW, int NB, int VW, bool TL>
 hipError_t run_kbw(const GemvArgs &a, hipStream_t stream)
 {
     constexpr int TR = 1;   // two groups measured slower: the loop is not latency-bound
     if (a.H % 64 == 0 && a.nkb % (VW * KBW) == 0)
-        return run<FMT, KBW, true, TR, NB, VW>(a, stream);
-    return run<FMT, KBW, false, TR, NB, VW>(a, stream);
+        return run<FMT, KBW, true, TR, NB, VW, TL>(a, stream);
+    return run<FMT, KBW, false, TR, NB, VW, TL>(a, stream);
 }
 
-template <int FMT>
+template <int FMT, bool TL>
 hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
 {
     const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;   // the 16-row split, for any R
     if (a.R > 16) {
         switch (kbw) {
-        case 1: return run_kbw<FMT, 1, 2>(a, stream);
-        case 2: return run_kbw<FMT, 2, 2>(a, stream);
-        case 3: return run_kbw<FMT, 3, 2>(a, stream);
-        case 4: return run_kbw<FMT, 4, 2>(a, stream);
+        case 1: return run_kbw<FMT, 1, 2, 2, TL>(a, stream);
+        case 2: return run_kbw<FMT, 2, 2, 2, TL>(a, stream);
+        case 3: return run_kbw<FMT, 3, 2, 2, TL>(a, stream);
+        case 4: return run_kbw<FMT, 4, 2, 2, TL>(a, stream);
         default: {
             // H > 4096: 32 rows of activations do not fit the registers, so rows 0..15 and
             // 16.. take a launch each (the weights are read twice; every row keeps its bits)
@@ -506,26 +532,26 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
             hi.logits = a.logits ? a.logits + skip : nullptr;
             hi.out16 = a.out16 ? a.out16 + skip : nullptr;
             hi.residual = a.residual ? a.residual + skip : nullptr;
-            const hipError_t e = run_fmt<FMT>(lo, stream);
-            return e != hipSuccess ? e : run_fmt<FMT>(hi, stream);
+            const hipError_t e = run_fmt<FMT, TL>(lo, stream);
+            return e != hipSuccess ? e : run_fmt<FMT, TL>(hi, stream);
         }
         }
     }
     switch (kbw) {
-    case 1: return run_kbw<FMT, 1, 1>(a, stream);
-    case 2: return run_kbw<FMT, 2, 1>(a, stream);
-    case 3: return run_kbw<FMT, 3, 1>(a, stream);
-    case 4: return run_kbw<FMT, 4, 1>(a, stream);
+    case 1: return run_kbw<FMT, 1, 1, 1, TL>(a, stream);
+    case 2: return run_kbw<FMT, 2, 1, 1, TL>(a, stream);
+    case 3: return run_kbw<FMT, 3, 1, 1, TL>(a, stream);
+    case 4: return run_kbw<FMT, 4, 1, 1, TL>(a, stream);
     // a bf16 tile of 5 blocks a wave does not fit 16 waves' 128 VGPRs next to the
     // activations (8 spilled); 8 waves of two virtual waves each (the same bits) fit and
     // measured 3.6% faster at H = 5120.  Wider bf16 tiles spill either way, FP8 tiles fit.
     case 5:
         if (FMT == DH_BF16)
-            return run_kbw<FMT, 5, 1, 2>(a, stream);
-        return run_kbw<FMT, 5, 1>(a, stream);
-    case 6: return run_kbw<FMT, 6, 1>(a, stream);
-    case 7: return run_kbw<FMT, 7, 1>(a, stream);
-    case 8: return run_kbw<FMT, 8, 1>(a, stream);
+            return run_kbw<FMT, 5, 1, 2, TL>(a, stream);
+        return run_kbw<FMT, 5, 1, 1, TL>(a, stream);
+    case 6: return run_kbw<FMT, 6, 1, 1, TL>(a, stream);
+    case 7: return run_kbw<FMT, 7, 1, 1, TL>(a, stream);
+    case 8: return run_kbw<FMT, 8, 1, 1, TL>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -546,15 +572,16 @@ size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows)
     return (size_t)nvw * (size_t)rows * (size_t)vocab * sizeof(float);
 }
 
-template <int FMT>
+template <int FMT, bool TL>
 hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
 {
     const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;
     const int nvw = (a.nkb + kbw - 1) / kbw;
     const int ntiles = (int)((a.V + 15) / 16);
-    hipError_t e = a.R > 16
-        ? launch(gemv_split<FMT, 2>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part)
-        : launch(gemv_split<FMT, 1>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part);
+    hipError_t e =
+        a.R > 16
+            ? launch(gemv_split<FMT, 2, TL>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part)
+            : launch(gemv_split<FMT, 1, TL>, dim3(ntiles, nvw), dim3(kWave), 0, stream, a, kbw, part);
     if (e != hipSuccess)
         return e;
     const int64_t n = (int64_t)a.R * a.V;
@@ -566,11 +593,11 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
                          const uint16_t *residual, void *out, hipStream_t stream,
                          void *scratch, size_t scratch_bytes)
 {
+    const int fmt = head.format & ~DH_TILED;
     GemvArgs a;
     a.w = static_cast<const uint8_t *>(head.weight);
-    a.bscale = head.format == DH_FP8_BLOCK32 ? static_cast<const uint8_t *>(head.scale)
-                                             : nullptr;
-    a.rscale = head.format == DH_FP8_ROW ? static_cast<const float *>(head.scale) : nullptr;
+    a.bscale = fmt == DH_FP8_BLOCK32 ? static_cast<const uint8_t *>(head.scale) : nullptr;
+    a.rscale = fmt == DH_FP8_ROW ? static_cast<const float *>(head.scale) : nullptr;
     a.x = x;
     a.logits = mode == DH_OUT_F32 ? static_cast<float *>(out) : nullptr;
     a.out16 = mode == DH_OUT_F32 ? nullptr : static_cast<uint16_t *>(out);
@@ -581,22 +608,29 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
     a.R = rows;
     a.ntiles = 0;   // set per tile height by run()
     a.nkb = (int)((head.hidden + 63) / 64);
+    a.tile_bytes = a.nkb * 1024 * (fmt == DH_BF16 ? 2 : 1);
     // few tiles and room for the partials: split by virtual wave (the same bits)
     const int64_t ntiles = (a.V + 15) / 16;
     if (scratch && ntiles <= device_cus() / 2 && (a.nkb + kMaxWaves - 1) / kMaxWaves <= kSplitMaxKbw &&
         scratch_bytes >= linear_split_bytes(a.V, head.hidden, rows)) {
         float *part = static_cast<float *>(scratch);
         switch (head.format) {
-        case DH_BF16: return run_split<DH_BF16>(a, part, stream);
-        case DH_FP8_BLOCK32: return run_split<DH_FP8_BLOCK32>(a, part, stream);
-        case DH_FP8_ROW: return run_split<DH_FP8_ROW>(a, part, stream);
+        case DH_BF16: return run_split<DH_BF16, false>(a, part, stream);
+        case DH_FP8_BLOCK32: return run_split<DH_FP8_BLOCK32, false>(a, part, stream);
+        case DH_FP8_ROW: return run_split<DH_FP8_ROW, false>(a, part, stream);
+        case DH_BF16 | DH_TILED: return run_split<DH_BF16, true>(a, part, stream);
+        case DH_FP8_BLOCK32 | DH_TILED: return run_split<DH_FP8_BLOCK32, true>(a, part, stream);
+        case DH_FP8_ROW | DH_TILED: return run_split<DH_FP8_ROW, true>(a, part, stream);
         default: return hipErrorInvalidValue;
         }
     }
     switch (head.format) {
-    case DH_BF16: return run_fmt<DH_BF16>(a, stream);
-    case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32>(a, stream);
-    case DH_FP8_ROW: return run_fmt<DH_FP8_ROW>(a, stream);
+    case DH_BF16: return run_fmt<DH_BF16, false>(a, stream);
+    case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32, false>(a, stream);
+    case DH_FP8_ROW: return run_fmt<DH_FP8_ROW, false>(a, stream);
+    case DH_BF16 | DH_TILED: return run_fmt<DH_BF16, true>(a, stream);
+    case DH_FP8_BLOCK32 | DH_TILED: return run_fmt<DH_FP8_BLOCK32, true>(a, stream);
+    case DH_FP8_ROW | DH_TILED: return run_fmt<DH_FP8_ROW, true>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

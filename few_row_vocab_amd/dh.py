@@ -18,6 +18,7 @@ BF16 = 0
 FP8_BLOCK32 = 1
 FP8_ROW = 2
 FORMATS = {"bf16": BF16, "fp8_block32": FP8_BLOCK32, "fp8_row": FP8_ROW}
+TILED = 16   # layout modifier: the weight tiled for the GEMV (see tile())
 
 OUT_F32 = 0
 OUT_BF16 = 1
@@ -72,13 +73,16 @@ def lib():
                                        sz, vp]
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_mapped.argtypes = [hp, vp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dh_tile_head.argtypes = [hp, vp, vp]
+        L.dh_tiled_bytes.argtypes = [i32, i64, i64]
+        L.dh_tiled_bytes.restype = sz
         L.dh_workspace_bytes.argtypes = [i32, i64, i32]
         L.dh_workspace_bytes.restype = sz
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
-                  L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample):
+                  L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample, L.dh_tile_head):
             f.restype = i32
         _lib = L
     return _lib
@@ -139,38 +143,80 @@ def _bits16(t):
 @dataclass
 class Head:
     """A vocabulary head: weight [V][H] (bf16, or uint8 E4M3 codes) and its scale (None,
-    uint8 E8M0 [ceil(V/32)][H/32], or float32 [V])."""
+    uint8 E8M0 [ceil(V/32)][H/32], or float32 [V]).  A tiled head (format | TILED, made by
+    tile()) holds its weight as a flat uint8 buffer of tiled_bytes() and its (V, H) in
+    `shape`."""
     format: int
     weight: torch.Tensor
     scale: Optional[torch.Tensor] = None
+    shape: Optional[tuple] = None
+
+    @property
+    def tiled(self):
+        return bool(self.format & TILED)
+
+    @property
+    def base_format(self):
+        return self.format & ~TILED
 
     @property
     def vocab(self):
-        return self.weight.shape[0]
+        return self.shape[0] if self.tiled else self.weight.shape[0]
 
     @property
     def hidden(self):
-        return self.weight.shape[1]
+        return self.shape[1] if self.tiled else self.weight.shape[1]
 
     def _c(self):
         w = self.weight
-        if self.format == BF16:
-            if w.dtype not in (torch.bfloat16, torch.int16):
-                raise TypeError("bf16 head: weight must be bfloat16 (or its int16 bits)")
-        elif w.dtype != torch.uint8:
-            raise TypeError("FP8 head: weight must be uint8 E4M3 codes")
-        _want(w, w.dtype, "weight")
-        if w.dim() != 2:
-            raise ValueError("weight: expected [V][H]")
-        V, H = w.shape
-        if self.format == FP8_ROW:
+        fmt = self.base_format
+        if self.tiled:
+            if self.shape is None or len(self.shape) != 2:
+                raise ValueError("a tiled head needs shape (V, H)")
+            V, H = (int(d) for d in self.shape)
+            if w.dtype != torch.uint8 or w.dim() != 1:
+                raise TypeError("tiled head: weight must be a flat uint8 buffer")
+            _want(w, torch.uint8, "weight")
+            if w.numel() != tiled_bytes(self.format, V, H):
+                raise ValueError(f"tiled head: weight must hold {tiled_bytes(self.format, V, H)} "
+                                 f"bytes, has {w.numel()}")
+        else:
+            if fmt == BF16:
+                if w.dtype not in (torch.bfloat16, torch.int16):
+                    raise TypeError("bf16 head: weight must be bfloat16 (or its int16 bits)")
+            elif w.dtype != torch.uint8:
+                raise TypeError("FP8 head: weight must be uint8 E4M3 codes")
+            _want(w, w.dtype, "weight")
+            if w.dim() != 2:
+                raise ValueError("weight: expected [V][H]")
+            V, H = w.shape
+        if fmt == FP8_ROW:
             _shaped(self.scale, (V,), torch.float32, "scale")
-        elif self.format == FP8_BLOCK32:
+        elif fmt == FP8_BLOCK32:
             _shaped(self.scale, ((V + 31) // 32, H // 32), torch.uint8, "scale")
         elif self.scale is not None:
             raise ValueError("a bf16 head has no scale")
         return _Head(self.format, V, H, w.data_ptr(),
                      None if self.scale is None else self.scale.data_ptr())
+
+
+def tiled_bytes(format, vocab, hidden):
+    """Bytes of a tiled weight (dh_tiled_bytes); 0 for sizes the library refuses."""
+    return int(lib().dh_tiled_bytes(format, vocab, hidden))
+
+
+def tile(head: Head, stream=None):
+    """The tiled copy of a row-major head (dh_tile_head): same format | TILED, same scale;
+    the GEMV forms give bitwise the same results from it and stream it faster."""
+    if head.tiled:
+        raise ValueError("the head is already tiled")
+    n = tiled_bytes(head.format, head.vocab, head.hidden)
+    if n == 0:
+        raise DHError(2, "sizes outside the library's limits")
+    out = torch.empty((n,), dtype=torch.uint8, device=head.weight.device)
+    h = head._c()
+    _check(lib().dh_tile_head(ctypes.byref(h), _ptr(out), _stream(stream)))
+    return Head(head.format | TILED, out, head.scale, (head.vocab, head.hidden))
 
 
 def workspace_bytes(rows, vocab, k):

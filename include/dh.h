@@ -61,6 +61,21 @@ typedef enum {
  * maxima lie in [2^-100, 2^100] always is). */
 typedef enum { DH_BF16 = 0, DH_FP8_BLOCK32 = 1, DH_FP8_ROW = 2 } dh_format;
 
+/* Layout modifier: `format | DH_TILED` names the same head with its weight stored tiled for
+ * the GEMV (made once, at load, by dh_tile_head; the scale keeps its layout above).  A tile
+ * is 16 rows, a block 64 columns, and E the bytes of an element (bf16 2, E4M3 1).  Block b of
+ * tile t is E KiB at byte (t * ceil(H/64) + b) * 1024 * E.  In it, the 16 bytes at
+ * (q * 64 + l) * 16 (q < E, lane l < 64) are row 16 t + l % 16's elements
+ *   E4M3: 64 b + 16 (l / 16) .. + 15;
+ *   bf16: 64 b + 16 (l / 16) + 8 q .. + 7.
+ * Rows past V and elements past H are zero.  Size: dh_tiled_bytes.  A wave's 1 KiB read is
+ * then exactly the operand of one 16-row x 64-column multiply, in whole cache lines, which
+ * the hardware streams faster than the row-major layout's 64-byte pieces of 16 rows.  The
+ * GEMV forms (dh_gemv, dh_linear, the stage-1 head of the dh_draft family) take tiled heads
+ * and give bitwise the same results as from the row-major head; dh_rescore's dense head and
+ * dh_gather_rows's source must be row-major (a tiled one is refused with DH_ERR_INVALID). */
+#define DH_TILED 16
+
 /* A head: a host struct naming device buffers.  `weight` must be 16-byte aligned; a float32
  * row scale must be 4-byte aligned. */
 typedef struct dh_head {
@@ -253,6 +268,18 @@ dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_he
                           const uint16_t *x, int32_t rows, int32_t k, int32_t *ids,
                           float *vals, int32_t *draft, float *exact, float *logits,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* dh_tile_head -- the tiled copy of a row-major head's weight (layout: DH_TILED above),
+ * made once at load.  head: DH_BF16, DH_FP8_BLOCK32 or DH_FP8_ROW, row-major.  tiled: device
+ * buffer of dh_tiled_bytes(head->format, V, H) bytes, 16-byte aligned, not overlapping the
+ * head.  The tiled head is then {head->format | DH_TILED, V, H, tiled, head->scale}.  A copy
+ * bound by HBM bandwidth. */
+dh_status dh_tile_head(const dh_head *head, void *tiled, void *stream);
+
+/* Bytes of a tiled weight: ceil(V/16) * ceil(H/64) * 1024 * (2 for bf16, else 1).  Pure
+ * host function; the format may carry DH_TILED; returns 0 for a format or size the library
+ * refuses. */
+size_t dh_tiled_bytes(int32_t format, int64_t vocab, int64_t hidden);
 
 /* Bytes of workspace dh_topk and dh_draft need for these sizes (dh_draft with logits ==
  * NULL included).  Pure host function; returns 0 for sizes the library refuses. */

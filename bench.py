@@ -5,7 +5,9 @@ with E8M0 32x32 block scales (H=5120, V=129280, one activation row; --rows 5, 10
 takes the row-sweep workload's head and rows instead): the GEMV (fp32 logits kept) then the
 top-64 and argmax.  Inputs are resident in HBM before timing;
 three copies of the FP8 head are rotated so that no step finds the head in the 256 MB
-Infinity Cache.
+Infinity Cache.  The head is stored tiled for the GEMV (dh_tile_head, once at load: the same
+bytes re-arranged so that each wave load reads 1 KiB of whole lines); the row-major head's
+GEMV time is reported beside it.
 
 Printed: one JSON line.  value = algorithmic HBM bytes of a step (head codes + scales +
 activations + fp32 logits written) / time per step, in GB/s.  Extra fields give the row
@@ -73,14 +75,15 @@ def measured_traffic(rows):
     return int(val.group(1))
 
 
-def gemv_kernel_name(fmt_code, H):
+def gemv_kernel_name(fmt_code, H, tiled=True):
     """The template instance the library launches for this head width and up to 16 rows (its
     rule for the per-wave K blocks and the unguarded tile loop), as rocprofv3 names it."""
     nkb = (H + 63) // 64
     kbw = -(-nkb // 16)
     vw = 2 if fmt_code == 0 and kbw == 5 else 1        # bf16 tiles of 5 blocks: 8 waves
     full = H % 64 == 0 and nkb % (vw * kbw) == 0
-    return f"gemv_kernel<{fmt_code}, {kbw}, {'true' if full else 'false'}, 1, 1, {vw}>"
+    tf = lambda b: "true" if b else "false"
+    return f"gemv_kernel<{fmt_code}, {kbw}, {tf(full)}, 1, 1, {vw}, {tf(tiled)}>"
 
 
 def copy_calibration():
@@ -170,11 +173,18 @@ def main():
     log(f"generated {V}x{H} head in {time.time() - t0:.1f}s")
     wd = torch.from_numpy(w.view(np.int16)).to(dev)
     xd = torch.from_numpy(x.view(np.int16)).to(dev)
-    heads = []
+    rm_heads = []
     for i in range(NCOPY):
         codes, scale = dh.quantize(wd, dh.FP8_BLOCK32)
-        heads.append(dh.Head(dh.FP8_BLOCK32, codes, scale))
+        rm_heads.append(dh.Head(dh.FP8_BLOCK32, codes, scale))
+    heads = [dh.tile(h) for h in rm_heads]             # load time: the tiled copies
     torch.cuda.synchronize()
+    te = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    te[0].record()
+    dh.tile(rm_heads[0])
+    te[1].record()
+    torch.cuda.synchronize()
+    tile_ms = te[0].elapsed_time(te[1])
     # quantization time (load-time prep; the pages quote 0.2 s on 16 CPU workers)
     qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     qe[0].record()
@@ -232,8 +242,10 @@ def main():
     torch.cuda.synchronize()
     gemv_avg_ms = g0.elapsed_time(g1) / args.steps
     achieved = step_bytes / (gemv_avg_ms * 1e-3) / 1e9
+    # the same GEMV from the row-major head (not the benchmarked layout), for comparison
+    rm_us = back_to_back_us(lambda i: dh.gemv(rm_heads[i % NCOPY], xd, logits), args.steps)
     log(f"step {ms_per_step * 1e3:.1f} us, gemv {gemv_avg_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s)")
+        f"({achieved:.0f} GB/s); row-major head gemv {rm_us:.1f} us")
 
     out = {
         "metric": "draft-head µs/call and achieved HBM GB/s (FP8 head, 1/5/10/16 rows)",
@@ -246,6 +258,7 @@ def main():
                                f"{R} activation rows, dh_draft: GEMV (fp32 logits kept) + "
                                f"top-{K} and argmax",
                    "H": H, "V": V, "rows": R, "k": K, "format": "fp8_block32",
+                   "layout": "tiled (dh_tile_head at load)",
                    "head_copies_rotated": NCOPY, "step_bytes": step_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -253,14 +266,18 @@ def main():
                      "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H),
                      "kernel_us": round(gemv_avg_ms * 1e3, 2),
                      "algorithmic_bytes": step_bytes, "kernel_source": gemv_source_hash()},
+        "row_major_head_gemv": {"us": rm_us,
+                                "GBps": round(step_bytes / (rm_us * 1e-6) / 1e9, 1),
+                                "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H, tiled=False)},
         "quantize_fp8_block32_ms": round(quant_ms, 3),
+        "tile_head_ms": round(tile_ms, 3),
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, V, H, R, K)
     if not args.quick:
         # the row sweep has a workload of its own (its head and 16 activation rows)
-        del heads, logits, ids, vals, am, ws, out_bufs, wd, xd
+        del heads, rm_heads, logits, ids, vals, am, ws, out_bufs, wd, xd
         torch.cuda.empty_cache()
         sw = "row_sweep"
         wd = torch.from_numpy(synth.head_bf16(sw).view(np.int16)).to(dev)
@@ -328,11 +345,23 @@ def timed(fn, n, warm=3):
     return [a.elapsed_time(b) for a, b in ev]
 
 
-def sweep(dh, torch, heads, wd, xd, V, H, K, n):
-    res = {"fp8_block32": [], "bf16": []}
+def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
+    """The row sweep on tiled heads (FP8 and bf16), with the row-major heads' GEMV at 1 and
+    16 rows beside it; then the two-stage head, the softmax statistics and the keyed pick."""
+    res = {"layout": "tiled", "fp8_block32": [], "bf16": [], "row_major_gemv_us": {}}
     dense = [dh.Head(dh.BF16, wd)] + [dh.Head(dh.BF16, wd.clone()) for _ in range(1)]
+    heads = [dh.tile(h) for h in rm_heads]
+    dense_t = [dh.tile(h) for h in dense]
     torch.cuda.synchronize()
-    for fmt, hs in (("fp8_block32", heads), ("bf16", dense)):
+    for fmt, hs in (("fp8_block32", rm_heads), ("bf16", dense)):
+        res["row_major_gemv_us"][fmt] = {}
+        for R in (1, 16):
+            x = xd[:R].contiguous()
+            lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
+            res["row_major_gemv_us"][fmt][str(R)] = back_to_back_us(
+                lambda i: dh.gemv(hs[i % len(hs)], x, lg), n)
+    log(f"row-major heads, gemv back to back: {res['row_major_gemv_us']}")
+    for fmt, hs in (("fp8_block32", heads), ("bf16", dense_t)):
         for R in (1, 5, 10, 15, 16):
             x = xd[:R].contiguous()
             lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
@@ -358,7 +387,7 @@ def sweep(dh, torch, heads, wd, xd, V, H, K, n):
                 f"gemv {bb['dh_gemv']:.1f}, topk {bb['dh_topk']:.1f}, draft {bb['dh_draft']:.1f}")
     # two-stage: FP8 row-scaled stage 1 + dense bf16 rescore of 512 candidates, 16 rows
     rc, rs = dh.quantize(wd, dh.FP8_ROW)
-    h1 = dh.Head(dh.FP8_ROW, rc, rs)
+    h1 = dh.tile(dh.Head(dh.FP8_ROW, rc, rs))
     R, k = 16, 512
     ws = dh.workspace(R, V, k)
     o = {"ids": torch.empty((R, k), dtype=torch.int32, device=xd.device),
@@ -435,8 +464,10 @@ def subset_sweep(dh, torch, n):
     fg = lambda i: dh.gather_rows(fulls[i % NCOPY], im, out=subs[i % NCOPY])
     gat = back_to_back_us(fg, n)
     gbytes = 2 * nd * H + 2 * nd * 4 + nd * 4
+    # both heads are projected from their tiled copies (the subset tiled after the gather)
+    fulls_t, subs_t = [dh.tile(h) for h in fulls], [dh.tile(h) for h in subs]
     res = {"workload": f"FP8 E4M3 head with a row scale, H={H}, V={V}; subset of {nd} "
-                       f"sorted token ids; top-{K}",
+                       f"sorted token ids; top-{K}; both heads tiled",
            "gather_us": gat, "gather_bytes": gbytes,
            "gather_GBps": round(gbytes / (gat * 1e-6) / 1e9, 1), "rows": []}
     for R in (1, 16, 32):
@@ -446,8 +477,8 @@ def subset_sweep(dh, torch, n):
                       "vals": torch.empty((R, K), dtype=torch.float32, device=dev),
                       "draft": torch.empty((R,), dtype=torch.int32, device=dev)}
         of, os_ = mk(), mk()
-        ff = lambda i: dh.draft(fulls[i % NCOPY], x, K, ws=ws_f, out=of)
-        fs = lambda i: dh.draft_mapped(subs[i % NCOPY], im, x, K, ws=ws_s, out=os_)
+        ff = lambda i: dh.draft(fulls_t[i % NCOPY], x, K, ws=ws_f, out=of)
+        fs = lambda i: dh.draft_mapped(subs_t[i % NCOPY], im, x, K, ws=ws_s, out=os_)
         tf, ts = back_to_back_us(ff, n), back_to_back_us(fs, n)
         bf = algorithmic_bytes("fp8_row", V, H, R)
         bs = algorithmic_bytes("fp8_row", nd, H, R)
@@ -477,8 +508,8 @@ def lowrank_sweep(dh, torch, n):
     ups = [torch.from_numpy(up.view(np.int16)).to(dev) for _ in range(NCOPY)]
     dense = dh.Head(dh.BF16, torch.from_numpy(synth.head_bf16(name).view(np.int16)).to(dev))
     x = torch.from_numpy(synth.activations(name, R).view(np.int16)).to(dev)
-    hd = dh.Head(dh.BF16, dn)
-    hu = [dh.Head(dh.BF16, u) for u in ups]
+    hd = dh.tile(dh.Head(dh.BF16, dn))                 # both factors tiled at load
+    hu = [dh.tile(dh.Head(dh.BF16, u)) for u in ups]
     ws = dh.workspace(R, V, k)
     o = {"ids": torch.empty((R, k), dtype=torch.int32, device=dev),
          "vals": torch.empty((R, k), dtype=torch.float32, device=dev),

@@ -308,3 +308,46 @@ def test_sample_refusals(no_device):
     assert c(rows=0) == 1 and c(rows=33) == 2 and c(kk=0) == 1 and c(kk=513) == 2
     assert c(t=ids) == 1                          # token overlaps the candidates
     assert tok.untouched() and kept.untouched()
+
+
+def test_tiled_bytes():
+    # ceil(V/16) tiles x ceil(H/64) blocks x 1 KiB x bytes per element
+    assert dh.tiled_bytes(dh.FP8_BLOCK32, 129280, 5120) == 8080 * 80 * 1024
+    assert dh.tiled_bytes(dh.FP8_BLOCK32 | dh.TILED, 129280, 5120) == 8080 * 80 * 1024
+    assert dh.tiled_bytes(dh.BF16, 129280, 5120) == 8080 * 80 * 2048
+    assert dh.tiled_bytes(dh.FP8_ROW, 37, 96) == 3 * 2 * 1024
+    assert dh.tiled_bytes(dh.BF16, 16, 32) == 1 * 1 * 2048
+    assert dh.tiled_bytes(dh.FP8_ROW, 0, 96) == 0
+    assert dh.tiled_bytes(dh.FP8_ROW, 100, 48) == 0
+    assert dh.tiled_bytes(dh.FP8_ROW, 100, 8224) == 0
+    assert dh.tiled_bytes(7, 100, 64) == 0
+    assert dh.tiled_bytes(dh.FP8_ROW | 32, 100, 64) == 0
+
+
+def test_tiled_refusals(no_device):
+    V, H = 100, 64
+    w, s, x, out = HostBuf(V * H), HostBuf(4 * H // 32), HostBuf(16 * H * 2), HostBuf(16 * V * 4)
+    tb = dh.tiled_bytes(dh.FP8_BLOCK32, V, H)
+    tw = HostBuf(tb)
+    L = dh.lib()
+    ok = head(dh.FP8_BLOCK32, V, H, w, s)
+    # dh_tile_head: a tiled source, a null or misaligned target, a target over the head
+    assert L.dh_tile_head(ctypes.byref(head(dh.FP8_BLOCK32 | dh.TILED, V, H, w, s)), tw.p,
+                          None) == 1
+    assert L.dh_tile_head(ctypes.byref(ok), None, None) == 1
+    assert L.dh_tile_head(ctypes.byref(ok), ctypes.c_void_p(tw.a.ctypes.data + 8), None) == 1
+    assert L.dh_tile_head(ctypes.byref(ok), w.p, None) == 1
+    assert L.dh_tile_head(ctypes.byref(head(dh.FP8_BLOCK32, V, 48, w, s)), tw.p, None) == 1
+    assert tw.untouched()
+    # a tiled head: unknown modifier bits, output over the tiled weight, a tiled dense head
+    th = head(dh.FP8_BLOCK32 | dh.TILED, V, H, tw, s)
+    assert call_gemv(head(dh.FP8_BLOCK32 | 64, V, H, tw, s), x, 1, out) == 1
+    assert call_gemv(th, x, 1, tw) == 1
+    assert out.untouched()
+    dense_t = head(dh.BF16 | dh.TILED, V, H, HostBuf(dh.tiled_bytes(dh.BF16, V, H)))
+    ids, exact, draft = HostBuf(4 * 4), HostBuf(4 * 4), HostBuf(4)
+    assert L.dh_rescore(ctypes.byref(dense_t), x.p, 1, ids.p, 4, exact.p, draft.p, None) == 1
+    assert exact.untouched() and draft.untouched()
+    gw = HostBuf(10 * H * 2)
+    assert L.dh_gather_rows(ctypes.byref(dense_t), ids.p, 4, gw.p, None, None) == 1
+    assert gw.untouched()

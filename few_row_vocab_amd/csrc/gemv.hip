@@ -44,6 +44,14 @@ constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data 
 // 1 KiB of whole lines, and there the non-temporal hint streams ~11% faster than plain loads.
 constexpr int kCachePolicy = 0;
 constexpr int kCacheNT = 2;              // gfx950 cache policy bit 1: non-temporal
+// Tiled heads: weight bytes a workgroup keeps in flight (KiB), so a wave refills only a
+// window of blocks ahead rather than a whole tile.  A streaming-read probe with the
+// non-temporal hint peaked with about 32 KiB in flight per compute unit (7.0 TB/s) and fell
+// with more (6.65 TB/s at 64 KiB).  In the GEMV at H = 5120, 32 KiB (FP8) and 48 KiB (bf16)
+// measured best, by about 1% over a whole tile in flight; 16 and 24 KiB (one FP8 block a
+// wave) were 15% slower.
+template <int FMT>
+constexpr int tiled_ahead_kib() { return FMT == DH_BF16 ? 48 : 32; }
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
 constexpr int kMaxDevices = 64;
 
@@ -140,6 +148,10 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     constexpr int TILE = 16 * TR;                // head rows per tile
     constexpr int OUTS = TILE * 16 * NB;         // (head row, activation row) sums per tile
     constexpr int KW = VW * KBW;                 // 64-column blocks of one wave
+    // blocks a wave keeps in flight: a whole tile (row-major heads), or a window sized so a
+    // full workgroup (16 / VW waves) holds about tiled_ahead_kib (tiled heads)
+    constexpr int AHW = tiled_ahead_kib<FMT>() * VW / (kMaxWaves * RQ);
+    constexpr int AH = !TL ? KW : AHW < 1 ? 1 : AHW > KW ? KW : AHW;
     __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
     extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
 
@@ -242,19 +254,20 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
 
     int tile = blockIdx.x;   // the launch keeps gridDim.x <= ntiles
     uint32_t sbytes;
+    __amdgpu_buffer_rsrc_t wcur[TR];             // this tile's descriptors
     {
-        __amdgpu_buffer_rsrc_t wr[TR], sr;
-        rsrcs(tile, true, wr, sr);
+        __amdgpu_buffer_rsrc_t sr;
+        rsrcs(tile, true, wcur, sr);
         sbytes = load_scales(sr);
 #pragma unroll
-        for (int kb = 0; kb < KW; kb++)
-            load_block(wr, kb);
+        for (int kb = 0; kb < AH; kb++)
+            load_block(wcur, kb);
     }
     int buf = 0, it = 0;
     for (;; it++) {
         const int next = tile + gridDim.x;
         const bool more = next < a.ntiles;
-        __amdgpu_buffer_rsrc_t wr[TR], sr;
+        __amdgpu_buffer_rsrc_t wr[TR], sr;       // the next tile's descriptors
         rsrcs(more ? next : tile, more, wr, sr);
         const uint32_t sbytes_next = load_scales(sr);
 
@@ -287,7 +300,12 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
                     widen16(raw[r][kb][0], scale, a0[r], a1[r]);
                 }
             }
-            load_block(wr, kb);
+            // the refill: AH blocks ahead, wrapping into the next tile (AH == KW: this slot's
+            // block of the next tile)
+            if (kb + AH < KW)
+                load_block(wcur, kb + AH);
+            else
+                load_block(wr, kb + AH - KW);
             // keep the refill here: the scheduler would otherwise sink every load below the
             // last MFMA, and the pipeline would drain once per tile
             __builtin_amdgcn_sched_barrier(0);
@@ -333,6 +351,9 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             break;
         tile = next;
         sbytes = sbytes_next;
+#pragma unroll
+        for (int r = 0; r < TR; r++)
+            wcur[r] = wr[r];
     }
     __syncthreads();
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave

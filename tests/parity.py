@@ -89,14 +89,16 @@ def check_topk_row(ids, vals, orc_row, k, tol, r=0, what="top-k"):
         return "exact"
     ov = orc_row.astype(np.float64)
     Lk = ov[order[kk - 1]]
-    gap = ov[order[kk - 1]] - ov[order[kk]] if n > k else np.inf
+    # equal neighbours (+inf ones included) are 0 apart, not inf - inf
+    step = lambda a, b: 0.0 if a == b else a - b
+    gap = step(ov[order[kk - 1]], ov[order[kk]]) if n > k else np.inf
     if gap > 2 * tol:
         assert set(gi.tolist()) == set(order[:kk].tolist()), \
             f"{what} row {r}: id set differs from the oracle (gap {gap:.3e} > 2tol {2*tol:.3e})"
         # clusters of oracle values closer than 2 tol may be permuted
         cl = np.zeros(kk, np.int64)
         for j in range(1, kk):
-            cl[j] = cl[j - 1] + (ov[order[j - 1]] - ov[order[j]] > 2 * tol)
+            cl[j] = cl[j - 1] + (step(ov[order[j - 1]], ov[order[j]]) > 2 * tol)
         cluster = {int(v): int(c) for v, c in zip(order[:kk], cl)}
         seq = np.array([cluster[int(v)] for v in gi])
         assert np.array_equal(seq, cl), f"{what} row {r}: order differs across separated values"

@@ -13,7 +13,9 @@
 Checks at each: codes and scales of the GPU quantizer equal the oracle's; every logit
 within tolerance of the oracle (the oracle computes all of them); the GPU top-k equals the
 oracle's top-k of the GPU's own logits bit for bit; the ids follow the gap rule against the
-oracle's logits; two-stage through the conditional oracle.
+oracle's logits; two-stage through the conditional oracle.  Every draft also runs on the
+head's tiled copy (dh_tile_head, the layout the benchmark times), whose logits, ids, values
+and drafts must equal the row-major head's bit for bit.
 """
 import numpy as np
 import pytest
@@ -65,9 +67,17 @@ def exact_topk_on_gpu_logits(glog, ids, vals, k):
     assert np.array_equal(vals.view(np.uint32), ov.view(np.uint32))
 
 
-def run_one_stage(head, x, k, want, R):
+def same_outputs(a, b, names):
+    for n in names:
+        assert host(a[n]).tobytes() == host(b[n]).tobytes(), f"tiled head: {n} differs"
+
+
+def run_one_stage(head, x, k, want, R, tiled=None):
     xd = dev_u16(x[:R])
     out = dh.draft(head, xd, k, keep_logits=True)
+    if tiled is not None:
+        same_outputs(out, dh.draft(tiled, xd, k, keep_logits=True),
+                     ("logits", "ids", "vals", "draft"))
     torch.cuda.synchronize()
     glog, ids, vals, dr = (host(out[n]) for n in ("logits", "ids", "vals", "draft"))
     tols = check_logits(glog, want[:R])
@@ -96,8 +106,9 @@ def test_fp8_block_1row():
     same_quant(codes, scale, oc, osc)
     want = oracle.gemv(oracle.FMT_FP8_BLOCK32, oc, osc, x)
     head = dh.Head(dh.FP8_BLOCK32, codes, scale)
+    tiled = dh.tile(head)
     for k in c["ks"]:
-        _, kinds = run_one_stage(head, x, k, want, 1)
+        _, kinds = run_one_stage(head, x, k, want, 1, tiled)
         say(f"fp8_block_1row k={k}: {kinds}")
 
 
@@ -114,9 +125,10 @@ def test_row_sweep(fmt):
         same_quant(codes, scale, oc, osc)
         head = dh.Head(dh.FP8_BLOCK32, codes, scale)
         want = oracle.gemv(oracle.FMT_FP8_BLOCK32, oc, osc, x)
+    tiled = dh.tile(head)
     first = None
     for R in c["rows"]:
-        glog, kinds = run_one_stage(head, x, 64, want, R)
+        glog, kinds = run_one_stage(head, x, 64, want, R, tiled)
         say(f"row_sweep {fmt} R={R}: {kinds}")
         if first is None:
             first = glog
@@ -135,6 +147,8 @@ def test_two_stage():
     dense = dh.Head(dh.BF16, dev_u16(w))
     xd = dev_u16(x)
     out = dh.draft(head, xd, k, dense=dense, keep_logits=True)
+    same_outputs(out, dh.draft(dh.tile(head), xd, k, dense=dense, keep_logits=True),
+                 ("logits", "ids", "vals", "exact", "draft"))
     torch.cuda.synchronize()
     glog, ids, vals, exact, dr = (host(out[n]) for n in ("logits", "ids", "vals", "exact", "draft"))
     want = oracle.gemv(oracle.FMT_FP8_ROW, oc, osc, x)
@@ -156,9 +170,10 @@ def test_edge():
     same_quant(codes, scale, oc, osc)
     want = oracle.gemv(oracle.FMT_FP8_BLOCK32, oc, osc, x)
     head = dh.Head(dh.FP8_BLOCK32, codes, scale)
+    tiled = dh.tile(head)
     hot = np.arange(synth.EDGE_HOT_BLOCK * 32, synth.EDGE_HOT_BLOCK * 32 + 32)
     for k in c["ks"]:
-        glog, kinds = run_one_stage(head, x, k, want, 16)
+        glog, kinds = run_one_stage(head, x, k, want, 16, tiled)
         say(f"edge k={k}: {kinds}")
         assert np.all(np.isnan(glog[synth.EDGE_NAN_ROW]))
         assert np.all(glog[synth.EDGE_ZERO_ROW] == 0)

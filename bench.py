@@ -244,8 +244,16 @@ def main():
     achieved = step_bytes / (gemv_avg_ms * 1e-3) / 1e9
     # the same GEMV from the row-major head (not the benchmarked layout), for comparison
     rm_us = back_to_back_us(lambda i: dh.gemv(rm_heads[i % NCOPY], xd, logits), args.steps)
+    # the device's practical streaming-read bandwidth: dh_stream_read over the same tiled head
+    # bytes (the three copies rotated), read the way the GEMV reads them
+    sink = torch.empty((dh.STREAM_SINK_WORDS,), dtype=torch.int32, device=dev)
+    sr_bytes = heads[0].weight.numel()
+    sr_us = back_to_back_us(lambda i: dh.stream_read(heads[i % NCOPY].weight, sink),
+                            args.steps)
+    sr_gbps = sr_bytes / (sr_us * 1e-6) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us, gemv {gemv_avg_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s); row-major head gemv {rm_us:.1f} us")
+        f"({achieved:.0f} GB/s); row-major head gemv {rm_us:.1f} us; stream read "
+        f"{sr_gbps:.0f} GB/s")
 
     out = {
         "metric": "draft-head µs/call and achieved HBM GB/s (FP8 head, 1/5/10/16 rows)",
@@ -266,6 +274,11 @@ def main():
                      "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H),
                      "kernel_us": round(gemv_avg_ms * 1e3, 2),
                      "algorithmic_bytes": step_bytes, "kernel_source": gemv_source_hash()},
+        "stream_read": {"bytes": sr_bytes, "us": sr_us, "GBps": round(sr_gbps, 1),
+                        "frac_of_8TBps": round(sr_gbps / PEAK_HBM_GBPS, 4),
+                        "gemv_frac_of_stream_read": round(achieved / sr_gbps, 4),
+                        "kernel": "dh_stream_read (1 KiB non-temporal loads, 32 KiB in "
+                                  "flight per CU)"},
         "row_major_head_gemv": {"us": rm_us,
                                 "GBps": round(step_bytes / (rm_us * 1e-6) / 1e9, 1),
                                 "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H, tiled=False)},

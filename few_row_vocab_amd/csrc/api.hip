@@ -508,6 +508,15 @@ size_t dh_tiled_bytes(int32_t format, int64_t vocab, int64_t hidden)
     return dh::tiled_bytes(format, vocab, hidden);
 }
 
+dh_status dh_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4) || bytes == 0 || bytes % 4096)
+        return DH_ERR_INVALID;
+    if (overlap(span(buf, bytes), span(sink, DH_STREAM_SINK_WORDS * sizeof(uint32_t))))
+        return DH_ERR_INVALID;
+    return device_status(dh::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream)
 {

@@ -41,6 +41,9 @@ size_t tiled_bytes(int format, int64_t vocab, int64_t hidden);
 hipError_t launch_quantize(int format, const uint16_t *w, int64_t vocab, int64_t hidden,
                            uint8_t *codes, void *scale, hipStream_t stream);
 
+// The streaming-read probe (dh_stream_read).
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cus();
 

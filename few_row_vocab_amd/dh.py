@@ -74,6 +74,7 @@ def lib():
         L.dh_topk_mapped.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_mapped.argtypes = [hp, vp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_tile_head.argtypes = [hp, vp, vp]
+        L.dh_stream_read.argtypes = [vp, sz, vp, vp]
         L.dh_tiled_bytes.argtypes = [i32, i64, i64]
         L.dh_tiled_bytes.restype = sz
         L.dh_workspace_bytes.argtypes = [i32, i64, i32]
@@ -82,7 +83,8 @@ def lib():
         L.dh_status_string.restype = c.c_char_p
         for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
-                  L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample, L.dh_tile_head):
+                  L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample, L.dh_tile_head,
+                  L.dh_stream_read):
             f.restype = i32
         _lib = L
     return _lib
@@ -463,6 +465,22 @@ def quantize(w, format, stream=None):
         raise ValueError("format must be FP8_BLOCK32 or FP8_ROW")
     _check(lib().dh_quantize(format, _ptr(w), V, H, _ptr(codes), _ptr(scale), _stream(stream)))
     return codes, scale
+
+
+STREAM_SINK_WORDS = 8192
+
+
+def stream_read(buf, sink=None, stream=None):
+    """dh_stream_read: a diagnostic read of a device buffer (uint8, size a multiple of 4096)
+    the way the GEMV streams a tiled head; returns the sink (int32 [STREAM_SINK_WORDS]) whose
+    words sum, mod 2^32, to the sum of the buffer's 32-bit words."""
+    _want(buf, buf.dtype, "buf")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty((STREAM_SINK_WORDS,), dtype=torch.int32, device=buf.device)
+    _shaped(sink, (STREAM_SINK_WORDS,), torch.int32, "sink")
+    _check(lib().dh_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def status_string(status):

@@ -281,6 +281,16 @@ dh_status dh_tile_head(const dh_head *head, void *tiled, void *stream);
  * refuses. */
 size_t dh_tiled_bytes(int32_t format, int64_t vocab, int64_t hidden);
 
+/* dh_stream_read -- a diagnostic, not a step of the projection: reads `bytes` of device
+ * memory once, the way the GEMV streams a tiled head (1 KiB contiguous loads with the
+ * non-temporal hint, about 32 KiB in flight per compute unit), so that its duration gives
+ * the device's practical streaming-read bandwidth to report beside the GEMV's.  buf: device,
+ * 16-byte aligned; bytes: a positive multiple of 4096.  sink: device uint32
+ * [DH_STREAM_SINK_WORDS]; afterwards its words sum (mod 2^32) to the sum of buf's 32-bit
+ * words, which shows that every byte was read exactly once.  sink must not overlap buf. */
+#define DH_STREAM_SINK_WORDS 8192
+dh_status dh_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Bytes of workspace dh_topk and dh_draft need for these sizes (dh_draft with logits ==
  * NULL included).  Pure host function; returns 0 for sizes the library refuses. */
 size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k);

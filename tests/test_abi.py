@@ -351,3 +351,15 @@ def test_tiled_refusals(no_device):
     gw = HostBuf(10 * H * 2)
     assert L.dh_gather_rows(ctypes.byref(dense_t), ids.p, 4, gw.p, None, None) == 1
     assert gw.untouched()
+
+
+def test_stream_read_refusals(no_device):
+    buf, sink = HostBuf(8192), HostBuf(dh.STREAM_SINK_WORDS * 4)
+    L = dh.lib()
+    assert L.dh_stream_read(None, 8192, sink.p, None) == 1
+    assert L.dh_stream_read(buf.p, 8192, None, None) == 1
+    assert L.dh_stream_read(buf.p, 0, sink.p, None) == 1
+    assert L.dh_stream_read(buf.p, 4100, sink.p, None) == 1
+    assert L.dh_stream_read(ctypes.c_void_p(buf.a.ctypes.data + 4), 4096, sink.p, None) == 1
+    assert L.dh_stream_read(buf.p, 8192, ctypes.c_void_p(buf.a.ctypes.data + 4096), None) == 1
+    assert sink.untouched() and buf.untouched()

@@ -415,6 +415,13 @@ def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
     t = stats_us(timed(lambda i: dh.topk(lg, k, ws=ws, ids=o["ids"], vals=o["vals"]), n))
     s = stats_us(timed(lambda i: dh.rescore(dense[0], xd, o["ids"], exact=o["exact"],
                                             draft=o["draft"]), n))
+    # the same ids every call stay in the Infinity Cache; a cold gather rotates four sets of
+    # uniformly random candidate ids (4 x 84 MB of rows)
+    gen = torch.Generator(device=xd.device).manual_seed(404)
+    sets = [torch.randint(0, V, (R, k), dtype=torch.int32, device=xd.device, generator=gen)
+            for _ in range(4)]
+    s_cold = back_to_back_us(lambda i: dh.rescore(dense[0], xd, sets[i % 4], exact=o["exact"],
+                                                   draft=o["draft"]), n)
     b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
     # the top-k with the softmax statistics (probabilities of the kept entries, each row's
     # log-sum-exp) against the plain top-k, on the FP8 head's 16-row logits, top-64
@@ -447,6 +454,8 @@ def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
         f"{sm['dh_sample_k64_graph_us']:.1f} and {sm['dh_sample_k512_graph_us']:.1f} us")
     res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
                         "dh_topk_us": t, "dh_rescore_us": s, "dh_draft_back_to_back_us": dbb,
+                        "dh_rescore_rotated_ids_us": s_cold,
+                        "rescore_rotated_GBps": round(R * k * H * 2 / (s_cold * 1e-6) / 1e9, 1),
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
     log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
         f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f})")

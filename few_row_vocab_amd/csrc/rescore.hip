@@ -7,7 +7,7 @@
 // Design: the work is a gather of rows*cand_k head rows (10 KB each at H = 5120) -- memory
 // bound, with one activation row per gathered head row, so plain FP32 FMAs on the vector
 // ALUs.  One wave per (row, slot): each lane reads 16 bytes of the head row and of the
-// activation row per step (a wave covers 1 KB of the head row per load), with eight steps
+// activation row per step (a wave covers 1 KB of the head row per load), with five steps
 // in flight before any is summed, sums its products in order, and the wave sums lanes with
 // a fixed butterfly.  A second small kernel picks
 // each row's winner under the same ordering as the top-k.
@@ -18,7 +18,11 @@ namespace dh {
 namespace {
 
 constexpr int kRescoreWaves = 4;
-constexpr int kSteps = 8;                // 512-column steps a lane has in flight
+// 512-column steps a lane has in flight: a 10 KB row (H = 5120) is two rounds.  Over four
+// rotated sets of 16 x 512 random candidates (a cold gather) five measured 18.4 us, two
+// 18.4-18.7, four 19.0 and eight 20.1: with 32 waves a compute unit, more in flight only
+// queues.
+constexpr int kSteps = 5;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(
     } else if (id < 0 || id >= V) {
         out = __builtin_nanf("");         // not a token of this head: never read
     } else {
-        // bounded buffer loads (bytes past the row read as 0, adding nothing), eight steps of
+        // bounded buffer loads (bytes past the row read as 0, adding nothing), kSteps steps of
         // 512 columns issued before any is used
         const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(W + id * H), (short)0, H * 2, kRsrcWord3);

@@ -53,10 +53,15 @@ def stats_us(times_ms):
 
 
 def gemv_source_hash():
+    """Hash of the GEMV kernel's code: its sources with comments and whitespace removed, so
+    that a comment edit does not void counters taken on the same code."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -23,9 +23,15 @@
 //    row l%16 at column 16*(l/16) of each 64-column block.  The waves' partial 16x16 tiles
 //    are summed through LDS in a fixed wave order (deterministic) and written as fp32.
 //  * Persistent grid: one workgroup per CU slot, tiles taken round-robin; each 64-column
-//    block's registers are refilled with the next tile as soon as they are widened, so a
-//    tile of loads is always in flight, also across the reduction's barrier.  The loop
-//    has no branches around loads and no stores (logits wait in LDS until the end).
+//    block's registers are refilled as soon as they are widened (row-major heads: with the
+//    same block of the next tile, so a tile of loads is always in flight; tiled heads: with
+//    the block a fixed window ahead, wrapping into the next tile), also across the
+//    reduction's barrier.  The loop has no branches around loads and no stores (logits wait
+//    in LDS until the end).
+//  * Tiled heads (DH_TILED, made at load): each 1 KiB of the weight is one wave's operand
+//    in lane order, so every load reads whole lines and carries the non-temporal hint; the
+//    lanes receive the same bytes as from the row-major head, so the results are the same
+//    bits.
 #include "dh_internal.h"
 #include "launch.h"
 

@@ -32,14 +32,17 @@ def _same(a, b):
         assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), n
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("two", [False, True])
-def test_graph_replays_equal_eager(two):
+def test_graph_replays_equal_eager(two, tiled):
     need_gpu()
     V, H, R, k = 20000, 1024, 16, 64
     w = synth.random_head(V, H, seed=5, std=0.02)
     wd = dev_u16(w)
     codes, scale = dh.quantize(wd, dh.FP8_BLOCK32 if not two else dh.FP8_ROW)
     head = dh.Head(dh.FP8_BLOCK32 if not two else dh.FP8_ROW, codes, scale)
+    if tiled:
+        head = dh.tile(head)
     dense = dh.Head(dh.BF16, wd) if two else None
     x = dev_u16(synth.random_acts(R, H, seed=6))
     ws = dh.workspace(R, V, k)

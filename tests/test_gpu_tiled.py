@@ -79,10 +79,11 @@ def test_tiled_gemv_bit_equal(fmt, V, H, R):
     check_logits(b, oracle.gemv(FMTS[fmt][1], ow, osc, x), what="tiled gemv")
 
 
+@pytest.mark.parametrize("R", [16, 32])
 @pytest.mark.parametrize("fmt", ["bf16", "row"])
-def test_tiled_linear_modes(fmt):
+def test_tiled_linear_modes(fmt, R):
     need_gpu()
-    N, K, R = 3001, 2048, 16
+    N, K = 3001, 2048
     w = synth.random_head(N, K, seed=91, std=0.02)
     x = synth.random_acts(R, K, seed=92)
     res = synth.random_acts(R, N, seed=93, std=0.5)
@@ -112,9 +113,10 @@ def test_tiled_draft_bit_equal(R, k):
         assert host(a[n]).tobytes() == host(b[n]).tobytes(), n
 
 
-def test_tiled_two_stage_and_lowrank():
+@pytest.mark.parametrize("R", [16, 32])
+def test_tiled_two_stage_and_lowrank(R):
     need_gpu()
-    V, H, R, k, r = 8000, 1024, 16, 128, 256
+    V, H, k, r = 8000, 1024, 128, 256
     w = synth.random_head(V, H, seed=111, std=0.02)
     x = synth.random_acts(R, H, seed=112)
     gr, _ = make_heads("row", w)
@@ -122,7 +124,8 @@ def test_tiled_two_stage_and_lowrank():
     xd = dev_u16(x)
     a = dh.draft(gr, xd, k, dense=dense)
     b = dh.draft(dh.tile(gr), xd, k, dense=dense)
-    # low rank: a few-tile down linear (r rows: the split over virtual waves) and the up GEMV
+    # low rank: a few-tile down linear (r rows: the split over virtual waves, two 16-row
+    # column blocks at 32 rows) and the up GEMV
     down = dh.Head(dh.BF16, dev_u16(synth.random_head(r, H, seed=113, std=0.03)))
     up = dh.Head(dh.BF16, dev_u16(synth.random_head(V, r, seed=114, std=0.06)))
     c = dh.draft_lowrank(down, up, xd, k, dense=dense)

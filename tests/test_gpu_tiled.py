@@ -63,7 +63,8 @@ def test_tile_layout(fmt, V, H):
 @pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
 @pytest.mark.parametrize("V,H,R", [(37, 32, 1), (1000, 96, 16), (4133, 1376, 5),
                                    (515, 7168, 16), (2051, 5120, 32), (9000, 1056, 20),
-                                   (70, 4096, 32)])
+                                   (70, 4096, 32), (1, 64, 1), (17, 8192, 3),
+                                   (300, 6144, 17)])
 def test_tiled_gemv_bit_equal(fmt, V, H, R):
     need_gpu()
     say(f"tiled gemv {fmt} V={V} H={H} R={R}")

@@ -197,6 +197,12 @@ def main():
     qe[1].record()
     torch.cuda.synchronize()
     quant_ms = qe[0].elapsed_time(qe[1])
+    # the same quantization written straight into the tiled layout
+    qe[0].record()
+    dh.quantize(wd, dh.FP8_BLOCK32 | dh.TILED)
+    qe[1].record()
+    torch.cuda.synchronize()
+    quant_tiled_ms = qe[0].elapsed_time(qe[1])
 
     logits = torch.empty((R, V), dtype=torch.float32, device=dev)
     ids = torch.empty((R, K), dtype=torch.int32, device=dev)
@@ -289,6 +295,7 @@ def main():
                                 "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H, tiled=False)},
         "quantize_fp8_block32_ms": round(quant_ms, 3),
         "tile_head_ms": round(tile_ms, 3),
+        "quantize_fp8_block32_tiled_ms": round(quant_tiled_ms, 3),
     }
 
     if not args.no_cpu_baseline:

@@ -520,13 +520,15 @@ dh_status dh_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *st
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream)
 {
-    if (format != DH_FP8_BLOCK32 && format != DH_FP8_ROW)
+    const int base = format & ~DH_TILED;   // codes row-major or (DH_TILED) tiled
+    if (!known_format(format) || (base != DH_FP8_BLOCK32 && base != DH_FP8_ROW))
         return DH_ERR_INVALID;
     if (vocab < 1 || hidden < 32 || hidden % 32 != 0)
         return DH_ERR_INVALID;
     if (hidden > DH_MAX_HIDDEN || vocab > (int64_t)INT32_MAX / 2)
         return DH_ERR_UNSUPPORTED;
-    if (!w || !codes || !scale || !aligned(w, 2) || (format == DH_FP8_ROW && !aligned(scale, 4)))
+    if (!w || !codes || !scale || !aligned(w, 2) || (base == DH_FP8_ROW && !aligned(scale, 4)) ||
+        ((format & DH_TILED) && !aligned(codes, 16)))
         return DH_ERR_INVALID;
     dh_head h{format, vocab, hidden, codes, scale};
     const Span sw = span(w, (size_t)vocab * (size_t)hidden * 2), sc = head_weight(h),

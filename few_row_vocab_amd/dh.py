@@ -451,18 +451,26 @@ def draft_mapped(head: Head, idmap, x, k, dense: Optional[Head] = None, **kw):
 
 
 def quantize(w, format, stream=None):
-    """FP8 head from a bf16 head [V][H]: (codes uint8 [V][H], scale)."""
+    """FP8 head from a bf16 head [V][H]: (codes uint8 [V][H], scale); with format | TILED the
+    codes come straight in the tiled layout (a flat uint8 buffer, as tile() makes)."""
     if w.dtype not in (torch.bfloat16, torch.int16):
         raise TypeError("w must be bfloat16 (or its int16 bits)")
     _want(w, w.dtype, "w")
     V, H = w.shape
-    codes = torch.empty((V, H), dtype=torch.uint8, device=w.device)
-    if format == FP8_BLOCK32:
+    base = format & ~TILED
+    if format & TILED:
+        n = tiled_bytes(format, V, H)
+        if n == 0:
+            raise DHError(2, "sizes outside the library's limits")
+        codes = torch.empty((n,), dtype=torch.uint8, device=w.device)
+    else:
+        codes = torch.empty((V, H), dtype=torch.uint8, device=w.device)
+    if base == FP8_BLOCK32:
         scale = torch.empty(((V + 31) // 32, H // 32), dtype=torch.uint8, device=w.device)
-    elif format == FP8_ROW:
+    elif base == FP8_ROW:
         scale = torch.empty((V,), dtype=torch.float32, device=w.device)
     else:
-        raise ValueError("format must be FP8_BLOCK32 or FP8_ROW")
+        raise ValueError("format must be FP8_BLOCK32 or FP8_ROW (optionally | TILED)")
     _check(lib().dh_quantize(format, _ptr(w), V, H, _ptr(codes), _ptr(scale), _stream(stream)))
     return codes, scale
 

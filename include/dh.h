@@ -193,7 +193,10 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
  *    stored as e + 127 clamped to [0, 254] (127 for an all-zero block), and code = E4M3
  *    round-to-nearest-even of w * 2^-e.  scale: device uint8 [ceil(V/32)][H/32].
  * E4M3 rounding saturates at +-448.  w: device bf16 bits [V][H] (finite values).  codes:
- * device uint8 [V][H]. */
+ * device uint8 [V][H]; or, with format | DH_TILED, the codes go straight into the tiled
+ * layout (zeros past V and H): device buffer of dh_tiled_bytes(format, V, H) bytes, 16-byte
+ * aligned, the same bytes dh_tile_head makes from the row-major codes.  The scale is the same
+ * either way. */
 dh_status dh_quantize(int32_t format, const uint16_t *w, int64_t vocab, int64_t hidden,
                       uint8_t *codes, void *scale, void *stream);
 

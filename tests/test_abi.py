@@ -176,6 +176,10 @@ def test_quantize_refusals(no_device):
     assert L.dh_quantize(dh.FP8_ROW, w.p, 0, 64, c.p, s.p, None) == 1
     assert L.dh_quantize(dh.FP8_ROW, w.p, 64, 64, None, s.p, None) == 1
     assert L.dh_quantize(dh.FP8_BLOCK32, w.p, 64, 64, w.p, s.p, None) == 1   # overlap
+    assert L.dh_quantize(dh.BF16 | dh.TILED, w.p, 64, 64, c.p, s.p, None) == 1
+    assert L.dh_quantize(dh.FP8_ROW | 64, w.p, 64, 64, c.p, s.p, None) == 1  # unknown bits
+    cm = ctypes.c_void_p(c.a.ctypes.data + 8)                                # tiled: 16-B
+    assert L.dh_quantize(dh.FP8_ROW | dh.TILED, w.p, 64, 64, cm, s.p, None) == 1
     assert c.untouched() and s.untouched()
 
 

@@ -175,3 +175,28 @@ def test_tiled_full_size_bit_equal(R):
     for n in ("logits", "ids", "vals", "draft"):
         assert torch.equal(a[n].view(torch.int32) if a[n].dtype == torch.float32 else a[n],
                            b[n].view(torch.int32) if b[n].dtype == torch.float32 else b[n]), n
+
+
+@pytest.mark.parametrize("fmt", ["block", "row"])
+@pytest.mark.parametrize("V,H", SHAPES + [(33, 96), (64, 8192)])
+def test_quantize_tiled_equals_tile_of_quantize(fmt, V, H):
+    """dh_quantize(format | DH_TILED) writes the same bytes (zero padding included) as
+    dh_tile_head of the row-major codes, and the same scale."""
+    need_gpu()
+    say(f"quantize tiled {fmt} V={V} H={H}")
+    w = dev_u16(synth.random_head(V, H, seed=V * 7 + H, std=0.02))
+    f = FMTS[fmt][0]
+    codes, scale = dh.quantize(w, f)
+    ref = dh.tile(dh.Head(f, codes, scale))
+    # into buffers pre-filled with 0xAB, so that padding left unwritten would show
+    tcodes = torch.full((dh.tiled_bytes(f, V, H),), 0xAB, dtype=torch.uint8, device="cuda")
+    tscale = torch.full_like(scale.view(torch.uint8), 0xAB).view(scale.dtype)
+    dh._check(dh.lib().dh_quantize(f | dh.TILED, dh._ptr(w), V, H, dh._ptr(tcodes),
+                                   dh._ptr(tscale), dh._stream(None)))
+    torch.cuda.synchronize()
+    assert host(tcodes).tobytes() == host(ref.weight).tobytes()
+    assert host(tscale).tobytes() == host(scale).tobytes()
+    # the binding's form gives the same bytes
+    bcodes, bscale = dh.quantize(w, f | dh.TILED)
+    torch.cuda.synchronize()
+    assert host(bcodes).tobytes() == host(ref.weight).tobytes()

@@ -274,7 +274,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) head quantized to FP8 on the GPU, N(0,1) rows)",
         "config": {"workload": f"FP8 E4M3 head with E8M0 32x32 block scales, H={H}, V={V}, "
-                               f"{R} activation rows, dh_draft: GEMV (fp32 logits kept) + "
+                               f"{R} activation row{'s' if R > 1 else ''}, dh_draft: GEMV (fp32 logits kept) + "
                                f"top-{K} and argmax",
                    "H": H, "V": V, "rows": R, "k": K, "format": "fp8_block32",
                    "layout": "tiled (dh_tile_head at load)",

@@ -548,8 +548,14 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
         case 2: return run_kbw<FMT, 2, 2, 2, TL>(a, stream);
         case 3: return run_kbw<FMT, 3, 2, 2, TL>(a, stream);
         case 4: return run_kbw<FMT, 4, 2, 2, TL>(a, stream);
+        // H <= 5120: 32 rows of activations fill 160 of a wave's 256 VGPRs, which still leaves
+        // room (218-246 VGPRs in all) except for the row-major bf16 tile, which spills
+        case 5:
+            if constexpr (FMT != DH_BF16 || TL)
+                return run_kbw<FMT, 5, 2, 2, TL>(a, stream);
+            [[fallthrough]];
         default: {
-            // H > 4096: 32 rows of activations do not fit the registers, so rows 0..15 and
+            // wider heads: 32 rows of activations do not fit the registers, so rows 0..15 and
             // 16.. take a launch each (the weights are read twice; every row keeps its bits)
             GemvArgs lo = a, hi = a;
             lo.R = 16;

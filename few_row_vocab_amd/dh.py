@@ -25,7 +25,7 @@ OUT_BF16 = 1
 OUT_ADD_BF16 = 2
 
 MAX_ROWS = 32
-MAX_HIDDEN_WIDE = 4096
+MAX_HIDDEN_WIDE = 5120   # 4096 for a row-major bf16 head
 MAX_K = 512
 MAX_HIDDEN = 8192
 MAX_VOCAB = 262144

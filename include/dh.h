@@ -89,11 +89,12 @@ typedef struct dh_head {
 /* Limits of this implementation (refused with DH_ERR_UNSUPPORTED beyond them).
  * Rows: [TFE] commit notes -- the head's own GEMV takes up to 16 rows; [SUPER] commit notes
  * on 32-row windows -- calls of 17 to 32 rows take the few-row forms too, each giving the same
- * bits as the 16-row form.  Up to H = DH_MAX_HIDDEN_WIDE such a call reads the head once (32
- * rows of activations held in registers); a wider head is read once per 16 rows.
+ * bits as the 16-row form.  Up to H = DH_MAX_HIDDEN_WIDE (4096 for a row-major bf16 head)
+ * such a call reads the head once (32 rows of activations held in registers); a wider head is
+ * read once per 16 rows.
  * k: [TFE] 'Update' -- the candidate count runs from 1 to 512. */
 #define DH_MAX_ROWS 32
-#define DH_MAX_HIDDEN_WIDE 4096    /* one pass over the head for more than 16 rows */
+#define DH_MAX_HIDDEN_WIDE 5120    /* one pass over the head for more than 16 rows */
 #define DH_MAX_K 512
 #define DH_MAX_HIDDEN 8192
 #define DH_MAX_VOCAB 262144        /* dh_topk / dh_draft */

@@ -5,7 +5,8 @@ C ABI, for the three weight formats.
  * the pages' bit-equality across row counts: each row of a 17..32-row call equals the same
    row of a 1-row and of a 16-row call bit for bit;
  * dh_linear's output modes, dh_draft (top-k of 32 rows) and the subset head at 32 rows;
- * above H = 4096 (two 16-row launches) the same parity and bit equality.
+ * H = 5120 (one pass for FP8 heads) and above (two 16-row launches): the same parity and
+   bit equality.
 """
 import numpy as np
 import pytest
@@ -102,12 +103,14 @@ def test_wide_subset_draft():
     assert np.array_equal(host(out["ids"]), oi)
 
 
+@pytest.mark.parametrize("H", [5120, 7168])
 @pytest.mark.parametrize("fmt", ["bf16", "block"])
-def test_wide_rows_on_a_wide_head(fmt):
-    """Above H = 4096 a 17..32-row call takes two 16-row launches: parity, and every row the
-    same bits as in a 16-row call."""
+def test_wide_rows_on_a_wide_head(fmt, H):
+    """At H = 5120 a 17..32-row call on an FP8 head runs in one pass (a row-major bf16 head
+    takes two 16-row launches), at H = 7168 both take two: parity, and every row the same bits
+    as in a 16-row call."""
     need_gpu()
-    V, H, R = 3001, 5120, 25
+    V, R = 3001, 25
     w = synth.random_head(V, H, seed=95, std=0.02)
     x = synth.random_acts(R, H, seed=96)
     gh, (ow, osc) = make_heads(fmt, w)

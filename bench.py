@@ -311,6 +311,7 @@ def main():
         out["sweep"] = sweep(dh, torch, heads, wd, xd, V, H, K, args.calls)
         del heads, wd, xd
         torch.cuda.empty_cache()
+        out["edge_shape"] = edge_shape(dh, torch, args.calls)
         out["subset_head"] = subset_sweep(dh, torch, args.calls)
         out["lowrank_two_stage"] = lowrank_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
@@ -471,6 +472,40 @@ def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
                         "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
     log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
         f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f})")
+    return res
+
+
+def edge_shape(dh, torch, n):
+    """The GEMV at a second shape, the edge-case workload's H=7168, V=163840 (7 blocks a wave):
+    FP8 E4M3 with E8M0 32x32 blocks quantized straight into the tiled layout from seeded
+    N(0, 0.02) weights made on the device (timing only; its parity is a test), three rotated
+    copies, 1 and 16 rows, dh_gemv and dh_draft (top-512) back to back."""
+    V, H = 163840, 7168
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(505)
+    heads = []
+    for _ in range(NCOPY):
+        w = (torch.randn((V, H), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        codes, scale = dh.quantize(w, dh.FP8_BLOCK32 | dh.TILED)
+        del w
+        heads.append(dh.Head(dh.FP8_BLOCK32 | dh.TILED, codes, scale, (V, H)))
+    res = {"workload": f"FP8 E4M3 head with E8M0 32x32 block scales, tiled, H={H}, V={V}",
+           "kernel": gemv_kernel_name(dh.FP8_BLOCK32, H), "rows": []}
+    for R in (1, 16):
+        x = torch.randn((R, H), device=dev, generator=g).to(torch.bfloat16)
+        lg = torch.empty((R, V), dtype=torch.float32, device=dev)
+        ws = dh.workspace(R, V, 512)
+        o = {}
+        tg = back_to_back_us(lambda i: dh.gemv(heads[i % NCOPY], x, lg), n)
+        td = back_to_back_us(lambda i: dh.draft(heads[i % NCOPY], x, 512, ws=ws, out=o), n)
+        b = algorithmic_bytes("fp8_block32", V, H, R)
+        res["rows"].append({"rows": R, "dh_gemv_us": tg, "gemv_GBps": round(b / (tg * 1e-6) / 1e9, 1),
+                            "frac_of_8TBps": round(b / (tg * 1e-6) / 8e12, 4),
+                            "dh_draft_top512_us": td})
+        log(f"edge shape R={R}: gemv {tg:.1f} us ({b / (tg * 1e-6) / 1e9:.0f} GB/s), "
+            f"draft top-512 {td:.1f} us")
+    del heads
+    torch.cuda.empty_cache()
     return res
 
 

@@ -373,50 +373,34 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
         return DH_ERR_WORKSPACE;
     float *L = logits ? logits : reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
-    // The stage-1 outputs and the workspace must be clear of the inputs and of each other.
-    const Span sl = span(L, lbytes), sw = span(workspace, tw.bytes);
+    DH_TRY(check_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft, workspace,
+                      tw.bytes));
+    if (dense)
+        DH_TRY(check_rescore(dense, x, rows, ids, k, exact, draft));
+    // Every buffer the call writes -- the logits, the workspace's top-k part, ids, vals,
+    // draft, exact and t -- must be clear of every buffer it reads and of every other one it
+    // writes (the rescore reads the stage-1 ids and values while it writes exact and draft).
+    const size_t rk = (size_t)rows * (size_t)k * 4;
     const Span in[] = {head_weight(*head), head_scale(*head), span(x, (size_t)rows * xw * 2),
                        dense ? head_weight(*dense) : Span{0, 0},
                        down ? head_weight(*down) : Span{0, 0},
-                       down ? head_scale(*down) : Span{0, 0}};
-    for (const Span &s : in)
-        if (overlap(sl, s) || overlap(sw, s))
-            return DH_ERR_INVALID;
-    if (logits && overlap(sl, span(workspace, need)))
-        return DH_ERR_INVALID;
-    DH_TRY(check_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft, workspace,
-                      tw.bytes));
-    if (dense) {
-        DH_TRY(check_rescore(dense, x, rows, ids, k, exact, draft));
-        // the rescore reads the stage-1 values while it writes `exact` and then `draft`
-        const Span sv = span(vals, (size_t)rows * k * 4);
-        if (overlap(sv, span(exact, (size_t)rows * k * 4)) ||
-            overlap(sv, span(draft, (size_t)rows * 4)))
-            return DH_ERR_INVALID;
-    }
-    for (const Span &s : in) {
-        if (overlap(span(ids, (size_t)rows * k * 4), s) ||
-            overlap(span(vals, (size_t)rows * k * 4), s) || overlap(span(draft, (size_t)rows * 4), s))
-            return DH_ERR_INVALID;
-    }
-    if (idmap)
-        DH_TRY(check_idmap(idmap, head->vocab,
-                           {sl, sw, span(ids, (size_t)rows * k * 4),
-                            span(vals, (size_t)rows * k * 4), span(draft, (size_t)rows * 4),
-                            span(exact, exact ? (size_t)rows * k * 4 : 0)}));
-    if (down) {
-        // t is written by the first GEMV and read by the second: clear of everything else
-        const Span stt = span(t, (size_t)rows * (size_t)head->hidden * 2);
+                       down ? head_scale(*down) : Span{0, 0},
+                       span(idmap, idmap ? (size_t)head->vocab * 4 : 0)};
+    const Span outs[] = {span(L, lbytes), span(workspace, tw.bytes), span(ids, rk),
+                         span(vals, rk), span(draft, (size_t)rows * 4),
+                         span(exact, exact ? rk : 0),
+                         span(t, down ? (size_t)rows * (size_t)head->hidden * 2 : 0)};
+    constexpr int nouts = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < nouts; i++) {
         for (const Span &s : in)
-            if (overlap(stt, s))
+            if (overlap(outs[i], s))
                 return DH_ERR_INVALID;
-        const Span outs[] = {sl, sw, span(ids, (size_t)rows * k * 4),
-                             span(vals, (size_t)rows * k * 4), span(draft, (size_t)rows * 4),
-                             span(exact, exact ? (size_t)rows * k * 4 : 0)};
-        for (const Span &s : outs)
-            if (overlap(stt, s))
+        for (int j = i + 1; j < nouts; j++)
+            if (overlap(outs[i], outs[j]))
                 return DH_ERR_INVALID;
     }
+    if (idmap && !aligned(idmap, 4))
+        return DH_ERR_INVALID;
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (down)   // nothing else is live in the checked workspace yet: it may hold partials

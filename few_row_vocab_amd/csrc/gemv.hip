@@ -42,7 +42,8 @@ constexpr int kMaxWaves = 16;
 // 17..32 activation rows: two 16-row MFMA column blocks.  Their activations double the VGPRs a
 // wave holds, so such launches run half the waves (256 VGPRs each), each wave doing the work
 // of two waves of the 16-row launch with separate sums (so a row's sums are the same bits
-// as in a 16-row call), for H <= 4096; wider heads take two 16-row launches.
+// as in a 16-row call), for H <= 5120 (4096 for a row-major bf16 head, whose tile spills
+// at 5120); wider heads take two 16-row launches.
 constexpr int kMaxWaves2 = kMaxWaves / 2;
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 // Row-major heads: plain loads.  A wave's load covers 16 rows x 64 bytes there, and with the

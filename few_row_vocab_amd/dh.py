@@ -5,6 +5,7 @@ buffers and the current stream.  There is no fallback: if libdh.so is missing or
 refused, this module raises.
 """
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -88,6 +89,20 @@ def lib():
             f.restype = i32
         _lib = L
     return _lib
+
+
+def _on_stream(fn):
+    """Run a binding call with `stream` (when given) as torch's current stream, so that the
+    outputs and any temporary workspace it allocates belong to the stream the library
+    launches on: the caching allocator then cannot hand a freed temporary to other work
+    while the kernels on that stream still use it."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
 
 
 def _check(status):
@@ -207,6 +222,7 @@ def tiled_bytes(format, vocab, hidden):
     return int(lib().dh_tiled_bytes(format, vocab, hidden))
 
 
+@_on_stream
 def tile(head: Head, stream=None):
     """The tiled copy of a row-major head (dh_tile_head): same format | TILED, same scale;
     the GEMV forms give bitwise the same results from it and stream it faster."""
@@ -232,6 +248,7 @@ def workspace(rows, vocab, k, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def gemv(head: Head, x, logits=None, stream=None):
     """logits [R][V] fp32 = x [R][H] (bf16) times the head."""
     R = x.shape[0]
@@ -244,6 +261,7 @@ def gemv(head: Head, x, logits=None, stream=None):
     return logits
 
 
+@_on_stream
 def linear(w: Head, x, mode=OUT_F32, residual=None, out=None, stream=None):
     """out [R][N] = x [R][K] (bf16) times the linear w [N][K]: float32 (OUT_F32), bf16
     (OUT_BF16) or bf16 of residual + the sum (OUT_ADD_BF16; out may be residual)."""
@@ -260,6 +278,7 @@ def linear(w: Head, x, mode=OUT_F32, residual=None, out=None, stream=None):
     return out
 
 
+@_on_stream
 def _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream):
     _want(logits, torch.float32, "logits")
     R, V = logits.shape
@@ -288,15 +307,16 @@ def _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream):
 def topk(logits, k, ws=None, ids=None, vals=None, argmax=None, with_argmax=True,
          stream=None):
     """(ids int32 [R][k], vals fp32 [R][k], argmax int32 [R] or None)."""
-    return _topk_call(logits, k, None, ws, ids, vals, argmax, with_argmax, stream)
+    return _topk_call(logits, k, None, ws, ids, vals, argmax, with_argmax, stream=stream)
 
 
 def topk_mapped(logits, k, idmap, ws=None, ids=None, vals=None, argmax=None,
                 with_argmax=True, stream=None):
     """topk over a subset head's logits; ids and argmax are vocabulary ids idmap[j]."""
-    return _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream)
+    return _topk_call(logits, k, idmap, ws, ids, vals, argmax, with_argmax, stream=stream)
 
 
+@_on_stream
 def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
     """(ids, vals, argmax, probs fp32 [R][k], lse fp32 [R]): dh_topk plus each row's softmax
     statistics (probs[:, 0] is the top-1's confidence)."""
@@ -315,6 +335,7 @@ def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
     return ids, vals, argmax, probs, lse
 
 
+@_on_stream
 def sample(ids, vals, positions, temperature=1.0, top_p=1.0, min_p=0.0, seed=0,
            with_kept=True, token=None, kept=None, stream=None):
     """dh_sample: (token int32 [R], kept int32 [R] or None) keyed by seed, positions (int64
@@ -335,6 +356,7 @@ def sample(ids, vals, positions, temperature=1.0, top_p=1.0, min_p=0.0, seed=0,
     return token, kept
 
 
+@_on_stream
 def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):
     """The subset head of `head` (BF16 or FP8_ROW) whose row j is row ids[j] (int32);
     written into `out` when given."""
@@ -360,6 +382,7 @@ def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):
     return Head(head.format, weight, scale)
 
 
+@_on_stream
 def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
     """(exact fp32 [R][cand_k], draft int32 [R])."""
     _want(cand_ids, torch.int32, "cand_ids")
@@ -384,6 +407,7 @@ def _check_outs(o, R, k, vocab):
     _shaped(o.get("logits"), (R, vocab), torch.float32, "logits")
 
 
+@_on_stream
 def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=False,
           out=None, stream=None, idmap=None):
     """The whole projection: dict with ids, vals, draft (+ exact, logits).  With `idmap`
@@ -417,6 +441,7 @@ def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=F
     return o
 
 
+@_on_stream
 def draft_lowrank(down: Head, up: Head, x, k, dense: Optional[Head] = None, ws=None,
                   keep_logits=False, out=None, stream=None):
     """dh_draft_lowrank: t = bf16(x down^T), logits = t up^T, then the draft (dict with ids,
@@ -450,6 +475,7 @@ def draft_mapped(head: Head, idmap, x, k, dense: Optional[Head] = None, **kw):
     return draft(head, x, k, dense=dense, idmap=idmap, **kw)
 
 
+@_on_stream
 def quantize(w, format, stream=None):
     """FP8 head from a bf16 head [V][H]: (codes uint8 [V][H], scale); with format | TILED the
     codes come straight in the tiled layout (a flat uint8 buffer, as tile() makes)."""
@@ -478,6 +504,7 @@ def quantize(w, format, stream=None):
 STREAM_SINK_WORDS = 8192
 
 
+@_on_stream
 def stream_read(buf, sink=None, stream=None):
     """dh_stream_read: a diagnostic read of a device buffer (uint8, size a multiple of 4096)
     the way the GEMV streams a tiled head; returns the sink (int32 [STREAM_SINK_WORDS]) whose

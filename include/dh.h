@@ -173,7 +173,13 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                      void *stream);
 
 /* dh_draft -- the whole projection in one call: dh_gemv, then dh_topk (k), then -- when
- * `dense` is not NULL -- the two-stage rescore of the top k candidates.  In the two-stage
+ * `dense` is not NULL -- the two-stage rescore of the top k candidates.  [TFE] two_stage
+ * commit note: a draft pass's vocabulary head gives each row its draft, either the argmax
+ * of its logits (the top-1 kernel) or, for a two_stage head, the argmax of the exact
+ * logits of its top cand_k candidates from the dense bf16 copy of the target's head,
+ * taken through the candidates' id map; 'What this changes': the head runs on one rank
+ * and its drafts need no collective; 'Update (8d8691c..ce9a427)': the two_stage head with
+ * cand_k up to 512 and a tie at the k-th value to the lower token id.  In the two-stage
  * form the pad slots of a row with fewer than k eligible logits are not candidates: their
  * exact logit is -inf and they are never drafted.
  * head: the stage-1 head (any format).  dense: NULL (one stage) or a DH_BF16 head of the

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for s in range(5):
-        assert dh.status_string(s)
+        assert dh.status_string(s) and dh.status_string(s) != "unknown status"
     assert dh.status_string(99) == "unknown status"
 
 
@@ -151,12 +151,22 @@ def test_rescore_and_draft_refusals(no_device):
     assert L.dh_rescore(ctypes.byref(dense), x.p, R, ids.p, 513, ex.p, dr.p, None) == 2
     assert L.dh_rescore(ctypes.byref(dense), x.p, R, ids.p, k, ids.p, dr.p, None) == 1
 
-    def draft(h=stage1, d=dense, rows=R, kk=k, exact=ex, wsb=None):
+    lg = HostBuf(R * V * 4)
+
+    def draft(h=stage1, d=dense, rows=R, kk=k, exact=ex, wsb=None, logits=None, drf=dr):
         return L.dh_draft(ctypes.byref(h), ctypes.byref(d) if d else None, x.p, rows, kk,
-                          ids.p, vals.p, dr.p, exact.p if exact else None, None, ws.p,
+                          ids.p, vals.p, drf.p, exact.p if exact else None,
+                          logits.p if logits else None, ws.p,
                           ws.a.size if wsb is None else wsb, None)
 
     assert draft(exact=vals) == 1                       # exact overlaps the stage-1 values
+    assert draft(exact=w) == 1                          # exact overlaps the stage-1 weight
+    assert draft(exact=s) == 1                          # exact overlaps the stage-1 scale
+    assert draft(exact=lg, logits=lg) == 1              # exact overlaps the logits
+    assert draft(drf=lg, logits=lg) == 1                # draft overlaps the logits
+    assert draft(exact=ws) == 1                         # exact inside the workspace
+    assert draft(drf=ws) == 1                           # draft inside the workspace
+    assert draft(d=None, exact=None, drf=w) == 1        # one-stage draft over the weight
     assert draft(exact=None) == 1                       # two-stage needs `exact`
     assert draft(d=None) == 1                           # one-stage must not pass `exact`
     assert draft(d=head(dh.BF16, V - 1, H, wd)) == 1   # dense head of another size
@@ -164,7 +174,7 @@ def test_rescore_and_draft_refusals(no_device):
     assert draft(kk=513) == 2
     assert draft(wsb=100) == 3
     assert draft(rows=33) == 2
-    for b in (ids, vals, ex, dr):
+    for b in (ids, vals, ex, dr, lg):
         assert b.untouched()
 
 
@@ -367,3 +377,4 @@ def test_stream_read_refusals(no_device):
     assert L.dh_stream_read(ctypes.c_void_p(buf.a.ctypes.data + 4), 4096, sink.p, None) == 1
     assert L.dh_stream_read(buf.p, 8192, ctypes.c_void_p(buf.a.ctypes.data + 4096), None) == 1
     assert sink.untouched() and buf.untouched()
+

@@ -44,3 +44,42 @@ def test_binding_shape_checks():
     with pytest.raises(ValueError):
         dh.gemv(dh.Head(dh.FP8_ROW, codes, scale[:-1]), x)        # row scales one short
     torch.cuda.synchronize()
+
+
+def test_draft_on_a_side_stream_with_a_temporary_workspace(monkeypatch):
+    """dh.draft(stream=s) with ws=None allocates its temporary workspace (which holds the
+    logits when they are not kept) on s, so memory the current stream allocates right after
+    the call cannot be that workspace while s still runs the draft."""
+    need_gpu()
+    V, H, R, k = 60000, 1024, 4, 64
+    head = dh.Head(dh.BF16, dev_u16(synth.random_head(V, H, seed=11, std=0.02)))
+    x = dev_u16(synth.random_acts(R, H, seed=12))
+    want = dh.draft(head, x, k)
+    torch.cuda.synchronize()
+    made = []
+    orig = dh.workspace
+
+    def spy(*a, **kw):
+        ws = orig(*a, **kw)
+        made.append((ws.data_ptr(), ws.numel()))
+        return ws
+
+    monkeypatch.setattr(dh, "workspace", spy)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        a = torch.ones((2048, 2048), device="cuda")
+        for _ in range(6):                                     # keeps the side stream busy
+            a = (a @ a) / 2048.0
+    got = dh.draft(head, x, k, stream=side)
+    assert len(made) == 1
+    # the current stream now allocates and writes as much memory as the workspace held
+    junk = [torch.full((made[0][1],), 0xFF, dtype=torch.uint8, device="cuda")
+            for _ in range(3)]
+    for j in junk:
+        lo, hi = j.data_ptr(), j.data_ptr() + j.numel()
+        assert hi <= made[0][0] or lo >= made[0][0] + made[0][1]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for name in ("ids", "vals", "draft"):
+        assert torch.equal(got[name], want[name]), name

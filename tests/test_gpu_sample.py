@@ -67,14 +67,16 @@ def test_sample_many_seeds_law():
     pos = dev(np.arange(R, dtype=np.int64))
     picks = []
     for s in range(100):
-        tok, _ = dh.sample(idd, vd, pos, temperature=0.8, top_p=0.9, seed=s)
-        picks.append(host(tok))
+        tok, kept = dh.sample(idd, vd, pos, temperature=0.8, top_p=0.9, seed=s)
+        picks.append((host(tok), host(kept)))
     torch.cuda.synchronize()
-    picks = np.concatenate(picks)
-    ot = np.concatenate([oracle.sample(np.repeat(ids, R, 0), np.repeat(vals, R, 0), 0.8, 0.9,
-                                       0.0, s, np.arange(R))[0] for s in range(100)])
-    assert np.mean(picks == ot) > 0.999
-    say(f"pick frequencies: {[int(np.sum(picks == i)) for i in ids[0]]}")
+    # every pick equals the oracle's except where the oracle's best two Gumbel scores are
+    # within 1e-9 (the same near-tie rule as test_sample_vs_oracle)
+    ri, rv, rp = np.repeat(ids, R, 0), np.repeat(vals, R, 0), np.arange(R, dtype=np.int64)
+    for s, (tok, kept) in enumerate(picks):
+        check_picks(ri, rv, 0.8, 0.9, 0.0, s, rp, tok, kept)
+    allp = np.concatenate([t for t, _ in picks])
+    say(f"pick frequencies: {[int(np.sum(allp == i)) for i in ids[0]]}")
 
 
 def test_sample_refusals():

@@ -4,6 +4,7 @@
 // (TF_DS_DRAFTER=eagle), off by default", commit notes on absorb and the review thread).
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <stdint.h>
 
 #include "dh_internal.h"
@@ -144,6 +145,37 @@ dh_status device_status(hipError_t e) { return e == hipSuccess ? DH_OK : DH_ERR_
 
 }  // namespace
 
+namespace {
+
+// The fixed scratch of dh_draft_noalloc: one array per GPU, made when the library's code is
+// loaded on that GPU and held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: host code only ever uses the device address that
+// hipGetSymbolAddress gives for the current device (scratch_address).
+__device__ __align__(256) unsigned char scratch[DH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::mutex scratch_mu;
+void *scratch_at[kScratchDevices];   // device address of `scratch` per device, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call on that device, with
+// that device current), or NULL if the runtime cannot give it.
+void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> g(scratch_mu);
+    if (!scratch_at[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        scratch_at[dev] = p;
+    }
+    return scratch_at[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *logits,
@@ -192,9 +224,12 @@ size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k)
     return w.bytes + ((logits + 255) & ~(size_t)255);
 }
 
+// own_scratch: the workspace is the library's fixed scratch (dh_draft_noalloc), which no
+// caller buffer can overlap; `workspace` is then NULL, and so is `logits` when the logits
+// are to live in that scratch.
 static dh_status check_topk(const float *logits, int32_t rows, int64_t vocab, int32_t k,
                             int32_t *ids, float *vals, int32_t *argmax, void *workspace,
-                            size_t workspace_bytes)
+                            size_t workspace_bytes, bool own_scratch = false)
 {
     DH_TRY(check_rows(rows));
     if (vocab < 1)
@@ -202,16 +237,16 @@ static dh_status check_topk(const float *logits, int32_t rows, int64_t vocab, in
     if (vocab > DH_MAX_VOCAB)
         return DH_ERR_UNSUPPORTED;
     DH_TRY(check_k(k, vocab));
-    if (!logits || !ids || !vals || !aligned(logits, 4) || !aligned(ids, 4) ||
-        !aligned(vals, 4) || (argmax && !aligned(argmax, 4)))
+    if ((!logits && !own_scratch) || !ids || !vals || !aligned(logits, 4) ||
+        !aligned(ids, 4) || !aligned(vals, 4) || (argmax && !aligned(argmax, 4)))
         return DH_ERR_INVALID;
-    if (!workspace || !aligned(workspace, 256) ||
-        workspace_bytes < dh::topk_ws_layout(rows, vocab, k).bytes)
+    if (!own_scratch && (!workspace || !aligned(workspace, 256) ||
+                         workspace_bytes < dh::topk_ws_layout(rows, vocab, k).bytes))
         return DH_ERR_WORKSPACE;
-    const Span in = span(logits, (size_t)rows * (size_t)vocab * sizeof(float));
+    const Span in = span(logits, logits ? (size_t)rows * (size_t)vocab * sizeof(float) : 0);
     const Span si = span(ids, (size_t)rows * k * 4), sv = span(vals, (size_t)rows * k * 4);
     const Span sa = span(argmax, argmax ? (size_t)rows * 4 : 0);
-    const Span sw = span(workspace, dh::topk_ws_layout(rows, vocab, k).bytes);
+    const Span sw = span(workspace, own_scratch ? 0 : dh::topk_ws_layout(rows, vocab, k).bytes);
     if (overlap(in, si) || overlap(in, sv) || overlap(in, sa) || overlap(si, sv) ||
         overlap(si, sa) || overlap(sv, sa) || overlap(sw, in) || overlap(sw, si) ||
         overlap(sw, sv) || overlap(sw, sa))
@@ -336,14 +371,16 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                                             draft, (hipStream_t)stream));
 }
 
-// dh_draft, dh_draft_mapped and dh_draft_lowrank: with an id map the head is a subset head
-// whose entry j is vocabulary id idmap[j], and the dense head spans the whole vocabulary;
-// with `down` the stage-1 head is low rank: t = bf16(x down^T), and `head` projects t.
+// dh_draft, dh_draft_mapped, dh_draft_lowrank and dh_draft_noalloc: with an id map the head
+// is a subset head whose entry j is vocabulary id idmap[j], and the dense head spans the
+// whole vocabulary; with `down` the stage-1 head is low rank: t = bf16(x down^T), and
+// `head` projects t.  own_scratch (workspace NULL): the workspace is the library's fixed
+// scratch, whose device address is looked up only once every argument has passed.
 static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t,
                            const int32_t *idmap, const dh_head *dense, const uint16_t *x,
                            int32_t rows, int32_t k, int32_t *ids, float *vals, int32_t *draft,
                            float *exact, float *logits, void *workspace,
-                           size_t workspace_bytes, void *stream)
+                           size_t workspace_bytes, void *stream, bool own_scratch = false)
 {
     DH_TRY(check_head(head));
     DH_TRY(check_gemv_rows(rows, head->hidden));
@@ -370,11 +407,17 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     const TopkWs tw = dh::topk_ws_layout(rows, head->vocab, k);
     const size_t lbytes = (size_t)rows * (size_t)head->vocab * sizeof(float);
     const size_t need = tw.bytes + (logits ? 0 : ((lbytes + 255) & ~(size_t)255));
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    if (own_scratch) {
+        if (need > DH_NOALLOC_SCRATCH_BYTES)
+            return DH_ERR_SCRATCH;
+    } else if (!workspace || !aligned(workspace, 256) || workspace_bytes < need) {
         return DH_ERR_WORKSPACE;
-    float *L = logits ? logits : reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
+    }
+    float *L = logits || own_scratch
+                   ? logits
+                   : reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
     DH_TRY(check_topk(L, rows, head->vocab, k, ids, vals, dense ? nullptr : draft, workspace,
-                      tw.bytes));
+                      tw.bytes, own_scratch));
     if (dense)
         DH_TRY(check_rescore(dense, x, rows, ids, k, exact, draft));
     // Every buffer the call writes -- the logits, the workspace's top-k part, ids, vals,
@@ -386,7 +429,8 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
                        down ? head_weight(*down) : Span{0, 0},
                        down ? head_scale(*down) : Span{0, 0},
                        span(idmap, idmap ? (size_t)head->vocab * 4 : 0)};
-    const Span outs[] = {span(L, lbytes), span(workspace, tw.bytes), span(ids, rk),
+    const Span outs[] = {span(L, L ? lbytes : 0), span(workspace, own_scratch ? 0 : tw.bytes),
+                         span(ids, rk),
                          span(vals, rk), span(draft, (size_t)rows * 4),
                          span(exact, exact ? rk : 0),
                          span(t, down ? (size_t)rows * (size_t)head->hidden * 2 : 0)};
@@ -401,6 +445,13 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     }
     if (idmap && !aligned(idmap, 4))
         return DH_ERR_INVALID;
+    if (own_scratch) {
+        workspace = scratch_address();
+        if (!workspace)
+            return DH_ERR_DEVICE;
+        if (!logits)
+            L = reinterpret_cast<float *>(static_cast<char *>(workspace) + tw.bytes);
+    }
     const hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipSuccess;
     if (down)   // nothing else is live in the checked workspace yet: it may hold partials
@@ -421,6 +472,14 @@ dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x,
 {
     return run_draft(head, nullptr, nullptr, nullptr, dense, x, rows, k, ids, vals, draft,
                      exact, logits, workspace, workspace_bytes, stream);
+}
+
+dh_status dh_draft_noalloc(const dh_head *head, const dh_head *dense, const uint16_t *x,
+                           int32_t rows, int32_t k, int32_t *ids, float *vals, int32_t *draft,
+                           float *exact, float *logits, void *stream)
+{
+    return run_draft(head, nullptr, nullptr, nullptr, dense, x, rows, k, ids, vals, draft,
+                     exact, logits, nullptr, DH_NOALLOC_SCRATCH_BYTES, stream, true);
 }
 
 dh_status dh_draft_mapped(const dh_head *head, const int32_t *idmap, const dh_head *dense,
@@ -534,6 +593,8 @@ const char *dh_status_string(int32_t status)
     case DH_ERR_WORKSPACE: return "workspace missing, misaligned or too small "
                                   "(see dh_workspace_bytes)";
     case DH_ERR_DEVICE: return "the HIP runtime reported an error at launch";
+    case DH_ERR_SCRATCH: return "the call needs more than the fixed scratch of "
+                                "dh_draft_noalloc (DH_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

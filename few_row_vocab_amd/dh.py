@@ -32,7 +32,8 @@ MAX_HIDDEN = 8192
 MAX_VOCAB = 262144
 
 STATUS = {0: "DH_OK", 1: "DH_ERR_INVALID", 2: "DH_ERR_UNSUPPORTED", 3: "DH_ERR_WORKSPACE",
-          4: "DH_ERR_DEVICE"}
+          4: "DH_ERR_DEVICE", 5: "DH_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 16 << 20   # the fixed scratch of dh_draft_noalloc
 
 
 class DHError(RuntimeError):
@@ -64,6 +65,7 @@ def lib():
         L.dh_topk.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, sz, vp]
         L.dh_rescore.argtypes = [hp, vp, i32, vp, i32, vp, vp, vp]
         L.dh_draft.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dh_draft_noalloc.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
         L.dh_gather_rows.argtypes = [hp, vp, i64, vp, vp, vp]
         L.dh_linear.argtypes = [hp, vp, i32, i32, vp, vp, vp]
@@ -82,7 +84,8 @@ def lib():
         L.dh_workspace_bytes.restype = sz
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
-        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_quantize,
+        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_draft_noalloc,
+                  L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
                   L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample, L.dh_tile_head,
                   L.dh_stream_read):
@@ -438,6 +441,34 @@ def draft(head: Head, x, k, dense: Optional[Head] = None, ws=None, keep_logits=F
         if idmap.numel() != head.vocab:
             raise ValueError(f"idmap: expected {head.vocab} ids, got {idmap.numel()}")
         _check(lib().dh_draft_mapped(ctypes.byref(h), _ptr(idmap), dref, *tail))
+    return o
+
+
+@_on_stream
+def draft_noalloc(head: Head, x, k, dense: Optional[Head] = None, keep_logits=False, out=None,
+                  stream=None):
+    """dh_draft_noalloc: dh_draft on the library's fixed device scratch (no workspace).  The
+    library call allocates nothing; pass every output in `out` (ids, vals, draft, and exact
+    with `dense`, logits with keep_logits) to make the whole call allocation-free, since
+    missing outputs are allocated here.  Calls that overlap on one GPU race."""
+    R = x.shape[0]
+    dev = x.device
+    o = {} if out is None else out
+    o.setdefault("ids", torch.empty((R, k), dtype=torch.int32, device=dev))
+    o.setdefault("vals", torch.empty((R, k), dtype=torch.float32, device=dev))
+    o.setdefault("draft", torch.empty((R,), dtype=torch.int32, device=dev))
+    if dense is not None:
+        o.setdefault("exact", torch.empty((R, k), dtype=torch.float32, device=dev))
+    if keep_logits:
+        o.setdefault("logits", torch.empty((R, head.vocab), dtype=torch.float32, device=dev))
+    _shaped(x, (R, head.hidden), BF16_BITS, "x")
+    _check_outs(o, R, k, head.vocab)
+    h = head._c()
+    d = dense._c() if dense is not None else None
+    _check(lib().dh_draft_noalloc(ctypes.byref(h), ctypes.byref(d) if d is not None else None,
+                                  _ptr(x), R, k, _ptr(o["ids"]), _ptr(o["vals"]),
+                                  _ptr(o["draft"]), _ptr(o.get("exact")), _ptr(o.get("logits")),
+                                  _stream(stream)))
     return o
 
 

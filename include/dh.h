@@ -43,7 +43,8 @@ typedef enum {
                                outputs overlapping inputs */
     DH_ERR_UNSUPPORTED = 2, /* a size outside what the kernels implement (see limits) */
     DH_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-    DH_ERR_DEVICE = 4       /* the HIP runtime reported an error at launch */
+    DH_ERR_DEVICE = 4,      /* the HIP runtime reported an error at launch */
+    DH_ERR_SCRATCH = 5      /* dh_draft_noalloc: the sizes need more than its fixed scratch */
 } dh_status;
 
 /* Storage formats of a vocabulary head [V][H].
@@ -190,6 +191,23 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
 dh_status dh_draft(const dh_head *head, const dh_head *dense, const uint16_t *x, int32_t rows,
                    int32_t k, int32_t *ids, float *vals, int32_t *draft, float *exact,
                    float *logits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* dh_draft_noalloc -- dh_draft without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  The call allocates nothing; its scratch (the top-k's
+ * chunk lists, and the logits when `logits` is NULL) is a fixed array of
+ * DH_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU, held from the first
+ * use of the library on that GPU until the process ends.  Sizes that need more than that
+ * (dh_workspace_bytes(rows, V, k), less rows * V * 4 rounded up to 256 when `logits` is
+ * given) are refused with DH_ERR_SCRATCH; 16 MiB covers every size with `logits` given, and
+ * without it e.g. 16 rows of 129,280 logits at any k.  All calls on one GPU share that GPU's
+ * array and leave their contents in it, so calls that may overlap on one GPU (other
+ * streams, other host threads) race and give undefined results: serialize them.  Every other
+ * argument, result and refusal is dh_draft's. */
+#define DH_NOALLOC_SCRATCH_BYTES (16u << 20)
+dh_status dh_draft_noalloc(const dh_head *head, const dh_head *dense, const uint16_t *x,
+                           int32_t rows, int32_t k, int32_t *ids, float *vals, int32_t *draft,
+                           float *exact, float *logits, void *stream);
 
 /* dh_quantize -- make an FP8 head from a bf16 head (load-time preparation).
  *  DH_FP8_ROW ([TFE] 'Update' on FP8 linears): s[v] = float(max_h |w[v][h]| / 448) and

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert dh.status_string(s) and dh.status_string(s) != "unknown status"
     assert dh.status_string(99) == "unknown status"
 
@@ -378,3 +378,28 @@ def test_stream_read_refusals(no_device):
     assert L.dh_stream_read(buf.p, 8192, ctypes.c_void_p(buf.a.ctypes.data + 4096), None) == 1
     assert sink.untouched() and buf.untouched()
 
+
+def test_draft_noalloc_refusals(no_device):
+    """dh_draft_noalloc refuses, before any launch, what dh_draft refuses and sizes beyond its
+    fixed scratch (DH_ERR_SCRATCH, 5)."""
+    L = dh.lib()
+    R, V, H, k = 2, 600, 64, 16
+    w, s = HostBuf(V * H), HostBuf(((V + 31) // 32) * (H // 32))
+    x, ids, vals, dr = HostBuf(R * H * 2), HostBuf(R * k * 4), HostBuf(R * k * 4), HostBuf(R * 4)
+    hd = head(dh.FP8_BLOCK32, V, H, w, s)
+
+    def call(h=hd, rows=R, kk=k, drf=dr, logits=None):
+        return L.dh_draft_noalloc(ctypes.byref(h), None, x.p, rows, kk, ids.p, vals.p, drf.p,
+                                  None, logits.p if logits else None, None)
+
+    assert call(rows=0) == 1
+    assert call(rows=33) == 2
+    assert call(kk=513) == 2
+    assert call(drf=vals) == 1                                 # draft overlaps vals
+    assert call(drf=w) == 1                                    # draft over the weight
+    # 32 rows of 200,000 logits (25.6 MB) do not fit the 16 MiB scratch without `logits`
+    big = head(dh.FP8_BLOCK32, 200000, H, w, s)
+    assert call(h=big, rows=32) == 5
+    assert dh.workspace_bytes(32, 200000, k) > dh.NOALLOC_SCRATCH_BYTES
+    for b in (ids, vals, dr):
+        assert b.untouched()

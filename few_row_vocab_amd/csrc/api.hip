@@ -456,11 +456,14 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     hipError_t e = hipSuccess;
     if (down)   // nothing else is live in the checked workspace yet: it may hold partials
         e = dh::launch_linear(*down, x, rows, DH_OUT_BF16, nullptr, t, st, workspace, need);
+    // the GEMV zeroes the top-k's tickets, so the top-k is one launch
     if (e == hipSuccess)
-        e = dh::launch_gemv(*head, down ? t : x, rows, L, st);
+        e = dh::launch_gemv(*head, down ? t : x, rows, L, st,
+                            dh::topk_tickets(workspace, rows, head->vocab, k), rows,
+                            dh::kTicketStride);
     if (e == hipSuccess)
         e = dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals, dense ? nullptr : draft,
-                            workspace, st);
+                            workspace, st, nullptr, nullptr, true);
     if (e == hipSuccess && dense)
         e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st);
     return device_status(e);

@@ -17,14 +17,18 @@ constexpr int kWave = 64;
 
 // Launchers: argument checking has been done by the caller (api.hip).  Each returns the
 // hipError_t of its launches.
+// zero, nzero, zstride: up to 64 words, zstride words apart, that the kernel sets to zero
+// (the tickets of the top-k that follows it on the stream), or NULL.
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
-                       hipStream_t stream);
+                       hipStream_t stream, uint32_t *zero = nullptr, int nzero = 0,
+                       int zstride = 1);
 // The same GEMV with an output mode (dh_out_mode): fp32, bf16, or bf16 of residual + sum.
 // scratch: optional device memory; with a few tiles and linear_split_bytes of it, the work
 // is split over more workgroups with bit-identical results.
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
                          const uint16_t *residual, void *out, hipStream_t stream,
-                         void *scratch = nullptr, size_t scratch_bytes = 0);
+                         void *scratch = nullptr, size_t scratch_bytes = 0,
+                         uint32_t *zero = nullptr, int nzero = 0, int zstride = 1);
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
 
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,

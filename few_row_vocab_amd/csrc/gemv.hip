@@ -77,6 +77,8 @@ struct GemvArgs {
     int ntiles;
     int nkb;                // number of 64-column blocks, ceil(H / 64)
     int tile_bytes;         // tiled layout: bytes of one 16-row tile, nkb * 1024 * (bytes/weight)
+    uint32_t *zero;         // nzero (<= 64) words, zstride apart, the first workgroup zeroes
+    int nzero, zstride;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -166,6 +168,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     const int nvw = (a.nkb + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
+    if (blockIdx.x == 0 && (int)threadIdx.x < a.nzero)
+        a.zero[threadIdx.x * a.zstride] = 0u;  // for the kernel that follows on the stream
     const int rr = lane & 15;
     const int g = lane >> 4;
     const int H = a.H;
@@ -593,9 +597,10 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
-                       hipStream_t stream)
+                       hipStream_t stream, uint32_t *zero, int nzero, int zstride)
 {
-    return launch_linear(head, x, rows, DH_OUT_F32, nullptr, logits, stream);
+    return launch_linear(head, x, rows, DH_OUT_F32, nullptr, logits, stream, nullptr, 0, zero,
+                         nzero, zstride);
 }
 
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows)
@@ -625,7 +630,8 @@ hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
 
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
                          const uint16_t *residual, void *out, hipStream_t stream,
-                         void *scratch, size_t scratch_bytes)
+                         void *scratch, size_t scratch_bytes, uint32_t *zero, int nzero,
+                         int zstride)
 {
     const int fmt = head.format & ~DH_TILED;
     GemvArgs a;
@@ -643,6 +649,9 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
     a.ntiles = 0;   // set per tile height by run()
     a.nkb = (int)((head.hidden + 63) / 64);
     a.tile_bytes = a.nkb * 1024 * (fmt == DH_BF16 ? 2 : 1);
+    a.zero = zero;
+    a.nzero = zero ? nzero : 0;
+    a.zstride = zstride;
     // few tiles and room for the partials: split by virtual wave (the same bits)
     const int64_t ntiles = (a.V + 15) / 16;
     if (scratch && ntiles <= device_cus() / 2 && (a.nkb + kMaxWaves - 1) / kMaxWaves <= kSplitMaxKbw &&

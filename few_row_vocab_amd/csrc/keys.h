@@ -14,7 +14,7 @@
 
 namespace dh {
 
-__device__ inline uint32_t order_key(float f)
+__device__ __forceinline__ uint32_t order_key(float f)
 {
     uint32_t u = __float_as_uint(f);
     if (f != f || u == 0xff800000u)
@@ -24,16 +24,16 @@ __device__ inline uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ inline uint64_t entry_key(uint32_t image, uint32_t id)
+__device__ __forceinline__ uint64_t entry_key(uint32_t image, uint32_t id)
 {
     return ((uint64_t)image << 32) | (uint64_t)(0xffffffffu - id);
 }
 
-__device__ inline uint32_t key_id(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
+__device__ __forceinline__ uint32_t key_id(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
 
 // The logit of a key, from its image; a zero's sign is not in the image, so zeros are read
 // back from the logits (`src`).
-__device__ inline float image_value(uint64_t key, const float *src)
+__device__ __forceinline__ float image_value(uint64_t key, const float *src)
 {
     const uint32_t im = (uint32_t)(key >> 32);
     if (im == 0x80000000u)
@@ -43,7 +43,7 @@ __device__ inline float image_value(uint64_t key, const float *src)
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16 lanes, then
 // the row totals broadcast to the later rows (gfx9 DPP row_shr / row_bcast).
-__device__ inline uint32_t wave_scan(uint32_t v)
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v)
 {
     v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);   // row_shr:1
     v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);   // row_shr:2
@@ -57,7 +57,7 @@ __device__ inline uint32_t wave_scan(uint32_t v)
 // Reserves `mine` consecutive slots per lane from an LDS counter with one atomic per wave
 // (a lane's slots follow those of the lanes below it); returns the lane's first slot.  All
 // 64 lanes must take part.
-__device__ inline uint32_t wave_reserve(uint32_t mine, uint32_t *fill)
+__device__ __forceinline__ uint32_t wave_reserve(uint32_t mine, uint32_t *fill)
 {
     const uint32_t incl = wave_scan(mine);
     const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
@@ -73,7 +73,7 @@ __device__ inline uint32_t wave_reserve(uint32_t mine, uint32_t *fill)
 // The smallest and largest of the non-zero 64-bit keys over the 64 lanes of a wave (the same
 // DPP pattern as wave_scan; masked lanes keep the identity).  An all-zero wave gives
 // (~0, 0).
-__device__ inline void wave_min_max(uint64_t &mn, uint64_t &mx)
+__device__ __forceinline__ void wave_min_max(uint64_t &mn, uint64_t &mx)
 {
 #define DH_MINMAX_STEP(ctrl, rmask)                                                            \
     {                                                                                          \
@@ -103,12 +103,41 @@ __device__ inline void wave_min_max(uint64_t &mn, uint64_t &mx)
          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mx, 63);
 }
 
+// The smallest non-zero and the largest of 32-bit images over the 64 lanes of a wave (DPP,
+// as wave_scan; masked lanes keep the identity), returned in every lane.  An all-zero wave
+// gives (~0, 0).
+__device__ __forceinline__ void wave_min_max32(uint32_t &mn, uint32_t &mx)
+{
+#define DH_MINMAX32_STEP(ctrl, rmask)                                                          \
+    {                                                                                          \
+        const uint32_t a = __builtin_amdgcn_update_dpp(0xffffffffu, mn, ctrl, rmask, 0xf, false); \
+        const uint32_t b = __builtin_amdgcn_update_dpp(0u, mx, ctrl, rmask, 0xf, false);       \
+        mn = a < mn ? a : mn;                                                                  \
+        mx = b > mx ? b : mx;                                                                  \
+    }
+    DH_MINMAX32_STEP(0x111, 0xf)   // row_shr:1
+    DH_MINMAX32_STEP(0x112, 0xf)   // row_shr:2
+    DH_MINMAX32_STEP(0x114, 0xf)   // row_shr:4
+    DH_MINMAX32_STEP(0x118, 0xf)   // row_shr:8
+    DH_MINMAX32_STEP(0x142, 0xa)   // row_bcast:15
+    DH_MINMAX32_STEP(0x143, 0xc)   // row_bcast:31
+#undef DH_MINMAX32_STEP
+    mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+    mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+}
+
+// The float of an eligible image (+0 for a zero of either sign).
+__device__ __forceinline__ float image_float(uint32_t im)
+{
+    return __uint_as_float((im & 0x80000000u) ? (im & 0x7fffffffu) : ~im);
+}
+
 // One wave's view of a round's histogram: lane l holds the bins just below NB - l * (NB/64),
 // in descending order, so a prefix sum over lanes is a suffix sum over bins.  Finds the bin d
 // with above < rem <= above + count, where `above` counts the keys in higher bins.  Returns
 // the total of the histogram.
 template <int NB>
-__device__ inline uint32_t locate(const uint32_t *h, uint32_t rem, uint32_t &d, uint32_t &above,
+__device__ __forceinline__ uint32_t locate(const uint32_t *h, uint32_t rem, uint32_t &d, uint32_t &above,
                                   uint32_t &count)
 {
     constexpr int PER = NB / 64;

@@ -14,15 +14,20 @@
 // (image << 32) | (0xffffffff - id) is a 64-bit key that is distinct per entry and whose
 // numeric order is exactly the ordering above, so ties need no special case.  Ineligible
 // entries get the key 0.
-//  * Pass 1, a workgroup per (row, chunk of 2048 to 8192 logits): a radix select over the chunk's keys
-//    (most significant byte first, histograms in LDS, stopping as soon as the boundary
-//    byte's bin is taken whole) finds the chunk's best min(k, n); they go to the workspace
-//    in any order, the rest of the chunk's k slots as zeros.  Any entry of the row's top-k
-//    is in its chunk's top-k.
-//  * Pass 2, a workgroup per row: the same select over the row's chunk lists keeps k; each
-//    survivor's slot is the number of survivors that beat it (the pages' rank-by-count
-//    order).  Values come back from the images (zeros, whose sign the image drops, are
-//    read from the logits, so -0 stays -0).
+//  * One launch, a workgroup per (row, chunk of 2048 to 8192 logits).  Chunk pass: a radix
+//    select over the chunk's keys (most significant byte first, histograms in LDS, stopping
+//    as soon as the boundary byte's bin is taken whole) finds the chunk's best min(k, n);
+//    they go to the workspace in any order, the rest of the chunk's k slots as zeros.  Any
+//    entry of the row's top-k is in its chunk's top-k.
+//  * Merge: each workgroup then takes a ticket on its row (an atomic count of the row's
+//    finished chunks, after a device-scope release of its list); the last one of the row
+//    (the "top-1 ... in parts and a join" of the pages, with the join done by whichever part
+//    ends last instead of a second launch) acquires the other lists and runs the same select
+//    over the row's chunk lists to keep k; each survivor's slot is the number of survivors
+//    that beat it (the pages' rank-by-count order).  Values come back from the images
+//    (zeros, whose sign the image drops, are read from the logits, so -0 stays -0).  The
+//    tickets start at zero: the GEMV before the top-k zeroes them (dh_draft), else a small
+//    kernel does (the call stays free of memset, so it can be captured in a graph).
 // Softmax statistics (STATS, for dh_topk_softmax): pass 1 also writes each chunk's largest
 // eligible logit m_c and s_c = sum over its eligible logits of exp(l - m_c) (1 for l == m_c,
 // so +inf entries count 1 each); the merge combines them in chunk order into the row's m and
@@ -42,32 +47,58 @@ namespace dh {
 namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
+constexpr int kCacheDevice = 16;         // gfx950 cache policy SC1: device-scope coherent
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
-// Radix select over 64-bit keys by ranges: a round sorts the keys of the current range into
-// 256 bins of width 2^shift from its base, the boundary bin becomes the next range (its width
-// 2^shift, the next bins 2^(shift - 8) wide), and the select stops as soon as that bin is
-// taken whole.  The
-// first range is [min, max] of the block's non-zero keys, so the first round spreads the keys
-// over the bins even when they share their leading bits (top logits share their exponent).
-// Each round has a histogram of its own (all cleared once at the start): after a round's one
-// barrier every wave scans the histogram itself (four bins a lane) and reaches the same
-// decision.  Eight rounds at most (the first shift is at most 56).
+// The lists a workgroup hands to the merging workgroup of its row, which may run on another
+// of the chip's dies (each has its own L2).  They are stored at device scope (SC1: written
+// through to where the dies' caches are coherent) and read back at device scope (SC1 loads,
+// which take no stale line from the reader's L2).  A wave's vmcnt reaching 0 means its
+// stores have been acknowledged there, so a wave waits for that before its workgroup takes
+// its ticket.  This avoids the release fence's write-back of the whole L2, which measured
+// many times the cost of the top-k itself.
+__device__ __forceinline__ void publish(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Two selects over the 64-bit keys a workgroup holds in registers (all distinct, 0 for an
+// ineligible entry); each finds the keys of the min(k, n) largest, n being the number of
+// non-zero keys.
+//  * select_bins (the usual one): one histogram round over the keys' values, in 256 bins of
+//    equal width between the smallest and the largest value (a monotone map, so a higher bin
+//    only holds larger values).  Logits spread over such bins; their order-preserving bits
+//    do not (the best logits of a row share their exponent, so a first round on the top
+//    byte of the bits puts most of them in one bin and serializes its LDS atomics).  The
+//    bin holding the k-th key is then resolved exactly: its keys are gathered in LDS and each
+//    counts the keys of the bin above it.
+//  * select_top, the fallback for a crowded boundary bin (many equal or nearly equal
+//    values): a radix select over the keys' bytes from the top, a round per byte, stopping as
+//    soon as the boundary byte's bin is taken whole.  Each round has a histogram of its own,
+//    and after a round's one barrier every wave scans the histogram itself (four bins a lane)
+//    and reaches the same decision.  Eight rounds at most.
 constexpr int kRounds = 8;
 constexpr int kHistWords = kRounds * 256;
+constexpr int kBoundMax = 512;   // keys of a boundary bin resolved by counting (in hist[256..])
 
 template <int NT>
 struct SelectLds {
-    uint32_t hist[kHistWords];
-    uint64_t wmin[NT / 64], wmax[NT / 64];         // per-wave extremes of the non-zero keys
+    uint32_t hist[kHistWords];                     // round histograms; [256..) the bin's keys
+    uint32_t imin[NT / 64], imax[NT / 64];         // per-wave extremes of the non-zero images
     float smax[NT / 64], ssum[NT / 64];            // per-wave softmax statistics (STATS)
-    uint32_t fill;                                 // survivors placed so far
+    uint64_t bkey;                                 // the boundary bin's cut
+    uint32_t fill, bfill;                          // survivors / boundary keys placed so far
 };
 
 // exp(l - m) of an eligible l below or at the maximum m; 1 when l == m (also for +inf).
-__device__ inline float rel_exp(float l, float m) { return l == m ? 1.0f : expf(l - m); }
+__device__ __forceinline__ float rel_exp(float l, float m) { return l == m ? 1.0f : expf(l - m); }
 
-__device__ inline float wave_max(float v)
+__device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -78,7 +109,7 @@ __device__ inline float wave_max(float v)
 }
 
 // A butterfly over the wave's lanes: a fixed association order, so the sum is reproducible.
-__device__ inline float wave_sum(float v)
+__device__ __forceinline__ float wave_sum(float v)
 {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1)
@@ -86,78 +117,78 @@ __device__ inline float wave_sum(float v)
     return v;
 }
 
+// Clears what select_bins needs (its round's histogram and the counters); the fallback
+// clears the other rounds' histograms itself.
 template <int NT>
-__device__ inline void clear_select(SelectLds<NT> &sh)
+__device__ __forceinline__ void clear_select(SelectLds<NT> &sh)
 {
-    for (int i = threadIdx.x; i < kHistWords; i += NT)
+    for (int i = threadIdx.x; i < 256; i += NT)
         sh.hist[i] = 0;
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         sh.fill = 0;
+        sh.bfill = 0;
+    }
 }
 
-// This wave's extremes to LDS (call before the barrier that follows clear_select).
+// This wave's extremes of the non-zero images to LDS (call before the barrier that follows
+// clear_select).
 template <int N, int NT>
-__device__ inline void publish_min_max(const uint64_t (&key)[N], SelectLds<NT> &sh)
+__device__ __forceinline__ void publish_range(const uint64_t (&key)[N], SelectLds<NT> &sh)
 {
-    uint64_t mn = ~0ull, mx = 0;
+    uint32_t mn = ~0u, mx = 0;
 #pragma unroll
     for (int i = 0; i < N; i++) {
-        mn = key[i] != 0 && key[i] < mn ? key[i] : mn;
-        mx = key[i] > mx ? key[i] : mx;
+        const uint32_t im = (uint32_t)(key[i] >> 32);
+        mn = im != 0 && im < mn ? im : mn;
+        mx = im > mx ? im : mx;
     }
-    wave_min_max(mn, mx);
+    wave_min_max32(mn, mx);
     if ((threadIdx.x & 63) == 0) {
-        sh.wmin[threadIdx.x >> 6] = mn;
-        sh.wmax[threadIdx.x >> 6] = mx;
+        sh.imin[threadIdx.x >> 6] = mn;
+        sh.imax[threadIdx.x >> 6] = mx;
     }
 }
 
-// Selects among the non-zero keys held in registers (all distinct).  Returns P such that
-// the keys >= P are exactly the min(k, n) largest, where n (returned in `total`) is the
-// number of non-zero keys.  RANGED: the first range is [min, max] of the non-zero keys (call
-// publish_min_max before the barrier); otherwise it is the whole key space, i.e. the digits
-// are the keys' bytes from the top, which costs no reduction and suits keys whose top byte
-// already varies.  Before the call: clear_select (and publish_min_max), a barrier.
-template <bool RANGED, int N, int NT>
-__device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds<NT> &sh,
-                               uint32_t &total)
+// The number of keys of list[0..n) above x, with several LDS reads in flight.
+__device__ __forceinline__ uint32_t count_above(const uint64_t *list, int n, uint64_t x)
 {
-    uint64_t lo = 0, hi = ~0ull;
-    if constexpr (RANGED) {
-        lo = ~0ull;
-        hi = 0;
+    uint32_t c = 0;
+    int j = 0;
+    for (; j + 8 <= n; j += 8) {
+        uint4 q[4];
 #pragma unroll
-        for (int w = 0; w < NT / 64; w++) {
-            lo = sh.wmin[w] < lo ? sh.wmin[w] : lo;
-            hi = sh.wmax[w] > hi ? sh.wmax[w] : hi;
+        for (int t = 0; t < 4; t++)
+            q[t] = *reinterpret_cast<const uint4 *>(&list[j + 2 * t]);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            c += (((uint64_t)q[t].y << 32) | q[t].x) > x;
+            c += (((uint64_t)q[t].w << 32) | q[t].z) > x;
         }
-        total = 0;
-        if (hi == 0)
-            return 1;                              // no non-zero key
     }
-    const uint64_t span = hi - lo;
-    int shift = span >> 8 ? 64 - __builtin_clzll(span >> 8) : 0;   // span >> shift < 256
-    uint64_t base = lo;
+    for (; j < n; j++)
+        c += list[j] > x;
+    return c;
+}
+
+// Radix select (the fallback; see above) among the non-zero keys i with inc(i).  Returns P
+// such that those keys >= P are exactly the min(k, n) largest of them; n in `total`.
+// Before the call: the whole histogram cleared, a barrier.
+template <int N, int NT, typename Inc>
+__device__ __forceinline__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds<NT> &sh,
+                               uint32_t &total, Inc inc)
+{
+    int shift = 56;
+    uint64_t base = 0;
     uint32_t rem = k;
-    int wshift = 64;                               // the range's width is 2^wshift (64: all)
+    int wshift = 64;                               // the range: keys sharing base above wshift
 #pragma unroll 1
     for (int round = 0; round < kRounds; round++) {
         uint32_t *h = sh.hist + 256 * round;
-        if constexpr (RANGED) {
+        const uint64_t mask = wshift == 64 ? 0ull : ~0ull << wshift;
 #pragma unroll
-            for (int i = 0; i < N; i++) {
-                const uint64_t off = key[i] - base;
-                if (key[i] != 0 && key[i] >= base && (wshift == 64 || (off >> wshift) == 0))
-                    atomicAdd(&h[(uint32_t)(off >> shift)], 1u);
-            }
-        } else {
-            // whole key space: the range is the keys sharing base's bits above wshift
-            const uint64_t mask = wshift == 64 ? 0ull : ~0ull << wshift;
-#pragma unroll
-            for (int i = 0; i < N; i++)
-                if (key[i] != 0 && (key[i] & mask) == base)
-                    atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
-        }
+        for (int i = 0; i < N; i++)
+            if (key[i] != 0 && inc(i) && (key[i] & mask) == base)
+                atomicAdd(&h[(uint32_t)(key[i] >> shift) & 255u], 1u);
         __syncthreads();
         uint32_t d, above, count;
         const uint32_t t = locate<256>(h, rem, d, above, count);
@@ -171,20 +202,105 @@ __device__ uint64_t select_top(const uint64_t (&key)[N], uint32_t k, SelectLds<N
         if (count == rem || shift == 0)            // the boundary bin is taken whole
             return base;
         wshift = shift;                            // the boundary bin is the next range
-        shift = shift > 8 ? shift - 8 : 0;
+        shift -= 8;
     }
     return base;                                   // not reached: shift 0 ends by then
 }
 
-// Pass 1: one workgroup of NT threads per (chunk of NT * kP1PerThread logits, row); thread
-// t holds entries base + j*NT + t.  STATS: the chunk's (m_c, s_c) to stats[row][chunk].
-template <int NT, bool STATS>
-__global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V, int k,
-                                                 int nchunks, uint64_t *cand, float2 *stats)
+// The outcome of select_bins: the survivors are the non-zero keys whose bin is above d, or
+// is d with a key >= P; when not binned, every non-zero key.
+struct Cut {
+    bool binned;
+    uint32_t d;
+    uint64_t P;
+};
+
+__device__ __forceinline__ bool survives(const Cut &c, uint64_t key, uint32_t bin)
 {
-    __shared__ __align__(16) SelectLds<NT> sh;
-    constexpr int PER = kP1PerThread;
-    const int r = blockIdx.y, c = blockIdx.x;
+    return key != 0 && (!c.binned || bin > c.d || (bin == c.d && key >= c.P));
+}
+
+// Before the call: clear_select, publish_range, a barrier.  bin[i] receives key i's bin.
+template <int N, int NT>
+__device__ __forceinline__ Cut select_bins(const uint64_t (&key)[N], uint32_t k, SelectLds<NT> &sh,
+                           uint32_t &total, uint32_t (&bin)[N])
+{
+    uint32_t mn = ~0u, mx = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) {
+        mn = sh.imin[w] < mn ? sh.imin[w] : mn;
+        mx = sh.imax[w] > mx ? sh.imax[w] : mx;
+    }
+    Cut c{false, 0u, 1ull};
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        bin[i] = 0;
+    if (mx == 0)
+        return c;                                  // no eligible entry
+    // bin(x) = min(255, floor((x - lo) * scale)): monotone in x.  Degenerate ranges stay
+    // monotone: a zero width (scale +inf) or a +inf maximum (scale 0) send the values that
+    // make (x - lo) * scale NaN or infinite to bin 255 (fminf drops a NaN) and the rest to 0.
+    const float lo = image_float(mn);
+    const float scale = 256.0f / (image_float(mx) - lo);
+    uint32_t *h = sh.hist;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        bin[i] = (uint32_t)fminf((image_float((uint32_t)(key[i] >> 32)) - lo) * scale, 255.0f);
+        if (key[i] != 0)
+            atomicAdd(&h[bin[i]], 1u);
+    }
+    __syncthreads();
+    uint32_t d, above, count;
+    total = locate<256>(h, k, d, above, count);
+    if (total <= k)
+        return c;                                  // every non-zero key
+    c.binned = true;
+    c.d = d;
+    const uint32_t rem = k - above;
+    if (count == rem)
+        return c;                                  // the boundary bin is taken whole
+    if (count <= (uint32_t)kBoundMax && count <= (uint32_t)NT) {
+        // the bin's keys to LDS; the key with exactly rem - 1 of them above it is the cut
+        uint64_t *list = reinterpret_cast<uint64_t *>(sh.hist + 256);
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < N; i++)
+            mine += key[i] != 0 && bin[i] == d;
+        uint32_t at = wave_reserve(mine, &sh.bfill);
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < N; i++)
+                if (key[i] != 0 && bin[i] == d)
+                    list[at++] = key[i];
+        }
+        __syncthreads();
+        if (threadIdx.x < count) {
+            const uint64_t x = list[threadIdx.x];
+            if (count_above(list, (int)count, x) == rem - 1)
+                sh.bkey = x;
+        }
+        __syncthreads();
+        c.P = sh.bkey;
+        return c;
+    }
+    // a crowded boundary bin: the radix select among its keys
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHistWords; i += NT)
+        sh.hist[i] = 0;
+    __syncthreads();
+    uint32_t n2;
+    c.P = select_top<N, NT>(key, rem, sh, n2, [&](int i) { return bin[i] == d; });
+    return c;
+}
+
+// The chunk pass: the best min(k, n) of chunk c of row r (its NT * PER logits; thread t
+// holds entries base + j * NT + t) to the row's list slots cand[r][c][0..k), in any order,
+// the remaining slots zero.  STATS: the chunk's (m_c, s_c) to stats[r][c].
+template <int NT, int PER, bool STATS>
+__device__ __forceinline__ void chunk_pass(const float *logits, int64_t V, int k, int nchunks, int r,
+                                  int c, uint64_t *cand, float2 *stats, SelectLds<NT> &sh)
+{
     const int64_t base = (int64_t)c * (NT * PER);
 
     // coalesced buffer loads bounded by the row, all issued before any is used; entries
@@ -204,6 +320,7 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         const uint32_t im = id < V ? order_key(__uint_as_float(u[j])) : 0u;
         key[j] = im ? entry_key(im, (uint32_t)id) : 0ull;
     }
+    publish_range<PER, NT>(key, sh);
     float lmax = -__builtin_inff();
     if constexpr (STATS) {
 #pragma unroll
@@ -218,7 +335,7 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
     }
     __syncthreads();
     if constexpr (STATS) {
-        // the chunk's maximum, then this wave's sum; select_top's first barrier publishes it
+        // the chunk's maximum, then this wave's sum; the select's first barrier publishes it
         lmax = sh.smax[0];
 #pragma unroll
         for (int w = 1; w < NT / 64; w++)
@@ -232,14 +349,15 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
         if ((threadIdx.x & 63) == 0)
             sh.ssum[threadIdx.x >> 6] = s;
     }
-    uint32_t n;
-    const uint64_t P = select_top<false, PER, NT>(key, (uint32_t)k, sh, n);
+    uint32_t n, bin[PER];
+    const Cut cut = select_bins<PER, NT>(key, (uint32_t)k, sh, n, bin);
     if constexpr (STATS) {
         if (threadIdx.x == 0) {
             float s = 0.f;
             for (int w = 0; w < NT / 64; w++)
                 s += sh.ssum[w];
-            stats[(int64_t)r * nchunks + c] = float2{lmax, s};
+            publish(reinterpret_cast<uint64_t *>(stats + (int64_t)r * nchunks + c),
+                    ((uint64_t)__float_as_uint(s) << 32) | __float_as_uint(lmax));
         }
     }
     const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
@@ -248,23 +366,23 @@ __global__ __launch_bounds__(NT) void topk_pass1(const float *logits, int64_t V,
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < PER; j++)
-        mine += key[j] != 0 && key[j] >= P;
+        mine += survives(cut, key[j], bin[j]);
     uint64_t *out = cand + ((int64_t)r * nchunks + c) * k;
     uint32_t at = wave_reserve(mine, &sh.fill);
     if (mine) {
 #pragma unroll
         for (int j = 0; j < PER; j++)
-            if (key[j] != 0 && key[j] >= P && at < (uint32_t)k)   // exactly `kept` survive
-                out[at++] = key[j];
+            if (survives(cut, key[j], bin[j]) && at < (uint32_t)k)   // exactly `kept` survive
+                publish(&out[at++], key[j]);
     }
     for (int s = kept + threadIdx.x; s < k; s += NT)
-        out[s] = 0ull;                             // empty slots
+        publish(&out[s], 0ull);                    // empty slots
 }
 
 // One step of a descending bitonic network on the key x held by slot i (a lane): the
 // partner is slot i ^ stride, and in a block of `size` whose size bit is clear the lower
 // slot keeps the larger key.
-__device__ inline uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size, int stride)
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size, int stride)
 {
     const bool lower = (i & stride) == 0, desc = (i & size) == 0;
     const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
@@ -275,7 +393,7 @@ __device__ inline uint64_t bitonic_step(uint64_t x, uint64_t y, int i, int size,
 // permutes for 1 and 2 (no LDS), ds_swizzle's xor mode within 32 lanes for 4..16, a
 // bpermute for 32.
 template <int S>
-__device__ inline uint32_t lane_xor(uint32_t v)
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v)
 {
     if constexpr (S == 1)
         return __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);   // quad_perm 1,0,3,2
@@ -288,7 +406,7 @@ __device__ inline uint32_t lane_xor(uint32_t v)
 }
 
 template <int SIZE, int S>
-__device__ inline uint64_t bitonic(uint64_t x, int l)
+__device__ __forceinline__ uint64_t bitonic(uint64_t x, int l)
 {
     const uint64_t y = ((uint64_t)lane_xor<S>((uint32_t)(x >> 32)) << 32) |
                        lane_xor<S>((uint32_t)x);
@@ -296,7 +414,7 @@ __device__ inline uint64_t bitonic(uint64_t x, int l)
 }
 
 // Sorts the 64 keys of a wave in descending order (lane 0 the largest).
-__device__ inline uint64_t wave_sort_desc(uint64_t x, int l)
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int l)
 {
     x = bitonic<2, 1>(x, l);
     x = bitonic<4, 2>(x, l);
@@ -321,81 +439,84 @@ __device__ inline uint64_t wave_sort_desc(uint64_t x, int l)
     return bitonic<64, 1>(x, l);
 }
 
-// Up to this many survivors the merge ranks by counting; above, by sorted runs of 64.
-constexpr int kCountMax = 128;
-// Above this k the merge's select ranges over [min, max] of the keys (measured: for k = 1
-// the reduction costs more than the rounds it saves).
-constexpr int kRangedMinK = 8;
+// LDS of the merge beyond the select's: the survivors, and the row's softmax statistics.
+struct MergeLds {
+    uint64_t sel[DH_MAX_K];
+    float row_m, row_z;
+};
 
-// Pass 2: one workgroup per row; a thread holds PER of the row's nchunks * k list slots
-// (PER * kMergeThreads >= nchunks * k).  The lists hold the chunks' top values, which share
-// their leading bits, so for more than a few winners the select ranges over [min, max].
-// STATS: the row's softmax statistics from the chunks' (m_c, s_c): probs[r][slot] and lse[r].
-template <int PER, bool RANGED, bool STATS>
-__global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits, int64_t V,
-                                                            int k, int nchunks,
-                                                            const uint64_t *cand,
-                                                            const int32_t *idmap, int32_t *ids,
-                                                            float *vals, int32_t *argmax,
-                                                            const float2 *stats, float *probs,
-                                                            float *lse)
+// The merge of row r: a thread holds MPER of the row's nchunks * k list slots
+// (MPER * NT >= nchunks * k), and the same select as the chunk pass keeps k of them.  STATS:
+// the row's softmax statistics from the chunks' (m_c, s_c): probs[r][slot] and lse[r].
+template <int MPER, int NT, bool STATS>
+__device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k, int nchunks, int r,
+                                 const uint64_t *cand, const int32_t *idmap, int32_t *ids,
+                                 float *vals, int32_t *argmax, const float2 *stats,
+                                 float *probs, float *lse, SelectLds<NT> &sh, MergeLds &ml)
 {
-    __shared__ __align__(16) SelectLds<kMergeThreads> sh;
-    __shared__ __align__(16) uint64_t sel[DH_MAX_K];
-    __shared__ float row_m, row_z;
-    const int r = blockIdx.x;
     const int slots = nchunks * k;
     const uint64_t *src = cand + (int64_t)r * slots;
+    uint64_t *sel = ml.sel;
 
     // all loads issued together (bounded buffer loads: slots past the end read as 0)
     const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
         (void *)src, (short)0, slots * 8, kRsrcWord3);
-    uint64_t key[PER];
+    uint64_t key[MPER];
 #pragma unroll
-    for (int j = 0; j < PER; j++) {
+    for (int j = 0; j < MPER; j++) {
         const v2u32 q = __builtin_amdgcn_raw_buffer_load_b64(
-            ls, (uint32_t)(j * kMergeThreads + threadIdx.x) * 8u, 0, 0);
+            ls, (uint32_t)(j * NT + threadIdx.x) * 8u, 0, kCacheDevice);
         key[j] = ((uint64_t)q.y << 32) | q.x;
     }
-    clear_select<kMergeThreads>(sh);
-    if constexpr (RANGED)
-        publish_min_max<PER, kMergeThreads>(key, sh);
+    clear_select<NT>(sh);
+    publish_range<MPER, NT>(key, sh);
     if constexpr (STATS) {
         // wave 0: m = max_c m_c, then z = sum_c s_c exp(m_c - m), chunks c = lane, lane + 64,
         // ... summed in that order per lane, then across lanes by a butterfly
         if (threadIdx.x < 64) {
-            const float2 *st = stats + (int64_t)r * nchunks;
+            const uint64_t *st = reinterpret_cast<const uint64_t *>(stats + (int64_t)r * nchunks);
+            constexpr int kMaxChunks = DH_MAX_VOCAB / 2048;
+            float cm[kMaxChunks / 64], cs[kMaxChunks / 64];   // this lane's chunks' (m_c, s_c)
+#pragma unroll
+            for (int j = 0; j < kMaxChunks / 64; j++) {
+                const int c = threadIdx.x + 64 * j;
+                const uint64_t v = c < nchunks ? fetch(&st[c]) : 0ull;
+                cm[j] = c < nchunks ? __uint_as_float((uint32_t)v) : -__builtin_inff();
+                cs[j] = __uint_as_float((uint32_t)(v >> 32));
+            }
             float m = -__builtin_inff();
-            for (int c = threadIdx.x; c < nchunks; c += 64)
-                m = st[c].x > m ? st[c].x : m;
+#pragma unroll
+            for (int j = 0; j < kMaxChunks / 64; j++)
+                m = cm[j] > m ? cm[j] : m;
             m = wave_max(m);
             float z = 0.f;
-            for (int c = threadIdx.x; c < nchunks; c += 64)
-                if (st[c].y > 0.f)
-                    z += st[c].y * rel_exp(st[c].x, m);
+#pragma unroll
+            for (int j = 0; j < kMaxChunks / 64; j++)
+                if (cs[j] > 0.f)
+                    z += cs[j] * rel_exp(cm[j], m);
             z = wave_sum(z);
             if (threadIdx.x == 0) {
-                row_m = m;
-                row_z = z;
+                ml.row_m = m;
+                ml.row_z = z;
                 lse[r] = z > 0.f ? m + logf(z) : -__builtin_inff();
             }
         }
     }
     __syncthreads();
-    uint32_t n;
-    const uint64_t P = select_top<RANGED, PER, kMergeThreads>(key, (uint32_t)k, sh, n);
+    uint32_t n, bin[MPER];
+    const Cut cut = select_bins<MPER, NT>(key, (uint32_t)k, sh, n, bin);
     const int kk = n < (uint32_t)k ? (int)n : k;
 
     // the survivors, in any order, to sel[0..kk)
     uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < PER; j++)
-        mine += key[j] != 0 && key[j] >= P;
+    for (int j = 0; j < MPER; j++)
+        mine += survives(cut, key[j], bin[j]);
     uint32_t at = wave_reserve(mine, &sh.fill);
     if (mine) {
 #pragma unroll
-        for (int j = 0; j < PER; j++)
-            if (key[j] != 0 && key[j] >= P && at < (uint32_t)kk)   // exactly kk survive
+        for (int j = 0; j < MPER; j++)
+            if (survives(cut, key[j], bin[j]) && at < (uint32_t)kk)   // exactly kk survive
                 sel[at++] = key[j];
     }
     __syncthreads();
@@ -410,19 +531,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         // few survivors: count directly
         if (i < kk) {
             x = sel[i];
-            int j = 0;
-            for (; j + 2 <= kk; j += 2) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(&sel[j]);
-                rank += (((uint64_t)q.y << 32) | q.x) > x;
-                rank += (((uint64_t)q.w << 32) | q.z) > x;
-            }
-            if (j < kk)
-                rank += sel[j] > x;
+            rank = count_above(sel, kk, x);
         }
     } else {
         // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then
         // a survivor's rank is its place in its run plus, for each other run, the number of
-        // that run's keys above it (a binary search)
+        // that run's keys above it (a binary search); the workgroup has a wave per run
         const int nruns = (kk + 63) >> 6;
         const int w = i >> 6, l = i & 63;
         if (w < nruns) {
@@ -474,11 +588,11 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         const float v = image_value(x, logits + (int64_t)r * V + id);
         rval[rank] = v;
         if constexpr (STATS)
-            probs[(int64_t)r * k + rank] = rel_exp(v, row_m) / row_z;
+            probs[(int64_t)r * k + rank] = rel_exp(v, ml.row_m) / ml.row_z;
         if (rank == 0 && argmax)
             argmax[r] = out;
     }
-    for (int p = kk + i; p < k; p += kMergeThreads) {
+    for (int p = kk + i; p < k; p += NT) {
         rid[p] = 0;
         rval[p] = -__builtin_inff();
         if constexpr (STATS)
@@ -488,97 +602,135 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *logits,
         argmax[r] = 0;
 }
 
+struct TopkArgs {
+    const float *logits;
+    int64_t V;
+    int k, nchunks;
+    uint64_t *cand;
+    float2 *stats;          // STATS only
+    uint32_t *tickets;      // [rows], zero at the start
+    const int32_t *idmap;
+    int32_t *ids;
+    float *vals;
+    int32_t *argmax;
+    float *probs, *lse;     // STATS only
+};
+
+// The whole top-k in one launch: a workgroup of NT threads per (chunk, row) runs the chunk
+// pass; the row's last workgroup to finish runs the merge.  Every wave's list stores are
+// acknowledged at device scope (publish, stores_done) before the workgroup takes its ticket;
+// the last workgroup reads the row's lists at device scope.  Nothing waits on another
+// workgroup: every workgroup either ends after its ticket or merges.
+template <int NT, int PER, int MPER, bool STATS>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a)
+{
+    __shared__ __align__(16) SelectLds<NT> sh;
+    __shared__ __align__(16) MergeLds ml;
+    __shared__ uint32_t last;
+    const int r = blockIdx.y, c = blockIdx.x;
+    chunk_pass<NT, PER, STATS>(a.logits, a.V, a.k, a.nchunks, r, c, a.cand, a.stats, sh);
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        last = atomicAdd(&a.tickets[(int64_t)r * kTicketStride], 1u) == (uint32_t)a.nchunks - 1u;
+    __syncthreads();
+    if (!last)
+        return;
+    merge_row<MPER, NT, STATS>(a.logits, a.V, a.k, a.nchunks, r, a.cand, a.idmap,
+                                       a.ids, a.vals, a.argmax, a.stats, a.probs, a.lse, sh,
+                                       ml);
+}
+
+__global__ __launch_bounds__(64) void zero_tickets(uint32_t *t, int n)
+{
+    if ((int)threadIdx.x < n)
+        t[threadIdx.x * kTicketStride] = 0u;
+}
+
 }  // namespace
 
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
 {
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    const size_t nc = (size_t)topk_chunks(vocab, k);
+    const size_t nc = (size_t)topk_shape(rows, vocab, k).nchunks;
     TopkWs w;
     w.keys_off = 0;   // the chunk lists hold keys that carry both the value and the id
     w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
-    w.bytes = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
+    w.tickets_off = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
+    w.bytes = w.tickets_off + up((size_t)rows * kTicketStride * sizeof(uint32_t));
     return w;
 }
 
-template <int PER, bool STATS>
-hipError_t launch_merge2(const float *logits, int rows, int64_t vocab, int k, int nc,
-                         const uint64_t *cand, const int32_t *idmap, int32_t *ids, float *vals,
-                         int32_t *argmax, const float2 *stats, float *probs, float *lse,
-                         hipStream_t stream)
+uint32_t *topk_tickets(void *ws, int rows, int64_t vocab, int k)
 {
-    if (k > kRangedMinK)
-        return launch(topk_merge<PER, true, STATS>, dim3(rows), dim3(kMergeThreads), 0, stream,
-                      logits, vocab, k, nc, cand, idmap, ids, vals, argmax, stats, probs, lse);
-    return launch(topk_merge<PER, false, STATS>, dim3(rows), dim3(kMergeThreads), 0, stream,
-                  logits, vocab, k, nc, cand, idmap, ids, vals, argmax, stats, probs, lse);
+    return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) +
+                                        topk_ws_layout(rows, vocab, k).tickets_off);
 }
 
-template <int PER>
-hipError_t launch_merge(const float *logits, int rows, int64_t vocab, int k, int nc,
-                        const uint64_t *cand, const int32_t *idmap, int32_t *ids, float *vals,
-                        int32_t *argmax, const float2 *stats, float *probs, float *lse,
-                        hipStream_t stream)
+template <int NT, int PER, int MPER, bool STATS>
+hipError_t launch_shape(const TopkArgs &a, int rows, hipStream_t stream)
 {
-    if (probs)
-        return launch_merge2<PER, true>(logits, rows, vocab, k, nc, cand, idmap, ids, vals,
-                                        argmax, stats, probs, lse, stream);
-    return launch_merge2<PER, false>(logits, rows, vocab, k, nc, cand, idmap, ids, vals, argmax,
-                                     nullptr, nullptr, nullptr, stream);
+    return launch(topk_kernel<NT, PER, MPER, STATS>, dim3(a.nchunks, rows), dim3(NT), 0,
+                  stream, a);
 }
 
-template <int NT>
-hipError_t launch_pass1(const float *logits, int rows, int64_t vocab, int k, int nc,
-                        uint64_t *cand, float2 *stats, hipStream_t stream)
+template <int NT, int PER, bool STATS>
+hipError_t launch_nt(const TopkArgs &a, int rows, hipStream_t stream)
 {
-    const dim3 g1(nc, rows);
-    if (stats)
-        return launch(topk_pass1<NT, true>, g1, dim3(NT), 0, stream, logits, vocab, k, nc, cand,
-                      stats);
-    return launch(topk_pass1<NT, false>, g1, dim3(NT), 0, stream, logits, vocab, k, nc, cand,
-                  stats);
+    const int64_t slots = (int64_t)a.nchunks * a.k;   // <= kMergePer * NT by the shape rule
+    if (slots <= NT)
+        return launch_shape<NT, PER, 1, STATS>(a, rows, stream);
+    if (slots <= 2 * NT)
+        return launch_shape<NT, PER, 2, STATS>(a, rows, stream);
+    if (slots <= 4 * NT)
+        return launch_shape<NT, PER, 4, STATS>(a, rows, stream);
+    if (slots <= 8 * NT)
+        return launch_shape<NT, PER, 8, STATS>(a, rows, stream);
+    return launch_shape<NT, PER, kMergePer, STATS>(a, rows, stream);
+}
+
+template <bool STATS>
+hipError_t launch_stats(const TopkArgs &a, const TopkShape &sh, int rows, hipStream_t stream)
+{
+    switch (sh.nt * 16 + sh.per) {
+    case 512 * 16 + 4: return launch_nt<512, 4, STATS>(a, rows, stream);
+    case 1024 * 16 + 4: return launch_nt<1024, 4, STATS>(a, rows, stream);
+    case 256 * 16 + 8: return launch_nt<256, 8, STATS>(a, rows, stream);
+    case 512 * 16 + 8: return launch_nt<512, 8, STATS>(a, rows, stream);
+    default: return launch_nt<1024, 8, STATS>(a, rows, stream);
+    }
 }
 
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                       void *ws, hipStream_t stream, float *probs, float *lse)
+                       void *ws, hipStream_t stream, float *probs, float *lse,
+                       bool tickets_zeroed)
 {
     const TopkWs w = topk_ws_layout(rows, vocab, k);
-    const int chunk = topk_chunk(vocab, k);
-    const int nc = (int)topk_chunks(vocab, k);
-    uint64_t *cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.keys_off);
-    float2 *stats = probs ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + w.stats_off)
-                          : nullptr;
-    hipError_t e;
-    switch (chunk) {
-    case 2048:
-        e = launch_pass1<2048 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
-        break;
-    case 4096:
-        e = launch_pass1<4096 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
-        break;
-    default:
-        e = launch_pass1<8192 / kP1PerThread>(logits, rows, vocab, k, nc, cand, stats, stream);
-        break;
+    TopkArgs a;
+    a.logits = logits;
+    a.V = vocab;
+    a.k = k;
+    const TopkShape shape = topk_shape(rows, vocab, k);
+    a.nchunks = (int)shape.nchunks;
+    a.cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.keys_off);
+    a.stats = probs ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + w.stats_off)
+                    : nullptr;
+    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + w.tickets_off);
+    a.idmap = idmap;
+    a.ids = ids;
+    a.vals = vals;
+    a.argmax = argmax;
+    a.probs = probs;
+    a.lse = lse;
+    if (!tickets_zeroed) {
+        const hipError_t e = launch(zero_tickets, dim3(1), dim3(64), 0, stream, a.tickets, rows);
+        if (e != hipSuccess)
+            return e;
     }
-    if (e != hipSuccess)
-        return e;
-    const uint64_t *cc = cand;
-    const int64_t slots = (int64_t)nc * k;         // <= kMergeSlots by the chunk choice
-    if (slots <= kMergeThreads)
-        return launch_merge<1>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stats, probs, lse, stream);
-    if (slots <= 2 * kMergeThreads)
-        return launch_merge<2>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stats, probs, lse, stream);
-    if (slots <= 4 * kMergeThreads)
-        return launch_merge<4>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stats, probs, lse, stream);
-    if (slots <= 8 * kMergeThreads)
-        return launch_merge<8>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                               stats, probs, lse, stream);
-    return launch_merge<16>(logits, rows, vocab, k, nc, cc, idmap, ids, vals, argmax,
-                            stats, probs, lse, stream);
+    if (probs)
+        return launch_stats<true>(a, shape, rows, stream);
+    return launch_stats<false>(a, shape, rows, stream);
 }
 
 }  // namespace dh

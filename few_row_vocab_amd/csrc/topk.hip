@@ -208,10 +208,11 @@ __device__ __forceinline__ uint64_t select_top(const uint64_t (&key)[N], uint32_
 }
 
 // The outcome of select_bins: the survivors are the non-zero keys whose bin is above d, or
-// is d with a key >= P; when not binned, every non-zero key.
+// is d with a key >= P (rem of them); when not binned, every non-zero key.  Unless crowded
+// (the fallback ran), hist[0..256) still holds every bin's count of non-zero keys.
 struct Cut {
-    bool binned;
-    uint32_t d;
+    bool binned, crowded;
+    uint32_t d, rem;
     uint64_t P;
 };
 
@@ -231,7 +232,7 @@ __device__ __forceinline__ Cut select_bins(const uint64_t (&key)[N], uint32_t k,
         mn = sh.imin[w] < mn ? sh.imin[w] : mn;
         mx = sh.imax[w] > mx ? sh.imax[w] : mx;
     }
-    Cut c{false, 0u, 1ull};
+    Cut c{false, false, 0u, 0u, 1ull};
     total = 0;
 #pragma unroll
     for (int i = 0; i < N; i++)
@@ -258,6 +259,7 @@ __device__ __forceinline__ Cut select_bins(const uint64_t (&key)[N], uint32_t k,
     c.binned = true;
     c.d = d;
     const uint32_t rem = k - above;
+    c.rem = rem;
     if (count == rem)
         return c;                                  // the boundary bin is taken whole
     if (count <= (uint32_t)kBoundMax && count <= (uint32_t)NT) {
@@ -285,6 +287,7 @@ __device__ __forceinline__ Cut select_bins(const uint64_t (&key)[N], uint32_t k,
         return c;
     }
     // a crowded boundary bin: the radix select among its keys
+    c.crowded = true;
     __syncthreads();
     for (int i = threadIdx.x; i < kHistWords; i += NT)
         sh.hist[i] = 0;
@@ -439,6 +442,142 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int l)
     return bitonic<64, 1>(x, l);
 }
 
+// The merge's select, select_sorted: select_bins that also puts the survivors in order.  The
+// histogram's atomics return each key's index among its bin's keys; bin b's survivors then
+// take the slots [start[b], start[b] + s(b)) of the output, s(b) being the bin's count above
+// the boundary bin d and rem in it (start: a suffix sum over the bins).  A survivor of a bin
+// above d goes to start[b] + its index, and the final pass counts the keys of its bin above
+// it; the survivors of bin d are picked by ranking its keys against each other (as
+// select_bins resolves its boundary), and that rank is already their place.  Bins are narrow,
+// so the final counts are short.  start and the bin of each slot live in the histogram words
+// past the boundary keys.
+constexpr int kStartOff = 256 + 2 * kBoundMax;
+constexpr int kBinOfOff = kStartOff + 256;
+constexpr uint32_t kPlaced = 0xffffffffu;   // a slot's bin when its key is already in order
+static_assert(kBinOfOff + DH_MAX_K <= kHistWords, "the merge's slots fit the histogram words");
+
+// One wave: start[] of every bin (a suffix sum over the bins, as locate's lanes hold them).
+__device__ __forceinline__ void bin_starts(const uint32_t *h, const Cut &c, uint32_t *start)
+{
+    const int lo = 256 - 4 * ((threadIdx.x & 63) + 1);   // this lane's four bins
+    uint32_t s[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const uint32_t b = (uint32_t)(lo + j);
+        s[j] = !c.binned || b > c.d ? h[b] : b == c.d ? c.rem : 0u;
+        sum += s[j];
+    }
+    uint32_t run = wave_scan(sum) - sum;           // survivors in the bins above this lane's
+#pragma unroll
+    for (int j = 3; j >= 0; j--) {
+        start[lo + j] = run;
+        run += s[j];
+    }
+}
+
+// The number of keys of list[lo..lo + n) above x (8-byte reads: a segment may start at any
+// slot), several in flight.
+__device__ __forceinline__ uint32_t count_above_at(const uint64_t *list, uint32_t lo,
+                                                   uint32_t n, uint64_t x)
+{
+    uint32_t c = 0, j = 0;
+    for (; j + 4 <= n; j += 4) {
+        uint64_t y[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            y[t] = list[lo + j + t];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            c += y[t] > x;
+    }
+    for (; j < n; j++)
+        c += list[lo + j] > x;
+    return c;
+}
+
+// Before the call: clear_select, publish_range, a barrier.  Returns the number of survivors
+// kk, written to sel[0..kk) with each slot's bin (or kPlaced) in hist[kBinOfOff + slot]; or
+// -1 when the boundary bin is crowded, with c and bin[] set for the caller's fallback (and
+// nothing placed).
+template <int N, int NT>
+__device__ __forceinline__ int select_sorted(const uint64_t (&key)[N], uint32_t k,
+                                             SelectLds<NT> &sh, uint64_t *sel, Cut &c,
+                                             uint32_t (&bin)[N])
+{
+    uint32_t mn = ~0u, mx = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) {
+        mn = sh.imin[w] < mn ? sh.imin[w] : mn;
+        mx = sh.imax[w] > mx ? sh.imax[w] : mx;
+    }
+    c = Cut{false, false, 0u, 0u, 1ull};
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        bin[i] = 0;
+    if (mx == 0)
+        return 0;                                  // no eligible entry
+    const float lo = image_float(mn);              // the value bins, as select_bins
+    const float scale = 256.0f / (image_float(mx) - lo);
+    uint32_t *h = sh.hist;
+    uint32_t idx[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        bin[i] = (uint32_t)fminf((image_float((uint32_t)(key[i] >> 32)) - lo) * scale, 255.0f);
+        idx[i] = key[i] != 0 ? atomicAdd(&h[bin[i]], 1u) : 0u;
+    }
+    __syncthreads();
+    uint32_t d, above, count;
+    const uint32_t total = locate<256>(h, k, d, above, count);
+    bool pick = false;                             // bin d's survivors picked through the list
+    if (total > k) {
+        c.binned = true;
+        c.d = d;
+        c.rem = k - above;
+        if (count > c.rem) {
+            if (count > (uint32_t)kBoundMax || count > (uint32_t)NT) {
+                c.crowded = true;
+                return -1;
+            }
+            pick = true;
+        }
+    }
+    uint32_t *start = sh.hist + kStartOff, *binof = sh.hist + kBinOfOff;
+    uint64_t *list = reinterpret_cast<uint64_t *>(sh.hist + 256);
+    if (threadIdx.x < 64)
+        bin_starts(h, c, start);
+    if (pick) {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < N; i++)
+            mine += key[i] != 0 && bin[i] == d;
+        uint32_t at = wave_reserve(mine, &sh.bfill);
+        if (mine) {
+#pragma unroll
+            for (int i = 0; i < N; i++)
+                if (key[i] != 0 && bin[i] == d)
+                    list[at++] = key[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        if (key[i] != 0 && (!c.binned || bin[i] > d || (bin[i] == d && !pick))) {
+            const uint32_t s = start[bin[i]] + idx[i];
+            sel[s] = key[i];
+            binof[s] = bin[i];
+        }
+    if (pick && threadIdx.x < count) {
+        const uint64_t x = list[threadIdx.x];
+        const uint32_t rk = count_above(list, (int)count, x);
+        if (rk < c.rem) {
+            sel[start[d] + rk] = x;
+            binof[start[d] + rk] = kPlaced;
+        }
+    }
+    __syncthreads();
+    return total < k ? (int)total : (int)k;
+}
+
 // LDS of the merge beyond the select's: the survivors, and the row's softmax statistics.
 struct MergeLds {
     uint64_t sel[DH_MAX_K];
@@ -503,84 +642,14 @@ __device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k,
         }
     }
     __syncthreads();
-    uint32_t n, bin[MPER];
-    const Cut cut = select_bins<MPER, NT>(key, (uint32_t)k, sh, n, bin);
-    const int kk = n < (uint32_t)k ? (int)n : k;
-
-    // the survivors, in any order, to sel[0..kk)
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < MPER; j++)
-        mine += survives(cut, key[j], bin[j]);
-    uint32_t at = wave_reserve(mine, &sh.fill);
-    if (mine) {
-#pragma unroll
-        for (int j = 0; j < MPER; j++)
-            if (survives(cut, key[j], bin[j]) && at < (uint32_t)kk)   // exactly kk survive
-                sel[at++] = key[j];
-    }
-    __syncthreads();
-
-    // slot of a survivor = the number of survivors that beat it (keys are distinct)
+    uint32_t bin[MPER];
+    Cut cut;
+    int kk = select_sorted<MPER, NT>(key, (uint32_t)k, sh, sel, cut, bin);
     int32_t *rid = ids + (int64_t)r * k;
     float *rval = vals + (int64_t)r * k;
     const int i = threadIdx.x;
-    uint32_t rank = 0;
-    uint64_t x = 0;
-    if (kk <= kCountMax) {
-        // few survivors: count directly
-        if (i < kk) {
-            x = sel[i];
-            rank = count_above(sel, kk, x);
-        }
-    } else {
-        // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then
-        // a survivor's rank is its place in its run plus, for each other run, the number of
-        // that run's keys above it (a binary search); the workgroup has a wave per run
-        const int nruns = (kk + 63) >> 6;
-        const int w = i >> 6, l = i & 63;
-        if (w < nruns) {
-            x = wave_sort_desc(i < kk ? sel[i] : 0ull, l);
-        }
-        __syncthreads();
-        if (w < nruns)
-            sel[i] = x;
-        __syncthreads();
-        if (w < nruns && x != 0) {
-            // the searches of all runs advance together (independent LDS reads per step);
-            // run q keeps run[0..lo) > x >= run[hi..64), and 7 halvings settle 64 keys
-            constexpr int kMaxRuns = DH_MAX_K / 64;
-            int lo[kMaxRuns], hi[kMaxRuns];
-#pragma unroll
-            for (int q = 0; q < kMaxRuns; q++) {
-                lo[q] = 0;
-                hi[q] = q < nruns && q != w ? 64 : 0;
-            }
-            // every run's probe is read each step, without a branch, so the step's eight LDS
-            // reads are in flight together (a settled or absent run reads a slot it ignores)
-#pragma unroll
-            for (int step = 0; step < 7; step++) {
-                int mid[kMaxRuns];
-                uint64_t y[kMaxRuns];
-#pragma unroll
-                for (int q = 0; q < kMaxRuns; q++) {
-                    mid[q] = (lo[q] + hi[q]) >> 1;
-                    y[q] = sel[64 * q + (mid[q] & 63)];
-                }
-#pragma unroll
-                for (int q = 0; q < kMaxRuns; q++) {
-                    const bool open = lo[q] < hi[q], above = y[q] > x;
-                    lo[q] = open && above ? mid[q] + 1 : lo[q];
-                    hi[q] = open && !above ? mid[q] : hi[q];
-                }
-            }
-            rank = (uint32_t)l;
-#pragma unroll
-            for (int q = 0; q < kMaxRuns; q++)
-                rank += (uint32_t)lo[q];
-        }
-    }
-    if (x != 0 && rank < (uint32_t)kk) {
+    // one survivor to its slot of the output
+    auto emit = [&](uint64_t x, uint32_t rank) {
         const uint32_t id = key_id(x);
         // a subset head's entry id is vocabulary id idmap[id]
         const int32_t out = idmap ? idmap[id] : (int32_t)id;
@@ -591,6 +660,104 @@ __device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k,
             probs[(int64_t)r * k + rank] = rel_exp(v, ml.row_m) / ml.row_z;
         if (rank == 0 && argmax)
             argmax[r] = out;
+    };
+
+    if (kk >= 0) {
+        // the survivors sit in their bins' slots: a key of the boundary bin is in its place,
+        // one of a bin above it adds the keys of its bin that beat it (keys are distinct)
+        if (i < kk) {
+            const uint64_t x = sel[i];
+            const uint32_t b = sh.hist[kBinOfOff + i];
+            uint32_t rank = (uint32_t)i;
+            if (b != kPlaced) {
+                const uint32_t s0 = sh.hist[kStartOff + b];
+                rank = s0 + count_above_at(sel, s0, sh.hist[b], x);
+            }
+            emit(x, rank);
+        }
+    } else {
+        // a crowded boundary bin (many equal or nearly equal values): the radix select among
+        // its keys, then the survivors ranked among themselves
+        kk = k;
+        __syncthreads();
+        for (int j = threadIdx.x; j < kHistWords; j += NT)
+            sh.hist[j] = 0;
+        __syncthreads();
+        uint32_t n2;
+        cut.P = select_top<MPER, NT>(key, cut.rem, sh, n2,
+                                     [&](int j) { return bin[j] == cut.d; });
+        // the survivors, in any order, to sel[0..kk)
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < MPER; j++)
+            mine += survives(cut, key[j], bin[j]);
+        uint32_t at = wave_reserve(mine, &sh.fill);
+        if (mine) {
+#pragma unroll
+            for (int j = 0; j < MPER; j++)
+                if (survives(cut, key[j], bin[j]) && at < (uint32_t)kk)   // exactly kk survive
+                    sel[at++] = key[j];
+        }
+        __syncthreads();
+
+        // slot of a survivor = the number of survivors that beat it (keys are distinct)
+        uint32_t rank = 0;
+        uint64_t x = 0;
+        if (kk <= kCountMax) {
+            // few survivors: count directly
+            if (i < kk) {
+                x = sel[i];
+                rank = count_above(sel, kk, x);
+            }
+        } else {
+            // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then
+            // a survivor's rank is its place in its run plus, for each other run, the number of
+            // that run's keys above it (a binary search); the workgroup has a wave per run
+            const int nruns = (kk + 63) >> 6;
+            const int w = i >> 6, l = i & 63;
+            if (w < nruns) {
+                x = wave_sort_desc(i < kk ? sel[i] : 0ull, l);
+            }
+            __syncthreads();
+            if (w < nruns)
+                sel[i] = x;
+            __syncthreads();
+            if (w < nruns && x != 0) {
+                // the searches of all runs advance together (independent LDS reads per step);
+                // run q keeps run[0..lo) > x >= run[hi..64), and 7 halvings settle 64 keys
+                constexpr int kMaxRuns = DH_MAX_K / 64;
+                int lo[kMaxRuns], hi[kMaxRuns];
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++) {
+                    lo[q] = 0;
+                    hi[q] = q < nruns && q != w ? 64 : 0;
+                }
+                // every run's probe is read each step, without a branch, so the step's eight LDS
+                // reads are in flight together (a settled or absent run reads a slot it ignores)
+#pragma unroll
+                for (int step = 0; step < 7; step++) {
+                    int mid[kMaxRuns];
+                    uint64_t y[kMaxRuns];
+#pragma unroll
+                    for (int q = 0; q < kMaxRuns; q++) {
+                        mid[q] = (lo[q] + hi[q]) >> 1;
+                        y[q] = sel[64 * q + (mid[q] & 63)];
+                    }
+#pragma unroll
+                    for (int q = 0; q < kMaxRuns; q++) {
+                        const bool open = lo[q] < hi[q], above = y[q] > x;
+                        lo[q] = open && above ? mid[q] + 1 : lo[q];
+                        hi[q] = open && !above ? mid[q] : hi[q];
+                    }
+                }
+                rank = (uint32_t)l;
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++)
+                    rank += (uint32_t)lo[q];
+            }
+        }
+        if (x != 0 && rank < (uint32_t)kk)
+            emit(x, rank);
     }
     for (int p = kk + i; p < k; p += NT) {
         rid[p] = 0;

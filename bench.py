@@ -140,9 +140,9 @@ def main():
                          "workload, the others the row-sweep workload's first rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["subset", "lowrank"],
-                    help="only the draft-vocabulary subset comparison or the low-rank "
-                         "two-stage head (for profiling)")
+    ap.add_argument("--only", choices=["subset", "lowrank", "twostage"],
+                    help="only the draft-vocabulary subset comparison, the low-rank "
+                         "two-stage head or the two-stage head (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the projection "
@@ -166,6 +166,13 @@ def main():
     if args.only == "lowrank":
         print(json.dumps({"lowrank_two_stage": lowrank_sweep(dh, torch, args.calls)}),
               flush=True)
+        return
+    if args.only == "twostage":
+        c = synth.CONFIGS["row_sweep"]
+        wd = torch.from_numpy(synth.head_bf16("row_sweep").view(np.int16)).to(dev)
+        xd = torch.from_numpy(synth.activations("row_sweep", 16).view(np.int16)).to(dev)
+        print(json.dumps({"two_stage": two_stage_sweep(dh, torch, wd, xd, c["V"], c["H"],
+                                                       args.calls)}), flush=True)
         return
     R = args.rows
     name = "fp8_block_1row" if R == 1 else "row_sweep"
@@ -411,31 +418,7 @@ def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
             log(f"{fmt} R={R}: gemv {g['median']:.1f} us, topk {t['median']:.1f} us, "
                 f"draft {d['median']:.1f} us (per-call events); back to back: "
                 f"gemv {bb['dh_gemv']:.1f}, topk {bb['dh_topk']:.1f}, draft {bb['dh_draft']:.1f}")
-    # two-stage: FP8 row-scaled stage 1 + dense bf16 rescore of 512 candidates, 16 rows
-    rc, rs = dh.quantize(wd, dh.FP8_ROW)
-    h1 = dh.tile(dh.Head(dh.FP8_ROW, rc, rs))
-    R, k = 16, 512
-    ws = dh.workspace(R, V, k)
-    o = {"ids": torch.empty((R, k), dtype=torch.int32, device=xd.device),
-         "vals": torch.empty((R, k), dtype=torch.float32, device=xd.device),
-         "draft": torch.empty((R,), dtype=torch.int32, device=xd.device),
-         "exact": torch.empty((R, k), dtype=torch.float32, device=xd.device)}
-    fd = lambda i: dh.draft(h1, xd, k, dense=dense[0], ws=ws, out=o)
-    d = stats_us(timed(fd, n))
-    dbb = back_to_back_us(fd, n)
-    lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
-    g = stats_us(timed(lambda i: dh.gemv(h1, xd, lg), n))
-    t = stats_us(timed(lambda i: dh.topk(lg, k, ws=ws, ids=o["ids"], vals=o["vals"]), n))
-    s = stats_us(timed(lambda i: dh.rescore(dense[0], xd, o["ids"], exact=o["exact"],
-                                            draft=o["draft"]), n))
-    # the same ids every call stay in the Infinity Cache; a cold gather rotates four sets of
-    # uniformly random candidate ids (4 x 84 MB of rows)
-    gen = torch.Generator(device=xd.device).manual_seed(404)
-    sets = [torch.randint(0, V, (R, k), dtype=torch.int32, device=xd.device, generator=gen)
-            for _ in range(4)]
-    s_cold = back_to_back_us(lambda i: dh.rescore(dense[0], xd, sets[i % 4], exact=o["exact"],
-                                                   draft=o["draft"]), n)
-    b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
+    res["two_stage"] = two_stage_sweep(dh, torch, wd, xd, V, H, n, dense[0])
     # the top-k with the softmax statistics (probabilities of the kept entries, each row's
     # log-sum-exp) against the plain top-k, on the FP8 head's 16-row logits, top-64
     lg16 = torch.empty((16, V), dtype=torch.float32, device=xd.device)
@@ -465,14 +448,45 @@ def sweep(dh, torch, rm_heads, wd, xd, V, H, K, n):
     log(f"keyed pick of 16 rows: {sm['dh_sample_k64_us']:.1f} us from 64 candidates, "
         f"{sm['dh_sample_k512_us']:.1f} us from 512 (host-launched back to back); in a graph "
         f"{sm['dh_sample_k64_graph_us']:.1f} and {sm['dh_sample_k512_graph_us']:.1f} us")
-    res["two_stage"] = {"rows": R, "cand_k": k, "dh_draft_us": d, "dh_gemv_us": g,
-                        "dh_topk_us": t, "dh_rescore_us": s, "dh_draft_back_to_back_us": dbb,
-                        "dh_rescore_rotated_ids_us": s_cold,
-                        "rescore_rotated_GBps": round(R * k * H * 2 / (s_cold * 1e-6) / 1e9, 1),
-                        "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
-    log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
-        f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f})")
     return res
+
+
+def two_stage_sweep(dh, torch, wd, xd, V, H, n, dense=None):
+    """The two-stage head of 16 rows: an FP8 row-scaled stage 1 (three tiled copies rotated,
+    as in the step), its top 512 candidates rescored from the dense bf16 head (wd), and each
+    part alone; the rescore also over rotated sets of random candidates (a cold gather)."""
+    dense = dense if dense is not None else dh.Head(dh.BF16, wd)
+    h1s = [dh.tile(dh.Head(dh.FP8_ROW, *dh.quantize(wd, dh.FP8_ROW))) for _ in range(NCOPY)]
+    R, k = 16, 512
+    ws = dh.workspace(R, V, k)
+    o = {"ids": torch.empty((R, k), dtype=torch.int32, device=xd.device),
+         "vals": torch.empty((R, k), dtype=torch.float32, device=xd.device),
+         "draft": torch.empty((R,), dtype=torch.int32, device=xd.device),
+         "exact": torch.empty((R, k), dtype=torch.float32, device=xd.device)}
+    fd = lambda i: dh.draft(h1s[i % NCOPY], xd, k, dense=dense, ws=ws, out=o)
+    d = stats_us(timed(fd, n))
+    dbb = back_to_back_us(fd, n)
+    lg = torch.empty((R, V), dtype=torch.float32, device=xd.device)
+    g = stats_us(timed(lambda i: dh.gemv(h1s[i % NCOPY], xd, lg), n))
+    t = stats_us(timed(lambda i: dh.topk(lg, k, ws=ws, ids=o["ids"], vals=o["vals"]), n))
+    s = stats_us(timed(lambda i: dh.rescore(dense, xd, o["ids"], exact=o["exact"],
+                                            draft=o["draft"]), n))
+    # the same ids every call stay in the Infinity Cache; a cold gather rotates four sets of
+    # uniformly random candidate ids (4 x 84 MB of rows)
+    gen = torch.Generator(device=xd.device).manual_seed(404)
+    sets = [torch.randint(0, V, (R, k), dtype=torch.int32, device=xd.device, generator=gen)
+            for _ in range(4)]
+    s_cold = back_to_back_us(lambda i: dh.rescore(dense, xd, sets[i % 4], exact=o["exact"],
+                                                   draft=o["draft"]), n)
+    b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
+    log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
+        f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f}); rescore over "
+        f"rotated random candidates {s_cold:.1f} us")
+    return {"rows": R, "cand_k": k, "stage1_copies_rotated": NCOPY, "dh_draft_us": d,
+            "dh_gemv_us": g, "dh_topk_us": t, "dh_rescore_us": s,
+            "dh_draft_back_to_back_us": dbb, "dh_rescore_rotated_ids_us": s_cold,
+            "rescore_rotated_GBps": round(R * k * H * 2 / (s_cold * 1e-6) / 1e9, 1),
+            "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
 
 
 def edge_shape(dh, torch, n):

@@ -459,13 +459,15 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     // the GEMV zeroes the top-k's tickets, so the top-k is one launch
     if (e == hipSuccess)
         e = dh::launch_gemv(*head, down ? t : x, rows, L, st,
-                            dh::topk_tickets(workspace, rows, head->vocab, k), rows,
-                            dh::kTicketStride);
+                            dh::topk_tickets(workspace, rows, head->vocab, k),
+                            dh::kSyncKinds * rows, dh::kTicketStride);
     if (e == hipSuccess)
         e = dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals, dense ? nullptr : draft,
                             workspace, st, nullptr, nullptr, true);
-    if (e == hipSuccess && dense)
-        e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st);
+    if (e == hipSuccess && dense)   // its sync lines were zeroed by the GEMV as well
+        e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st,
+                               dh::topk_tickets(workspace, rows, head->vocab, k) +
+                                   (size_t)rows * dh::kTicketStride);
     return device_status(e);
 }
 

@@ -17,8 +17,8 @@ constexpr int kWave = 64;
 
 // Launchers: argument checking has been done by the caller (api.hip).  Each returns the
 // hipError_t of its launches.
-// zero, nzero, zstride: up to 64 words, zstride words apart, that the kernel sets to zero
-// (the tickets of the top-k that follows it on the stream), or NULL.
+// zero, nzero, zstride: nzero pairs of words, zstride words apart, that the kernel sets to
+// zero (the sync lines of the kernels that follow it on the stream), or NULL.
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream, uint32_t *zero = nullptr, int nzero = 0,
                        int zstride = 1);
@@ -31,9 +31,13 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
                          uint32_t *zero = nullptr, int nzero = 0, int zstride = 1);
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
 
+// sync: NULL (a second kernel picks the drafts), or the rescore's zeroed sync lines in a
+// top-k workspace (ticket lines, then best-key lines, `rows` of each, kTicketStride words
+// apart): the candidates' last workgroup of a row picks its draft.
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,
-                          float *exact, int32_t *draft, hipStream_t stream);
+                          float *exact, int32_t *draft, hipStream_t stream,
+                          uint32_t *sync = nullptr);
 hipError_t launch_gather_rows(const dh_head &head, const int32_t *ids, int64_t n, void *weight,
                               float *scale, hipStream_t stream);
 hipError_t launch_sample(const int32_t *ids, const float *vals, int rows, int k, double T,

@@ -77,7 +77,7 @@ struct GemvArgs {
     int ntiles;
     int nkb;                // number of 64-column blocks, ceil(H / 64)
     int tile_bytes;         // tiled layout: bytes of one 16-row tile, nkb * 1024 * (bytes/weight)
-    uint32_t *zero;         // nzero (<= 64) words, zstride apart, the first workgroup zeroes
+    uint32_t *zero;         // nzero pairs of words, zstride apart, the first workgroup zeroes
     int nzero, zstride;
 };
 
@@ -168,8 +168,11 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     const int nvw = (a.nkb + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
-    if (blockIdx.x == 0 && (int)threadIdx.x < a.nzero)
-        a.zero[threadIdx.x * a.zstride] = 0u;  // for the kernel that follows on the stream
+    if (blockIdx.x == 0)                       // for the kernels that follow on the stream
+        for (int i = threadIdx.x; i < a.nzero; i += blockDim.x) {
+            a.zero[i * a.zstride] = 0u;
+            a.zero[i * a.zstride + 1] = 0u;
+        }
     const int rr = lane & 15;
     const int g = lane >> 4;
     const int H = a.H;

@@ -6,13 +6,19 @@
 //
 // Design: the work is a gather of rows*cand_k head rows (10 KB each at H = 5120) -- memory
 // bound, with one activation row per gathered head row, so plain FP32 FMAs on the vector
-// ALUs.  One wave per (row, slot): each lane reads 16 bytes of the head row and of the
-// activation row per step (a wave covers 1 KB of the head row per load), with five steps
-// in flight before any is summed, sums its products in order, and the wave sums lanes with
-// a fixed butterfly.  A second small kernel picks
-// each row's winner under the same ordering as the top-k.
+// ALUs.  One wave per (row, slot), four waves a workgroup, all of one activation row: the
+// workgroup stages that row in LDS once (every wave reading it from L2 doubled the cache
+// traffic of the gather), while each wave's first round of head-row loads is already in
+// flight.  Each lane reads 16 bytes of the head row per step (a wave covers 1 KB of the row
+// per load), with five steps in flight, sums its products in order, and the wave sums lanes
+// with a fixed butterfly.  The winning candidate is picked either by a second small kernel,
+// or -- inside dh_draft, which has a workspace -- by the candidates' workgroups themselves:
+// each takes the 64-bit maximum of its candidates' (exact logit, token id) keys into the
+// row's best word, then a ticket, and the row's last workgroup writes the draft.
 #include "dh_internal.h"
+#include "keys.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace dh {
 namespace {
@@ -30,56 +36,110 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(
-    const uint16_t *W, int64_t V, int H, const uint16_t *x, const int32_t *cand,
-    const float *cand_vals, int ck, float *exact)
+struct RescoreArgs {
+    const uint16_t *W;      // dense bf16 head [V][H]
+    int64_t V;
+    int H;
+    const uint16_t *x;      // bf16 [rows][H]
+    const int32_t *cand;    // [rows][ck]
+    const float *cand_vals; // stage-1 values [rows][ck], or NULL
+    int ck;
+    float *exact;           // [rows][ck]
+    // PICK: the zeroed ticket lines and best-key lines of the rows (kTicketStride words
+    // apart), and the drafts [rows]
+    uint32_t *tickets;
+    uint64_t *best;
+    int32_t *draft;
+};
+
+// exact[r][slot] for one slot a wave; PICK: and the row's draft (see above).
+template <bool PICK>
+__global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(RescoreArgs a)
 {
-    const int lane = threadIdx.x & 63;
-    const int slot = blockIdx.x * kRescoreWaves + (threadIdx.x >> 6);
+    __shared__ __align__(16) uint16_t xs[DH_MAX_HIDDEN];
+    __shared__ uint64_t wbest[kRescoreWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = blockIdx.x * kRescoreWaves + wave;
     const int r = blockIdx.y;
-    if (slot >= ck)
-        return;
-    const int64_t t = (int64_t)r * ck + slot;
-    const int64_t id = cand[t];
-    float out;
-    if (cand_vals && !(cand_vals[t] > -__builtin_inff())) {
-        out = -__builtin_inff();          // a pad of the stage-1 list: not a candidate
-    } else if (id < 0 || id >= V) {
-        out = __builtin_nanf("");         // not a token of this head: never read
-    } else {
-        // bounded buffer loads (bytes past the row read as 0, adding nothing), kSteps steps of
-        // 512 columns issued before any is used
-        const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(W + id * H), (short)0, H * 2, kRsrcWord3);
-        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(x + (int64_t)r * H), (short)0, H * 2, kRsrcWord3);
-        float acc = 0.f;
-        for (int h0 = 0; h0 < H; h0 += kSteps * 8 * kWave) {
-            u32x4 wq[kSteps], xq[kSteps];
+    const int H = a.H;
+    const int64_t t = (int64_t)r * a.ck + slot;
+    const bool live = slot < a.ck;
+    const int64_t id = live ? a.cand[t] : -1;
+    // a pad of the stage-1 list is not a candidate; an id outside the head is not read
+    const bool pad = live && a.cand_vals && !(a.cand_vals[t] > -__builtin_inff());
+    const bool read = live && !pad && id >= 0 && id < a.V;
+
+    // bounded buffer loads (bytes past the row read as 0, adding nothing), kSteps steps of
+    // 512 columns a round; the first round is issued before the activations are staged
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.W + (read ? id : 0) * H), (short)0, read ? H * 2 : 0, kRsrcWord3);
+    u32x4 wq[kSteps];
+    auto issue = [&](int h0) {
 #pragma unroll
-            for (int j = 0; j < kSteps; j++) {
-                const uint32_t off = (uint32_t)(h0 + j * 8 * kWave + lane * 8) * 2u;
-                wq[j] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0);
-                xq[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
-            }
+        for (int j = 0; j < kSteps; j++)
+            wq[j] = __builtin_amdgcn_raw_buffer_load_b128(
+                wrs, (uint32_t)(h0 + j * 8 * kWave + lane * 8) * 2u, 0, 0);
+    };
+    issue(0);
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(a.x + (int64_t)r * H);
+    for (int i = threadIdx.x; i < H / 8; i += kRescoreWaves * kWave)
+        reinterpret_cast<u32x4 *>(xs)[i] = xg[i];
+    __syncthreads();
+
+    float acc = 0.f;
+    constexpr int kRound = kSteps * 8 * kWave;
+    for (int h0 = 0; h0 < H; h0 += kRound) {
+        u32x4 cur[kSteps];
 #pragma unroll
-            for (int j = 0; j < kSteps; j++) {
-                acc = __builtin_fmaf(lo_bf16(xq[j].x), lo_bf16(wq[j].x), acc);
-                acc = __builtin_fmaf(hi_bf16(xq[j].x), hi_bf16(wq[j].x), acc);
-                acc = __builtin_fmaf(lo_bf16(xq[j].y), lo_bf16(wq[j].y), acc);
-                acc = __builtin_fmaf(hi_bf16(xq[j].y), hi_bf16(wq[j].y), acc);
-                acc = __builtin_fmaf(lo_bf16(xq[j].z), lo_bf16(wq[j].z), acc);
-                acc = __builtin_fmaf(hi_bf16(xq[j].z), hi_bf16(wq[j].z), acc);
-                acc = __builtin_fmaf(lo_bf16(xq[j].w), lo_bf16(wq[j].w), acc);
-                acc = __builtin_fmaf(hi_bf16(xq[j].w), hi_bf16(wq[j].w), acc);
+        for (int j = 0; j < kSteps; j++)
+            cur[j] = wq[j];
+        if (h0 + kRound < H)
+            issue(h0 + kRound);          // the next round in flight while this one is summed
+#pragma unroll
+        for (int j = 0; j < kSteps; j++) {
+            const int c = h0 + j * 8 * kWave + lane * 8;
+            const u32x4 xq = c < H ? *reinterpret_cast<const u32x4 *>(&xs[c])
+                                   : u32x4{0u, 0u, 0u, 0u};
+            acc = __builtin_fmaf(lo_bf16(xq.x), lo_bf16(cur[j].x), acc);
+            acc = __builtin_fmaf(hi_bf16(xq.x), hi_bf16(cur[j].x), acc);
+            acc = __builtin_fmaf(lo_bf16(xq.y), lo_bf16(cur[j].y), acc);
+            acc = __builtin_fmaf(hi_bf16(xq.y), hi_bf16(cur[j].y), acc);
+            acc = __builtin_fmaf(lo_bf16(xq.z), lo_bf16(cur[j].z), acc);
+            acc = __builtin_fmaf(hi_bf16(xq.z), hi_bf16(cur[j].z), acc);
+            acc = __builtin_fmaf(lo_bf16(xq.w), lo_bf16(cur[j].w), acc);
+            acc = __builtin_fmaf(hi_bf16(xq.w), hi_bf16(cur[j].w), acc);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1)
+        acc += __shfl_xor(acc, off);
+    const float out = pad ? -__builtin_inff() : read ? acc : __builtin_nanf("");
+    if (live && lane == 0)
+        a.exact[t] = out;
+    if constexpr (PICK) {
+        // the workgroup's best (exact, token id) key; 0 when none of its candidates is
+        // eligible (NaN, -inf, or no slot)
+        if (lane == 0) {
+            const uint32_t im = live ? order_key(out) : 0u;
+            wbest[wave] = im ? entry_key(im, (uint32_t)id) : 0ull;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t m = 0;
+#pragma unroll
+            for (int w = 0; w < kRescoreWaves; w++)
+                m = wbest[w] > m ? wbest[w] : m;
+            uint64_t *bw = a.best + (int64_t)r * (kTicketStride / 2);
+            if (m != 0)
+                atomicMax((unsigned long long *)bw, (unsigned long long)m);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the maximum is in place
+            const uint32_t nb = (uint32_t)gridDim.x;   // the row's workgroups
+            if (atomicAdd(&a.tickets[(int64_t)r * kTicketStride], 1u) == nb - 1u) {
+                const uint64_t b = __hip_atomic_load(bw, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                a.draft[r] = b ? (int32_t)key_id(b) : 0;
             }
         }
-        for (int off = 32; off > 0; off >>= 1)
-            acc += __shfl_xor(acc, off);
-        out = acc;
     }
-    if (lane == 0)
-        exact[t] = out;
 }
 
 __device__ inline bool eligible(float l) { return l == l && l > -__builtin_inff(); }
@@ -142,12 +202,24 @@ __global__ __launch_bounds__(kPickThreads) void rescore_pick(const float *exact,
 
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,
-                          float *exact, int32_t *draft, hipStream_t stream)
+                          float *exact, int32_t *draft, hipStream_t stream, uint32_t *sync)
 {
+    RescoreArgs a;
+    a.W = static_cast<const uint16_t *>(dense.weight);
+    a.V = dense.vocab;
+    a.H = (int)dense.hidden;
+    a.x = x;
+    a.cand = cand_ids;
+    a.cand_vals = cand_vals;
+    a.ck = cand_k;
+    a.exact = exact;
+    a.tickets = sync;
+    a.best = sync ? reinterpret_cast<uint64_t *>(sync + (size_t)rows * kTicketStride) : nullptr;
+    a.draft = draft;
     const dim3 grid((cand_k + kRescoreWaves - 1) / kRescoreWaves, rows);
-    hipError_t e = launch(rescore_dot, grid, dim3(kRescoreWaves * kWave), 0, stream,
-                          static_cast<const uint16_t *>(dense.weight), (int64_t)dense.vocab,
-                          (int)dense.hidden, x, cand_ids, cand_vals, cand_k, exact);
+    if (sync)
+        return launch(rescore_dot<true>, grid, dim3(kRescoreWaves * kWave), 0, stream, a);
+    hipError_t e = launch(rescore_dot<false>, grid, dim3(kRescoreWaves * kWave), 0, stream, a);
     if (e != hipSuccess)
         return e;
     return launch(rescore_pick, dim3(rows), dim3(kPickThreads), 0, stream, (const float *)exact,

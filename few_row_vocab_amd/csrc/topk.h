@@ -41,11 +41,15 @@ inline TopkShape topk_shape(int rows, int64_t vocab, int k)
 
 // Workspace layout of the top-k (offsets in bytes, each 256-byte aligned): the chunk lists
 // of 64-bit keys, [rows][chunks][k]; the chunks' softmax statistics [rows][chunks] (float2:
-// the largest eligible logit and the sum of exp(l - it)); one 32-bit ticket a row, counting
-// the row's chunks that are done (zero when the top-k starts), each in a 256-byte line of its
-// own (rows sharing a line serialize their workgroups' atomics: measured up to 8 us at 16
-// rows).
-constexpr int kTicketStride = 64;    // words from one row's ticket to the next
+// the largest eligible logit and the sum of exp(l - it)); then the sync lines, kSyncKinds
+// 256-byte lines a row ([kind][row]), each zero when its kernel starts:
+//   kind 0: the top-k's ticket (the row's chunks that are done);
+//   kind 1: the draft's rescore ticket (the row's candidate workgroups that are done);
+//   kind 2: the rescore's best 64-bit key of the row so far.
+// Each in a line of its own: rows sharing a line serialize their workgroups' atomics
+// (measured up to 8 us at 16 rows).
+constexpr int kTicketStride = 64;    // words from one sync line to the next
+constexpr int kSyncKinds = 3;
 struct TopkWs {
     size_t keys_off, stats_off, tickets_off, bytes;
 };
@@ -61,8 +65,8 @@ hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        void *ws, hipStream_t stream, float *probs = nullptr,
                        float *lse = nullptr, bool tickets_zeroed = false);
 
-// The tickets of a top-k workspace (rows of them, kTicketStride words apart), for the GEMV to
-// zero.
+// The sync lines of a workspace (kSyncKinds * rows of them, kTicketStride words apart), for
+// the GEMV to zero (two words of each).
 uint32_t *topk_tickets(void *ws, int rows, int64_t vocab, int k);
 
 }  // namespace dh

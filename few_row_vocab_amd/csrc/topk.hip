@@ -824,7 +824,7 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
     w.keys_off = 0;   // the chunk lists hold keys that carry both the value and the id
     w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
     w.tickets_off = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
-    w.bytes = w.tickets_off + up((size_t)rows * kTicketStride * sizeof(uint32_t));
+    w.bytes = w.tickets_off + up((size_t)kSyncKinds * rows * kTicketStride * sizeof(uint32_t));
     return w;
 }
 

@@ -649,7 +649,9 @@ def cpu_baseline(w, x, V, H, R, K):
         pass
     log(f"cpu oracle: full step {dt:.2f}s median of {len(times)} on {nt} threads; "
         f"1 thread: {S} vocab rows in {d1:.2f}s ({cpu})")
+    wider = cpu_baseline_wider(oracle, nt)
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": nt, "cpu": cpu,
+            "rows16": wider["rows16"], "two_stage": wider["two_stage"],
             "kind": "oracle", "seconds_per_step": round(dt, 3), "steps": len(times),
             "quantize_seconds": round(tq, 3),
             "single_thread": {"value": round(b1 / d1 / 1e9, 4), "unit": "GB/s",
@@ -658,6 +660,40 @@ def cpu_baseline(w, x, V, H, R, K):
             "sample": f"the full step (GEMV over all {V} vocabulary rows of the FP8 block "
                       f"head for {R} activation row(s), then top-{K}), {len(times)} times, median; GB/s "
                       f"over the step's algorithmic bytes"}
+
+
+def cpu_baseline_wider(oracle, nt):
+    """The oracle once each on the row-sweep workload's head (H=5120, V=129280) at 16 rows:
+    the 16-row step (FP8 32x32 block head, GEMV then top-64 and argmax) and the two-stage
+    draft (FP8 row-scaled stage 1, top 512, rescore from the dense bf16 head).  Quantization
+    is the oracle's own and is not timed."""
+    import synth
+    name = "row_sweep"
+    c = synth.CONFIGS[name]
+    V, H, R = c["V"], c["H"], 16
+    w = synth.head_bf16(name)
+    x = synth.activations(name, R)
+    codes, scales = oracle.quant_block32(w)
+    t0 = time.time()
+    oracle.draft(oracle.FMT_FP8_BLOCK32, codes, scales, x, 64)
+    d16 = time.time() - t0
+    del codes, scales
+    rc, rs = oracle.quant_row(w)
+    t0 = time.time()
+    oracle.draft(oracle.FMT_FP8_ROW, rc, rs, x, 512, dense_w=w)
+    d2 = time.time() - t0
+    b16 = algorithmic_bytes("fp8_block32", V, H, R)
+    b2 = algorithmic_bytes("fp8_row", V, H, R) + R * 512 * H * 2
+    log(f"cpu oracle: 16-row step {d16:.2f}s, two-stage draft {d2:.2f}s on {nt} threads")
+    return {"rows16": {"seconds": round(d16, 3), "value": round(b16 / d16 / 1e9, 4),
+                       "unit": "GB/s", "cores": nt, "kind": "oracle",
+                       "sample": f"one dh_draft-equivalent call: {R} activation rows, FP8 "
+                                 f"32x32 block head H={H} V={V}, GEMV then top-64 and argmax"},
+            "two_stage": {"seconds": round(d2, 3), "value": round(b2 / d2 / 1e9, 4),
+                          "unit": "GB/s", "cores": nt, "kind": "oracle",
+                          "sample": f"one two-stage draft: {R} rows, FP8 row-scaled stage 1 "
+                                    f"H={H} V={V}, top 512, rescore from the dense bf16 head "
+                                    f"(GB/s over the upper-bound bytes)"}}
 
 
 if __name__ == "__main__":

@@ -140,7 +140,7 @@ def main():
                          "workload, the others the row-sweep workload's first rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["subset", "lowrank", "twostage"],
+    ap.add_argument("--only", choices=["subset", "lowrank", "twostage", "widelinear"],
                     help="only the draft-vocabulary subset comparison, the low-rank "
                          "two-stage head or the two-stage head (for profiling)")
     args = ap.parse_args()
@@ -166,6 +166,9 @@ def main():
     if args.only == "lowrank":
         print(json.dumps({"lowrank_two_stage": lowrank_sweep(dh, torch, args.calls)}),
               flush=True)
+        return
+    if args.only == "widelinear":
+        print(json.dumps({"wide_linear": wide_linear(dh, torch, args.calls)}), flush=True)
         return
     if args.only == "twostage":
         c = synth.CONFIGS["row_sweep"]
@@ -320,6 +323,7 @@ def main():
         torch.cuda.empty_cache()
         out["edge_shape"] = edge_shape(dh, torch, args.calls)
         out["subset_head"] = subset_sweep(dh, torch, args.calls)
+        out["wide_linear"] = wide_linear(dh, torch, args.calls)
         out["lowrank_two_stage"] = lowrank_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
     print(json.dumps(out), flush=True)
@@ -519,6 +523,38 @@ def edge_shape(dh, torch, n):
         log(f"edge shape R={R}: gemv {tg:.1f} us ({b / (tg * 1e-6) / 1e9:.0f} GB/s), "
             f"draft top-512 {td:.1f} us")
     del heads
+    torch.cuda.empty_cache()
+    return res
+
+
+def wide_linear(dh, torch, n):
+    """One of the head's own linears with a wide input, like a w2 whose input is the FFN width:
+    N=5120 outputs, K=18432 inputs, FP8 E4M3 with a row scale (tiled), fp32 and bf16-add
+    outputs, 1 and 16 rows, back to back over three rotated weight copies (device-generated
+    N(0, 0.02) weights; timing only, its parity is a test).  The GEMV streams the 18432 columns
+    in chunks of 8192."""
+    N, K = 5120, 18432
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(808)
+    ws = []
+    for _ in range(NCOPY):
+        w = (torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        ws.append(dh.tile(dh.Head(dh.FP8_ROW, *dh.quantize(w, dh.FP8_ROW))))
+        del w
+    res = {"workload": f"linear N={N} K={K}, FP8 E4M3 with a row scale, tiled", "rows": []}
+    for R in (1, 16):
+        x = torch.randn((R, K), device=dev, generator=g).to(torch.bfloat16)
+        out = torch.empty((R, N), dtype=torch.float32, device=dev)
+        r16 = torch.zeros((R, N), dtype=torch.bfloat16, device=dev)
+        tf = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_F32, out=out), n)
+        ta = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_ADD_BF16,
+                                                 residual=r16, out=r16), n)
+        b = N * K + N * 4 + R * K * 2 + R * N * 4
+        res["rows"].append({"rows": R, "f32_us": tf, "f32_GBps": round(b / (tf * 1e-6) / 1e9, 1),
+                            "add_bf16_us": ta, "frac_of_8TBps": round(b / (tf * 1e-6) / 8e12, 4)})
+        log(f"wide linear R={R}: f32 {tf:.1f} us ({b / (tf * 1e-6) / 1e9:.0f} GB/s), "
+            f"bf16 add {ta:.1f} us")
+    del ws
     torch.cuda.empty_cache()
     return res
 

@@ -594,7 +594,7 @@ const char *dh_status_string(int32_t status)
     case DH_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad format, "
                                 "bad size, or overlapping buffers)";
     case DH_ERR_UNSUPPORTED: return "size outside the implemented limits (rows <= 32, "
-                                    "k <= 512, hidden <= 8192, vocab <= 262144)";
+                                    "k <= 512, hidden <= 32768, vocab <= 262144)";
     case DH_ERR_WORKSPACE: return "workspace missing, misaligned or too small "
                                   "(see dh_workspace_bytes)";
     case DH_ERR_DEVICE: return "the HIP runtime reported an error at launch";

@@ -60,6 +60,12 @@ constexpr int kCacheNT = 2;              // gfx950 cache policy bit 1: non-tempo
 template <int FMT>
 constexpr int tiled_ahead_kib() { return FMT == DH_BF16 ? 48 : 32; }
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
+// Heads wider than 16 waves of 8 blocks (H > 8192) are streamed in column chunks of 16 * 8
+// 64-column blocks (CH below): a wave holds one chunk's activations at a time.  Both layouts
+// take the same chunks and the same 16 virtual waves (so they keep giving the same bits); a
+// row-major chunked launch runs 8 waves of two virtual waves (256 VGPRs) and keeps 4 blocks
+// of loads in flight, as 16 waves with a tile in flight spill registers.
+constexpr int kChunkKbw = 8;
 constexpr int kMaxDevices = 64;
 
 struct GemvArgs {
@@ -145,11 +151,16 @@ __device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
 // waves of KBW blocks each); a wave covers VW of them with a sum apiece, and the reduction
 // adds the virtual waves' sums in order, so VW changes neither a result nor its bits -- only
 // how many waves share the work (VW = 2: 8 waves of up to 256 VGPRs).
+// CH: the head is streamed in column chunks of 16 * KBW blocks (for H > 8192, whose
+// activations do not fit the waves' registers at once): for each chunk the waves load that
+// chunk's activations, every tile of the block streams that chunk of its rows, and the
+// tile's reduced sums are added to its running sums in LDS, chunk after chunk (so a row's
+// sums still do not depend on how many rows share the call).
 // TL: the head is tiled (DH_TILED): a tile's 64-column block is RQ KiB in which lane l's
 // 16 bytes sit at 16 l, so a wave's load reads 1 KiB of whole lines, with the non-temporal
 // hint; rows past V and columns past H are zeros in the tiled copy.  The lanes receive the
 // same bytes as from the row-major head, so the sums and their bits are the same.
-template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL>
+template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false>
 __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(GemvArgs a)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
@@ -160,14 +171,14 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // blocks a wave keeps in flight: a whole tile (row-major heads), or a window sized so a
     // full workgroup (16 / VW waves) holds about tiled_ahead_kib (tiled heads)
     constexpr int AHW = tiled_ahead_kib<FMT>() * VW / (kMaxWaves * RQ);
-    constexpr int AH = !TL ? KW : AHW < 1 ? 1 : AHW > KW ? KW : AHW;
+    constexpr int AH = !TL ? (CH ? 4 : KW) : AHW < 1 ? 1 : AHW > KW ? KW : AHW;
     __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
     extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
 
+    static_assert(!CH || !FULL, "a chunked launch guards its loads");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
-    const int nvw = (a.nkb + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
     if (blockIdx.x == 0)                       // for the kernels that follow on the stream
         for (int i = threadIdx.x; i < a.nzero; i += blockDim.x) {
             a.zero[i * a.zstride] = 0u;
@@ -177,6 +188,13 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int g = lane >> 4;
     const int H = a.H;
     const int64_t V = a.V;
+    constexpr int CB = kMaxWaves * KBW;          // CH: blocks a chunk
+    const int nch = CH ? (a.nkb + CB - 1) / CB : 1;
+    int it = 0, buf = 0;
+    for (int ch = 0; ch < nch; ch++) {
+    const int cb = CH ? ch * CB : 0;            // the chunk's first 64-column block
+    const int nkbc = CH ? (a.nkb - cb < CB ? a.nkb - cb : CB) : a.nkb;
+    const int nvw = (nkbc + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
 
     // This wave's H-slice of the activations: the B operands of every tile.
     bf16x8 xb[NB][KW][2];
@@ -190,8 +208,9 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             Pack8 p0, p1;
             p0.q = u32x4{0u, 0u, 0u, 0u};
             p1.q = u32x4{0u, 0u, 0u, 0u};
-            if (row < a.R && (FULL || (blk < a.nkb && k0 < H))) {
-                const u32x4 *px = reinterpret_cast<const u32x4 *>(a.x + (int64_t)row * H + k0);
+            if (row < a.R && (FULL || (blk < nkbc && cb * 64 + k0 < H))) {
+                const u32x4 *px =
+                    reinterpret_cast<const u32x4 *>(a.x + (int64_t)row * H + cb * 64 + k0);
                 p0.q = px[0];
                 p1.q = px[1];
             }
@@ -211,13 +230,16 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // a branch, so the wait before each block is a fixed count of younger loads.
     static_assert(!TL || TR == 1, "a tiled tile is one 16-row group");
     const uint32_t wrow = (uint32_t)H * ES;
-    const uint32_t woff = TL ? (uint32_t)(16 * lane + wave * KW * RQ * 1024)
-                             : (uint32_t)rr * wrow + (uint32_t)(wave * KW * 64 + 16 * g) * ES;
-    const uint32_t sbase = (uint32_t)(2 * wave * KW);
+    const uint32_t woff =
+        TL ? (uint32_t)(16 * lane + (cb + wave * KW) * RQ * 1024)
+           : (uint32_t)rr * wrow + (uint32_t)((cb + wave * KW) * 64 + 16 * g) * ES;
+    const uint32_t sbase = (uint32_t)(2 * (cb + wave * KW));
     auto load_block = [&](const __amdgpu_buffer_rsrc_t (&wr)[TR], int kb) {
         const int blk = wave * KW + kb;
-        // tiled: blocks past the tile read as zeros through the descriptor's bound
-        if (FULL || TL || (blk < a.nkb && blk * 64 + 16 * g < H)) {
+        // tiled: blocks past the tile read as zeros through the descriptor's bound (a chunk
+        // guards the blocks past its own end, which belong to the next chunk)
+        if (FULL || (TL && !CH) ||
+            (blk < nkbc && (TL || (cb + blk) * 64 + 16 * g < H))) {
 #pragma unroll
             for (int r = 0; r < TR; r++)
 #pragma unroll
@@ -266,7 +288,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
                                                kRsrcWord3);
     };
 
-    int tile = blockIdx.x;   // the launch keeps gridDim.x <= ntiles
+    int tile = blockIdx.x;   // the launch keeps gridDim.x <= ntiles (the same tiles each chunk)
     uint32_t sbytes;
     __amdgpu_buffer_rsrc_t wcur[TR];             // this tile's descriptors
     {
@@ -277,8 +299,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
         for (int kb = 0; kb < AH; kb++)
             load_block(wcur, kb);
     }
-    int buf = 0, it = 0;
-    for (;; it++) {
+    for (it = 0;; it++) {
         const int next = tile + gridDim.x;
         const bool more = next < a.ntiles;
         __amdgpu_buffer_rsrc_t wr[TR], sr;       // the next tile's descriptors
@@ -358,6 +379,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             float s = 0.f;
             for (int w = 0; w < nvw; w++)
                 s += red[buf][w][c >> 4][j][src];
+            if (CH && ch > 0)
+                s = stage[it * OUTS + o] + s;     // the earlier chunks' sums, then this one's
             stage[it * OUTS + o] = s;
         }
         buf ^= 1;
@@ -369,6 +392,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
         for (int r = 0; r < TR; r++)
             wcur[r] = wr[r];
     }
+    }   // chunks
     __syncthreads();
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave
     // w writes tiles w, w + nw, ...; a lane takes (activation row c, head row i) pairs.
@@ -501,14 +525,15 @@ __global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const fl
     write_out(a, c, v, s);
 }
 
-template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL>
+template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false>
 hipError_t run(GemvArgs a, hipStream_t stream)
 {
     static int occ_cache[kMaxWaves + 1];
     static int lds_set[kMaxDevices];               // per device: the LDS limit has been raised
-    const int nw = (a.nkb + VW * KBW - 1) / (VW * KBW);
+    const int nkb = CH && a.nkb > kMaxWaves * KBW ? kMaxWaves * KBW : a.nkb;   // blocks a pass
+    const int nw = (nkb + VW * KBW - 1) / (VW * KBW);
     const int block = nw * kWave;
-    auto kern = gemv_kernel<FMT, KBW, FULL, TR, NB, VW, TL>;
+    auto kern = gemv_kernel<FMT, KBW, FULL, TR, NB, VW, TL, CH>;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -593,7 +618,11 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
     case 6: return run_kbw<FMT, 6, 1, 1, TL>(a, stream);
     case 7: return run_kbw<FMT, 7, 1, 1, TL>(a, stream);
     case 8: return run_kbw<FMT, 8, 1, 1, TL>(a, stream);
-    default: return hipErrorInvalidValue;
+    default:   // H > 8192: column chunks
+        if constexpr (TL)
+            return run<FMT, kChunkKbw, false, 1, 1, 1, true, true>(a, stream);
+        else
+            return run<FMT, kChunkKbw, false, 1, 1, 2, false, true>(a, stream);
     }
 }
 

@@ -56,7 +56,7 @@ struct RescoreArgs {
 template <bool PICK>
 __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(RescoreArgs a)
 {
-    __shared__ __align__(16) uint16_t xs[DH_MAX_HIDDEN];
+    extern __shared__ __align__(16) uint16_t xs[];   // the activation row, H of them
     __shared__ uint64_t wbest[kRescoreWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = blockIdx.x * kRescoreWaves + wave;
@@ -217,9 +217,26 @@ hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
     a.best = sync ? reinterpret_cast<uint64_t *>(sync + (size_t)rows * kTicketStride) : nullptr;
     a.draft = draft;
     const dim3 grid((cand_k + kRescoreWaves - 1) / kRescoreWaves, rows);
+    const size_t lds = (size_t)a.H * sizeof(uint16_t);   // up to 64 KiB (H <= 32768)
+    static int lds_set[64];                              // per device: the limit raised
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    if (!__atomic_load_n(&lds_set[dev], __ATOMIC_RELAXED)) {
+        for (const void *k : {(const void *)rescore_dot<true>, (const void *)rescore_dot<false>}) {
+            e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    DH_MAX_HIDDEN * (int)sizeof(uint16_t));
+            if (e != hipSuccess)
+                return e;
+        }
+        __atomic_store_n(&lds_set[dev], 1, __ATOMIC_RELAXED);
+    }
     if (sync)
-        return launch(rescore_dot<true>, grid, dim3(kRescoreWaves * kWave), 0, stream, a);
-    hipError_t e = launch(rescore_dot<false>, grid, dim3(kRescoreWaves * kWave), 0, stream, a);
+        return launch(rescore_dot<true>, grid, dim3(kRescoreWaves * kWave), lds, stream, a);
+    e = launch(rescore_dot<false>, grid, dim3(kRescoreWaves * kWave), lds, stream, a);
     if (e != hipSuccess)
         return e;
     return launch(rescore_pick, dim3(rows), dim3(kPickThreads), 0, stream, (const float *)exact,

@@ -28,7 +28,7 @@ OUT_ADD_BF16 = 2
 MAX_ROWS = 32
 MAX_HIDDEN_WIDE = 5120   # 4096 for a row-major bf16 head
 MAX_K = 512
-MAX_HIDDEN = 8192
+MAX_HIDDEN = 32768
 MAX_VOCAB = 262144
 
 STATUS = {0: "DH_OK", 1: "DH_ERR_INVALID", 2: "DH_ERR_UNSUPPORTED", 3: "DH_ERR_WORKSPACE",

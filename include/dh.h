@@ -93,11 +93,13 @@ typedef struct dh_head {
  * bits as the 16-row form.  Up to H = DH_MAX_HIDDEN_WIDE (4096 for a row-major bf16 head)
  * such a call reads the head once (32 rows of activations held in registers); a wider head is
  * read once per 16 rows.
- * k: [TFE] 'Update' -- the candidate count runs from 1 to 512. */
+ * k: [TFE] 'Update' -- the candidate count runs from 1 to 512.
+ * H: [TFE] commit notes -- the head's own linears (wo, w2) go through the same few-row GEMV,
+ * and w2's input is the FFN width; up to DH_MAX_HIDDEN columns (heads and linears alike). */
 #define DH_MAX_ROWS 32
 #define DH_MAX_HIDDEN_WIDE 5120    /* one pass over the head for more than 16 rows */
 #define DH_MAX_K 512
-#define DH_MAX_HIDDEN 8192
+#define DH_MAX_HIDDEN 32768         /* wider than 8192: streamed in 8192-column chunks */
 #define DH_MAX_VOCAB 262144        /* dh_topk / dh_draft */
 #define DH_MAX_GEMV_VOCAB 33554432 /* dh_gemv, dh_rescore: 2^25 rows */
 

@@ -96,7 +96,7 @@ def test_gemv_refusals_leave_outputs_untouched(no_device):
         (ok, x, 0, out, 1), (ok, x, 33, out, 2), (ok, None, 1, out, 1), (ok, x, 1, None, 1),
         (head(7, V, H, w, s), x, 1, out, 1),                       # bad format
         (head(dh.FP8_BLOCK32, V, 48, w, s), x, 1, out, 1),         # H % 32
-        (head(dh.FP8_BLOCK32, V, 8224, w, s), x, 1, out, 2),       # H > 8192
+        (head(dh.FP8_BLOCK32, V, 32800, w, s), x, 1, out, 2),      # H > 32768
         (head(dh.FP8_BLOCK32, 0, H, w, s), x, 1, out, 1),          # V < 1
         (head(dh.FP8_BLOCK32, V, H, w, None), x, 1, out, 1),       # missing scale
         (head(dh.BF16, V, H, w, s), x, 1, out, 1),                 # bf16 with a scale
@@ -333,7 +333,7 @@ def test_tiled_bytes():
     assert dh.tiled_bytes(dh.BF16, 16, 32) == 1 * 1 * 2048
     assert dh.tiled_bytes(dh.FP8_ROW, 0, 96) == 0
     assert dh.tiled_bytes(dh.FP8_ROW, 100, 48) == 0
-    assert dh.tiled_bytes(dh.FP8_ROW, 100, 8224) == 0
+    assert dh.tiled_bytes(dh.FP8_ROW, 100, 32800) == 0
     assert dh.tiled_bytes(7, 100, 64) == 0
     assert dh.tiled_bytes(dh.FP8_ROW | 32, 100, 64) == 0
 

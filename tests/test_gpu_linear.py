@@ -45,17 +45,9 @@ def check_bf16(gpu_bits, orc_bits, orc_pre, what):
         assert np.all(err <= tol + ulp), f"{what} row {r}: {float((err - tol - ulp).max()):.3e}"
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
-@pytest.mark.parametrize("N,K,R", [(37, 32, 16), (1000, 96, 1), (4133, 1376, 5),
-                                   (5120, 5120, 16), (2051, 8192, 3)])
-def test_linear_modes(fmt, N, K, R):
-    need_gpu()
-    say(f"linear {fmt} N={N} K={K} R={R}")
-    w = synth.random_head(N, K, seed=N + K, std=0.02)
-    x = synth.random_acts(R, K, seed=R + K)
-    res = synth.random_acts(R, N, seed=N + R, std=0.5)
-    gh, (ow, osc) = make_heads(fmt, w)
-    of = FMTS[fmt][1]
+def _check_modes(gh, x, res, of, ow, osc):
+    """dh_linear's three modes on head gh against the oracle's O14 (and the bf16 modes against
+    the GPU's own fp32 sums rounded on the host); returns the GPU outputs."""
     xd, rd = dev_u16(x), dev_u16(res)
     f32 = dh.linear(gh, xd, dh.OUT_F32)
     b16 = dh.linear(gh, xd, dh.OUT_BF16)
@@ -77,6 +69,50 @@ def test_linear_modes(fmt, N, K, R):
     pre = bf16_f32(res).astype(np.float64) + want
     check_bf16(ga, oracle.linear(of, ow, osc, x, oracle.MODE_ADD_BF16, res), pre,
                "linear add")
+    return gf, gb, ga
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
+@pytest.mark.parametrize("N,K,R", [(37, 32, 16), (1000, 96, 1), (4133, 1376, 5),
+                                   (5120, 5120, 16), (2051, 8192, 3)])
+def test_linear_modes(fmt, N, K, R):
+    need_gpu()
+    say(f"linear {fmt} N={N} K={K} R={R}")
+    w = synth.random_head(N, K, seed=N + K, std=0.02)
+    x = synth.random_acts(R, K, seed=R + K)
+    res = synth.random_acts(R, N, seed=N + R, std=0.5)
+    gh, (ow, osc) = make_heads(fmt, w)
+    _check_modes(gh, x, res, FMTS[fmt][1], ow, osc)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
+@pytest.mark.parametrize("N,K,R", [(2051, 16384, 3), (5120, 18432, 16), (300, 32768, 32),
+                                   (77, 8256, 1)])
+def test_linear_wide(fmt, N, K, R):
+    """Inputs wider than 8192 (a w2 whose input is the FFN width): the GEMV streams the
+    columns in chunks of 8192.  All three modes against the oracle, and the tiled head bit
+    for bit equal to the row-major one (both take the same chunks and virtual waves)."""
+    need_gpu()
+    say(f"wide linear {fmt} N={N} K={K} R={R}")
+    w = synth.random_head(N, K, seed=N + K, std=0.02)
+    x = synth.random_acts(R, K, seed=R + K)
+    res = synth.random_acts(R, N, seed=N + R, std=0.5)
+    gh, (ow, osc) = make_heads(fmt, w)
+    of = FMTS[fmt][1]
+    gf, gb, ga = _check_modes(gh, x, res, of, ow, osc)
+    th = dh.tile(gh)
+    xd, rd = dev_u16(x), dev_u16(res)
+    tf = dh.linear(th, xd, dh.OUT_F32)
+    tb = dh.linear(th, xd, dh.OUT_BF16)
+    ta = dh.linear(th, xd, dh.OUT_ADD_BF16, residual=rd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tf).view(np.uint32), gf.view(np.uint32))
+    assert np.array_equal(host(tb).view(np.uint16), gb)
+    assert np.array_equal(host(ta).view(np.uint16), ga)
+    # a row's sums do not depend on how many rows share the call
+    one = dh.linear(th, xd[R - 1:R].contiguous(), dh.OUT_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(one)[0].view(np.uint32), gf[R - 1].view(np.uint32))
 
 
 def test_linear_refusals_on_device():

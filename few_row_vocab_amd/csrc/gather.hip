@@ -34,7 +34,9 @@ __global__ __launch_bounds__(kGatherWaves * kWave) void gather_rows(
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; u++) {
             const int c = c0 + u * kWave + lane;
-            v[u] = ok && c < row_vecs ? src[c] : zero;
+            v[u] = zero;
+            if (ok && c < row_vecs)
+                v[u] = src[c];
         }
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; u++) {

@@ -456,14 +456,25 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
     hipError_t e = hipSuccess;
     if (down)   // nothing else is live in the checked workspace yet: it may hold partials
         e = dh::launch_linear(*down, x, rows, DH_OUT_BF16, nullptr, t, st, workspace, need);
-    // the GEMV zeroes the top-k's tickets, so the top-k is one launch
+    // Up to 16 rows, the GEMV also cuts each of its workgroups' logits for the top-k, which
+    // one workgroup per row then merges; else (or when the GEMV's grid is too large for the
+    // merge) the top-k is one launch of its own.  The GEMV zeroes the sync lines of the
+    // kernels after it.
+    const dh::GemvCut cut = dh::topk_cut(workspace, rows, head->vocab, k);
+    int grid = 0;
     if (e == hipSuccess)
         e = dh::launch_gemv(*head, down ? t : x, rows, L, st,
                             dh::topk_tickets(workspace, rows, head->vocab, k),
-                            dh::kSyncKinds * rows, dh::kTicketStride);
+                            dh::kSyncKinds * rows, dh::kTicketStride, rows <= 16 ? &cut : nullptr,
+                            &grid);
+    const bool cut_made = rows <= 16 && grid >= 1 && grid <= dh::kCutMaxChunks &&
+                          grid * cut.slots <= cut.max_keys;
     if (e == hipSuccess)
-        e = dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals, dense ? nullptr : draft,
-                            workspace, st, nullptr, nullptr, true);
+        e = cut_made ? dh::launch_cut_merge(L, rows, head->vocab, k, idmap, ids, vals,
+                                            dense ? nullptr : draft, workspace, grid, st)
+                     : dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals,
+                                       dense ? nullptr : draft, workspace, st, nullptr, nullptr,
+                                       true);
     if (e == hipSuccess && dense)   // its sync lines were zeroed by the GEMV as well
         e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st,
                                dh::topk_tickets(workspace, rows, head->vocab, k) +

@@ -19,16 +19,29 @@ constexpr int kWave = 64;
 // hipError_t of its launches.
 // zero, nzero, zstride: nzero pairs of words, zstride words apart, that the kernel sets to
 // zero (the sync lines of the kernels that follow it on the stream), or NULL.
+// cut: NULL, or the draft's fused top-k cut (up to 16 rows): each workgroup also leaves, per
+// row, the keys of its tiles' logits in the value bins at and above the bin of its m-th
+// largest (those strictly above when they would not fit `slots`), and a floor key above
+// every key it left out (0 when it left none out), for the merge of topk.h.  The cut is made
+// when the launch's grid is at most kCutMaxChunks and grid * slots <= max_keys;
+// grid_used (host) receives the grid.
+struct GemvCut {
+    uint64_t *keys;     // [rows][grid][slots], 0 past a workgroup's cut
+    uint64_t *floors;   // [rows][grid]
+    int m, slots, max_keys;
+};
+constexpr int kCutMaxChunks = 1024;
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
                        hipStream_t stream, uint32_t *zero = nullptr, int nzero = 0,
-                       int zstride = 1);
+                       int zstride = 1, const GemvCut *cut = nullptr, int *grid_used = nullptr);
 // The same GEMV with an output mode (dh_out_mode): fp32, bf16, or bf16 of residual + sum.
 // scratch: optional device memory; with a few tiles and linear_split_bytes of it, the work
 // is split over more workgroups with bit-identical results.
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
                          const uint16_t *residual, void *out, hipStream_t stream,
                          void *scratch = nullptr, size_t scratch_bytes = 0,
-                         uint32_t *zero = nullptr, int nzero = 0, int zstride = 1);
+                         uint32_t *zero = nullptr, int nzero = 0, int zstride = 1,
+                         const GemvCut *cut = nullptr, int *grid_used = nullptr);
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
 
 // sync: NULL (a second kernel picks the drafts), or the rescore's zeroed sync lines in a

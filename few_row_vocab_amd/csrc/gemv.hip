@@ -33,6 +33,7 @@
 //    lanes receive the same bytes as from the row-major head, so the results are the same
 //    bits.
 #include "dh_internal.h"
+#include "keys.h"
 #include "launch.h"
 
 namespace dh {
@@ -60,6 +61,12 @@ constexpr int kCacheNT = 2;              // gfx950 cache policy bit 1: non-tempo
 template <int FMT>
 constexpr int tiled_ahead_kib() { return FMT == DH_BF16 ? 48 : 32; }
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
+// A tile's sums in the stage.  Up to 16 rows (the draft's cut runs there) a tile is padded by
+// 16 floats: the cut reads one row's entries of four tiles in one instruction, and unpadded
+// tiles (a multiple of 64 floats apart) would put all four on the same LDS banks.  32-row
+// tiles are not padded: at 129,280 rows a workgroup keeps 32 of them, which padding would
+// push past the stage's 64 KiB (and the launch past one workgroup per compute unit).
+constexpr int stage_stride(int outs) { return outs == 256 ? outs + 16 : outs; }
 // Heads wider than 16 waves of 8 blocks (H > 8192) are streamed in column chunks of 16 * 8
 // 64-column blocks (CH below): a wave holds one chunk's activations at a time.  Both layouts
 // take the same chunks and the same 16 virtual waves (so they keep giving the same bits); a
@@ -85,6 +92,9 @@ struct GemvArgs {
     int tile_bytes;         // tiled layout: bytes of one 16-row tile, nkb * 1024 * (bytes/weight)
     uint32_t *zero;         // nzero pairs of words, zstride apart, the first workgroup zeroes
     int nzero, zstride;
+    // the draft's fused top-k cut (GemvCut; cut_m == 0: none)
+    uint64_t *cut_keys, *cut_floors;
+    int cut_m, cut_slots, cut_max;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -125,11 +135,15 @@ __device__ inline uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16
 // two 2^(b-127) for bytes 1..254.
 __device__ inline float e8m0_scale(uint32_t b) { return __uint_as_float(b << 23); }
 
-// The output of one (activation row c, head row v) sum s: the row scale, then the mode.
-__device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
+// A sum s of head row v with the row scale applied (FP8 row format).
+__device__ inline float row_scaled(const GemvArgs &a, int64_t v, float s)
 {
-    if (a.rscale)
-        s *= a.rscale[v];
+    return a.rscale ? s * a.rscale[v] : s;
+}
+
+// The output of one (activation row c, head row v) scaled sum s, in the mode.
+__device__ inline void store_out(const GemvArgs &a, int c, int64_t v, float s)
+{
     const int64_t at = (int64_t)c * a.V + v;
     if (a.mode == DH_OUT_F32) {
         a.logits[at] = s;
@@ -138,6 +152,169 @@ __device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
         if (a.mode == DH_OUT_ADD_BF16)
             s += __uint_as_float((uint32_t)a.residual[at] << 16);
         a.out16[at] = bf16_bits(s);
+    }
+}
+
+// The output of one (activation row c, head row v) sum s: the row scale, then the mode.
+__device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
+{
+    store_out(a, c, v, row_scaled(a, v, s));
+}
+
+// The draft's fused top-k cut of every row over this workgroup's entries, by the whole
+// workgroup (every thread calls it; nw waves).  The workgroup did tiles blockIdx.x + t *
+// gridDim.x for t < ntl; entry 16 t + i is head row 16 (blockIdx.x + t * gridDim.x) + i.
+// The writer of the logits leaves in stage[t * SST + 16 r + i] the image of the entry's
+// logit (topk.hip's order-preserving image; 0 when not eligible or past the head's rows) and
+// each row's range of images in rng (rng[r] the smallest non-zero one, rng[16 + r] the
+// largest).  An entry's key is topk.hip's (image, id).  Per row, the keys are binned over the
+// range (256 bins of equal width, as the top-k's select: a higher bin holds only larger
+// values); with d the bin of the m-th largest key, the cut is the keys of bins >= d, or of
+// bins > d (fewer than m) when those would not fit `slots`.  They go to the workgroup's slots
+// in any order, zeros after them; the floor is the smallest key of the cut, every key left
+// out being smaller, or 0 when none was left out.
+// A row is cut by a group of g waves, g a power of two up to 4 with g R <= nw (one wave a
+// row from nw / 2 rows up, a batch of rows after another when there are more than nw); lane
+// l of the group's wave q takes entries 64 (g j + q) + l.  The workgroup's 16 waves share 4
+// SIMDs, so a pass's fixed work costs once per wave there: more than 4 waves a row only
+// repeat it.  The code runs once per workgroup, from a cold instruction cache, so it is kept
+// short: each of the two passes (histogram, cut) re-reads the images from LDS rather than
+// holding them in registers (unrolled into registers, the code grew several-fold and
+// measured several microseconds slower).
+// ws: 16 KiB + 256 B of free LDS (the reduction buffer), set up by cut_init.
+constexpr int kCutLgWavesPerRow = 2;   // log2 of the waves that cut one row, at most
+// The smallest non-zero and the largest of (mn, mx) over each row of 16 lanes, in the row's
+// last lane (DPP row shifts; lanes with no source keep the identity).
+__device__ __forceinline__ void row_min_max32(uint32_t &mn, uint32_t &mx)
+{
+#define DH_ROW_STEP(ctrl)                                                                      \
+    {                                                                                          \
+        const uint32_t p = __builtin_amdgcn_update_dpp(0xffffffffu, mn, ctrl, 0xf, 0xf, false); \
+        const uint32_t q = __builtin_amdgcn_update_dpp(0u, mx, ctrl, 0xf, 0xf, false);          \
+        mn = p < mn ? p : mn;                                                                  \
+        mx = q > mx ? q : mx;                                                                  \
+    }
+    DH_ROW_STEP(0x111)   // row_shr:1
+    DH_ROW_STEP(0x112)   // row_shr:2
+    DH_ROW_STEP(0x114)   // row_shr:4
+    DH_ROW_STEP(0x118)   // row_shr:8
+#undef DH_ROW_STEP
+}
+// A workgroup barrier for the cut's LDS only: this wave's LDS operations complete, then
+// s_barrier.  __syncthreads() would also wait for every global store still in flight (the
+// logits, the cut keys), which nothing in the workgroup reads: that wait measured about
+// 0.4 us a barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+struct CutLdsView {
+    uint32_t *hist;                 // [16][256]
+    uint32_t *gcnt;                 // [16] per group: cut keys placed
+    unsigned long long *gfloor;     // [16] per group: the smallest cut key
+};
+__device__ __forceinline__ CutLdsView cut_view(uint32_t *ws)
+{
+    CutLdsView v;
+    v.hist = ws;
+    v.gcnt = ws + 16 * 256;
+    v.gfloor = reinterpret_cast<unsigned long long *>(v.gcnt + 16);
+    return v;
+}
+// Every group's counters and histogram to their start (call before a barrier).
+__device__ __forceinline__ void cut_init(uint32_t *ws)
+{
+    const CutLdsView v = cut_view(ws);
+    for (int q = threadIdx.x; q < 16 * 256; q += blockDim.x)
+        v.hist[q] = 0;
+    if (threadIdx.x < 16) {
+        v.gcnt[threadIdx.x] = 0;
+        v.gfloor[threadIdx.x] = ~0ull;
+    }
+}
+
+template <int SST>
+__device__ __forceinline__ void cut_rows(const GemvArgs &a, const uint32_t *stage, int ntl,
+                                         uint32_t *ws, const uint32_t *rng)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    // waves a row: a power of two, at most kCutWavesPerRow (more only repeat the fixed work
+    // of a pass on every SIMD), with lg = log2 of it
+    int lg = 0;
+    while (lg < kCutLgWavesPerRow && (a.R << (lg + 1)) <= nw)
+        lg++;
+    const int rows_per_batch = nw >> lg;
+    const int grp = wave >> lg, wig = wave & ((1 << lg) - 1);
+    // lane l of wave wig takes entries 64 (g j + wig) + l: tiles t = 4 (g j + wig) + l / 16,
+    // head rows 16 (blockIdx.x + t * gridDim.x) + l % 16
+    const int t0 = 4 * wig + (lane >> 4), tstep = 4 << lg;
+    const int i = lane & 15;
+    const uint32_t id0 = ((uint32_t)blockIdx.x + (uint32_t)t0 * gridDim.x) * 16u + (uint32_t)i;
+    const uint32_t idstep = (uint32_t)tstep * gridDim.x * 16u;
+    const CutLdsView v = cut_view(ws);
+    uint32_t *hist = v.hist + grp * 256;
+    const int slots = a.cut_slots;
+    for (int b0 = 0; b0 < a.R; b0 += rows_per_batch) {
+        const int r = b0 + grp;
+        const bool act = grp < rows_per_batch && r < a.R;
+        // the image of the entry of tile t (0 when not eligible, or past the head's rows)
+        const uint32_t *srow = stage + 16 * r + i;
+        auto image = [&](int t) -> uint32_t { return srow[t * SST]; };
+        // 1: the histogram over the range of the row's eligible images (rng, from the writer)
+        const uint32_t mn = act ? rng[r] : ~0u, mx = act ? rng[16 + r] : 0u;
+        const float lo = image_float(mn);
+        const float scale = 256.0f / (image_float(mx) - lo);
+        // the select's bin map (a NaN product, from a zero or infinite width, goes to 255)
+        auto bin_of = [&](uint32_t x) -> uint32_t {
+            return (uint32_t)fminf((image_float(x) - lo) * scale, 255.0f);
+        };
+        if (act && mx != 0) {
+#pragma unroll 2
+            for (int t = t0; t < ntl; t += tstep) {
+                const uint32_t im = image(t);
+                if (im != 0)
+                    atomicAdd(&hist[bin_of(im)], 1u);
+            }
+        }
+        lds_barrier();
+        // 2: the cut (every key when at most m, bins >= d, or bins > d) to the slots
+        uint64_t *out = a.cut_keys + ((int64_t)r * gridDim.x + blockIdx.x) * slots;
+        bool all = true;
+        if (act && mx != 0) {
+            uint32_t d, above, count;
+            const uint32_t total = locate<256>(hist, (uint32_t)a.cut_m, d, above, count);
+            all = total <= (uint32_t)a.cut_m;
+            uint32_t dmin = 0;
+            if (!all) {
+                dmin = above + count <= (uint32_t)slots ? d : d + 1;
+                all = dmin == d && above + count == total;
+            }
+            uint32_t id = id0;
+#pragma unroll 2
+            for (int t = t0; t < ntl; t += tstep, id += idstep) {
+                const uint32_t im = image(t);
+                if (im != 0 && (all || bin_of(im) >= dmin)) {
+                    const uint64_t key = entry_key(im, id);
+                    out[atomicAdd(&v.gcnt[grp], 1u)] = key;
+                    atomicMin(&v.gfloor[grp], (unsigned long long)key);
+                }
+            }
+        }
+        lds_barrier();
+        // 3: zeros after the cut; the floor; the group's counters back to their start
+        if (act && wig == 0) {
+            const uint32_t placed = v.gcnt[grp];
+            for (int q = (int)placed + lane; q < slots; q += kWave)
+                out[q] = 0;
+            if (lane == 0)
+                a.cut_floors[(int64_t)r * gridDim.x + blockIdx.x] = all ? 0ull : v.gfloor[grp];
+        }
+        if (b0 + rows_per_batch < a.R) {           // another batch: reset, then a barrier
+            lds_barrier();
+            cut_init(ws);
+            lds_barrier();
+        }
     }
 }
 
@@ -167,6 +344,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     constexpr int ES = FMT == DH_BF16 ? 2 : 1;   // bytes per weight element
     constexpr int TILE = 16 * TR;                // head rows per tile
     constexpr int OUTS = TILE * 16 * NB;         // (head row, activation row) sums per tile
+    constexpr int SST = stage_stride(OUTS);      // floats a tile takes in the stage
     constexpr int KW = VW * KBW;                 // 64-column blocks of one wave
     // blocks a wave keeps in flight: a whole tile (row-major heads), or a window sized so a
     // full workgroup (16 / VW waves) holds about tiled_ahead_kib (tiled heads)
@@ -174,6 +352,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     constexpr int AH = !TL ? (CH ? 4 : KW) : AHW < 1 ? 1 : AHW > KW ? KW : AHW;
     __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
     extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
+    __shared__ uint32_t cut_rng[2][16];          // the cut: each row's image range (min, max)
 
     static_assert(!CH || !FULL, "a chunked launch guards its loads");
     const int lane = threadIdx.x & 63;
@@ -184,6 +363,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             a.zero[i * a.zstride] = 0u;
             a.zero[i * a.zstride + 1] = 0u;
         }
+    if (threadIdx.x < 32)                      // seen by the writer after the loop's barriers
+        cut_rng[threadIdx.x >> 4][threadIdx.x & 15] = threadIdx.x < 16 ? ~0u : 0u;
     const int rr = lane & 15;
     const int g = lane >> 4;
     const int H = a.H;
@@ -380,8 +561,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             for (int w = 0; w < nvw; w++)
                 s += red[buf][w][c >> 4][j][src];
             if (CH && ch > 0)
-                s = stage[it * OUTS + o] + s;     // the earlier chunks' sums, then this one's
-            stage[it * OUTS + o] = s;
+                s = stage[it * SST + o] + s;      // the earlier chunks' sums, then this one's
+            stage[it * SST + o] = s;
         }
         buf ^= 1;
         if (!more)
@@ -397,15 +578,53 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave
     // w writes tiles w, w + nw, ...; a lane takes (activation row c, head row i) pairs.
     static_assert(TR == 1, "the writer below assumes one 16-row group per tile");
+    const bool cut = a.cut_m > 0 && NB == 1 && (int)gridDim.x <= kCutMaxChunks &&
+                     (int)gridDim.x * a.cut_slots <= a.cut_max;
     const int per_tile = a.R * 16;
+    // the cut: the images' range of activation rows 4 q + lane / 16, q < 4, as they are written
+    uint32_t rmn[4] = {~0u, ~0u, ~0u, ~0u}, rmx[4] = {0u, 0u, 0u, 0u};
     for (int t = wave; t <= it; t += nw) {
         const int64_t v0 = (int64_t)(blockIdx.x + t * gridDim.x) * TILE;
-        for (int o = lane; o < per_tile; o += kWave) {
+#pragma unroll
+        for (int q = 0; q < 32 * 16 / kWave; q++) {
+            const int o = lane + kWave * q;
             const int c = o >> 4, i = o & 15;
             const int64_t v = v0 + i;
-            if (v < V)
-                write_out(a, c, v, stage[t * OUTS + c * 16 + i]);
+            if (o < per_tile) {
+                float *sp = &stage[t * SST + c * 16 + i];
+                uint32_t im = 0;
+                if (v < V) {
+                    const float s = row_scaled(a, v, *sp);
+                    store_out(a, c, v, s);
+                    im = order_key(s);               // the cut ranks the logits as written
+                }
+                if (cut && q < 4) {
+                    // the slot keeps the image (0 past the head's rows) for the cut
+                    *reinterpret_cast<uint32_t *>(sp) = im;
+                    rmn[q & 3] = im != 0 && im < rmn[q & 3] ? im : rmn[q & 3];
+                    rmx[q & 3] = im > rmx[q & 3] ? im : rmx[q & 3];
+                }
+            }
         }
+    }
+    if (cut) {
+        // each row's range over its 16 lanes (lane 15 of a row of lanes ends with it), then
+        // over the waves
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            row_min_max32(rmn[q], rmx[q]);
+            const int c = 4 * q + (lane >> 4);
+            if ((lane & 15) == 15 && c < a.R) {
+                atomicMin(&cut_rng[0][c], rmn[q]);
+                atomicMax(&cut_rng[1][c], rmx[q]);
+            }
+        }
+        // the cut's LDS in the reduction buffer, which is free now
+        static_assert(sizeof(red) >= 16 * 256 * sizeof(uint32_t) + 256, "the cut's LDS fits");
+        uint32_t *cws = reinterpret_cast<uint32_t *>(&red[0][0][0][0][0]);
+        cut_init(cws);
+        lds_barrier();                               // the scaled sums, ranges, the cut's LDS
+        cut_rows<SST>(a, reinterpret_cast<const uint32_t *>(stage), it + 1, cws, &cut_rng[0][0]);
     }
 }
 
@@ -526,7 +745,7 @@ __global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const fl
 }
 
 template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false>
-hipError_t run(GemvArgs a, hipStream_t stream)
+hipError_t run(GemvArgs a, hipStream_t stream, int *grid_used)
 {
     static int occ_cache[kMaxWaves + 1];
     static int lds_set[kMaxDevices];               // per device: the LDS limit has been raised
@@ -551,41 +770,44 @@ hipError_t run(GemvArgs a, hipStream_t stream)
     const int occ = occupancy(kern, block, occ_cache[nw]);
     int64_t grid = (int64_t)device_cus() * occ;
     // each block keeps its tiles' logits in LDS: at most kMaxStageBytes of them
-    const int64_t max_per = kMaxStageBytes / (TR * 256 * NB * (int)sizeof(float));
+    const int64_t max_per = kMaxStageBytes / (stage_stride(TR * 256 * NB) * (int)sizeof(float));
     const int64_t min_grid = (a.ntiles + max_per - 1) / max_per;
     if (grid < min_grid)
         grid = min_grid;
     if (grid > a.ntiles)
         grid = a.ntiles;
     const int64_t per = (a.ntiles + grid - 1) / grid;
+    if (grid_used)
+        *grid_used = (int)grid;
     return launch(kern, dim3((unsigned)grid), dim3(block),
-                  (size_t)per * TR * 256 * NB * sizeof(float), stream, a);
+                  (size_t)per * stage_stride(TR * 256 * NB) * sizeof(float), stream, a);
 }
 
 template <int FMT, int KBW, int NB, int VW, bool TL>
-hipError_t run_kbw(const GemvArgs &a, hipStream_t stream)
+hipError_t run_kbw(const GemvArgs &a, hipStream_t stream, int *grid_used)
 {
     constexpr int TR = 1;   // two groups measured slower: the loop is not latency-bound
     if (a.H % 64 == 0 && a.nkb % (VW * KBW) == 0)
-        return run<FMT, KBW, true, TR, NB, VW, TL>(a, stream);
-    return run<FMT, KBW, false, TR, NB, VW, TL>(a, stream);
+        return run<FMT, KBW, true, TR, NB, VW, TL>(a, stream, grid_used);
+    return run<FMT, KBW, false, TR, NB, VW, TL>(a, stream, grid_used);
 }
 
+// grid_used: the grid of the (last) launch.
 template <int FMT, bool TL>
-hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
+hipError_t run_fmt(const GemvArgs &a, hipStream_t stream, int *grid_used)
 {
     const int kbw = (a.nkb + kMaxWaves - 1) / kMaxWaves;   // the 16-row split, for any R
     if (a.R > 16) {
         switch (kbw) {
-        case 1: return run_kbw<FMT, 1, 2, 2, TL>(a, stream);
-        case 2: return run_kbw<FMT, 2, 2, 2, TL>(a, stream);
-        case 3: return run_kbw<FMT, 3, 2, 2, TL>(a, stream);
-        case 4: return run_kbw<FMT, 4, 2, 2, TL>(a, stream);
+        case 1: return run_kbw<FMT, 1, 2, 2, TL>(a, stream, grid_used);
+        case 2: return run_kbw<FMT, 2, 2, 2, TL>(a, stream, grid_used);
+        case 3: return run_kbw<FMT, 3, 2, 2, TL>(a, stream, grid_used);
+        case 4: return run_kbw<FMT, 4, 2, 2, TL>(a, stream, grid_used);
         // H <= 5120: 32 rows of activations fill 160 of a wave's 256 VGPRs, which still leaves
         // room (218-246 VGPRs in all) except for the row-major bf16 tile, which spills
         case 5:
             if constexpr (FMT != DH_BF16 || TL)
-                return run_kbw<FMT, 5, 2, 2, TL>(a, stream);
+                return run_kbw<FMT, 5, 2, 2, TL>(a, stream, grid_used);
             [[fallthrough]];
         default: {
             // wider heads: 32 rows of activations do not fit the registers, so rows 0..15 and
@@ -598,41 +820,42 @@ hipError_t run_fmt(const GemvArgs &a, hipStream_t stream)
             hi.logits = a.logits ? a.logits + skip : nullptr;
             hi.out16 = a.out16 ? a.out16 + skip : nullptr;
             hi.residual = a.residual ? a.residual + skip : nullptr;
-            const hipError_t e = run_fmt<FMT, TL>(lo, stream);
-            return e != hipSuccess ? e : run_fmt<FMT, TL>(hi, stream);
+            const hipError_t e = run_fmt<FMT, TL>(lo, stream, grid_used);
+            return e != hipSuccess ? e : run_fmt<FMT, TL>(hi, stream, grid_used);
         }
         }
     }
     switch (kbw) {
-    case 1: return run_kbw<FMT, 1, 1, 1, TL>(a, stream);
-    case 2: return run_kbw<FMT, 2, 1, 1, TL>(a, stream);
-    case 3: return run_kbw<FMT, 3, 1, 1, TL>(a, stream);
-    case 4: return run_kbw<FMT, 4, 1, 1, TL>(a, stream);
+    case 1: return run_kbw<FMT, 1, 1, 1, TL>(a, stream, grid_used);
+    case 2: return run_kbw<FMT, 2, 1, 1, TL>(a, stream, grid_used);
+    case 3: return run_kbw<FMT, 3, 1, 1, TL>(a, stream, grid_used);
+    case 4: return run_kbw<FMT, 4, 1, 1, TL>(a, stream, grid_used);
     // a bf16 tile of 5 blocks a wave does not fit 16 waves' 128 VGPRs next to the
     // activations (8 spilled); 8 waves of two virtual waves each (the same bits) fit and
     // measured 3.6% faster at H = 5120.  Wider bf16 tiles spill either way, FP8 tiles fit.
     case 5:
         if (FMT == DH_BF16)
-            return run_kbw<FMT, 5, 1, 2, TL>(a, stream);
-        return run_kbw<FMT, 5, 1, 1, TL>(a, stream);
-    case 6: return run_kbw<FMT, 6, 1, 1, TL>(a, stream);
-    case 7: return run_kbw<FMT, 7, 1, 1, TL>(a, stream);
-    case 8: return run_kbw<FMT, 8, 1, 1, TL>(a, stream);
+            return run_kbw<FMT, 5, 1, 2, TL>(a, stream, grid_used);
+        return run_kbw<FMT, 5, 1, 1, TL>(a, stream, grid_used);
+    case 6: return run_kbw<FMT, 6, 1, 1, TL>(a, stream, grid_used);
+    case 7: return run_kbw<FMT, 7, 1, 1, TL>(a, stream, grid_used);
+    case 8: return run_kbw<FMT, 8, 1, 1, TL>(a, stream, grid_used);
     default:   // H > 8192: column chunks
         if constexpr (TL)
-            return run<FMT, kChunkKbw, false, 1, 1, 1, true, true>(a, stream);
+            return run<FMT, kChunkKbw, false, 1, 1, 1, true, true>(a, stream, grid_used);
         else
-            return run<FMT, kChunkKbw, false, 1, 1, 2, false, true>(a, stream);
+            return run<FMT, kChunkKbw, false, 1, 1, 2, false, true>(a, stream, grid_used);
     }
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const dh_head &head, const uint16_t *x, int rows, float *logits,
-                       hipStream_t stream, uint32_t *zero, int nzero, int zstride)
+                       hipStream_t stream, uint32_t *zero, int nzero, int zstride,
+                       const GemvCut *cut, int *grid_used)
 {
     return launch_linear(head, x, rows, DH_OUT_F32, nullptr, logits, stream, nullptr, 0, zero,
-                         nzero, zstride);
+                         nzero, zstride, cut, grid_used);
 }
 
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows)
@@ -663,7 +886,7 @@ hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
                          const uint16_t *residual, void *out, hipStream_t stream,
                          void *scratch, size_t scratch_bytes, uint32_t *zero, int nzero,
-                         int zstride)
+                         int zstride, const GemvCut *cut, int *grid_used)
 {
     const int fmt = head.format & ~DH_TILED;
     GemvArgs a;
@@ -684,6 +907,14 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
     a.zero = zero;
     a.nzero = zero ? nzero : 0;
     a.zstride = zstride;
+    const bool with_cut = cut && mode == DH_OUT_F32 && rows <= 16;
+    a.cut_keys = with_cut ? cut->keys : nullptr;
+    a.cut_floors = with_cut ? cut->floors : nullptr;
+    a.cut_m = with_cut ? cut->m : 0;
+    a.cut_slots = with_cut ? cut->slots : 0;
+    a.cut_max = with_cut ? cut->max_keys : 0;
+    if (grid_used)
+        *grid_used = 0;
     // few tiles and room for the partials: split by virtual wave (the same bits)
     const int64_t ntiles = (a.V + 15) / 16;
     if (scratch && ntiles <= device_cus() / 2 && (a.nkb + kMaxWaves - 1) / kMaxWaves <= kSplitMaxKbw &&
@@ -700,12 +931,12 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
         }
     }
     switch (head.format) {
-    case DH_BF16: return run_fmt<DH_BF16, false>(a, stream);
-    case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32, false>(a, stream);
-    case DH_FP8_ROW: return run_fmt<DH_FP8_ROW, false>(a, stream);
-    case DH_BF16 | DH_TILED: return run_fmt<DH_BF16, true>(a, stream);
-    case DH_FP8_BLOCK32 | DH_TILED: return run_fmt<DH_FP8_BLOCK32, true>(a, stream);
-    case DH_FP8_ROW | DH_TILED: return run_fmt<DH_FP8_ROW, true>(a, stream);
+    case DH_BF16: return run_fmt<DH_BF16, false>(a, stream, grid_used);
+    case DH_FP8_BLOCK32: return run_fmt<DH_FP8_BLOCK32, false>(a, stream, grid_used);
+    case DH_FP8_ROW: return run_fmt<DH_FP8_ROW, false>(a, stream, grid_used);
+    case DH_BF16 | DH_TILED: return run_fmt<DH_BF16, true>(a, stream, grid_used);
+    case DH_FP8_BLOCK32 | DH_TILED: return run_fmt<DH_FP8_BLOCK32, true>(a, stream, grid_used);
+    case DH_FP8_ROW | DH_TILED: return run_fmt<DH_FP8_ROW, true>(a, stream, grid_used);
     default: return hipErrorInvalidValue;
     }
 }

@@ -50,10 +50,39 @@ inline TopkShape topk_shape(int rows, int64_t vocab, int k)
 // (measured up to 8 us at 16 rows).
 constexpr int kTicketStride = 64;    // words from one sync line to the next
 constexpr int kSyncKinds = 3;
+// Then the draft's fused top-k cut (GemvCut): the cut keys, [rows][grid][slots], and the
+// floors, [rows][grid], sized for a grid of up to min(ntiles, kCutMaxChunks) workgroups.
 struct TopkWs {
-    size_t keys_off, stats_off, tickets_off, bytes;
+    size_t keys_off, stats_off, tickets_off, cut_keys_off, cut_floors_off, bytes;
 };
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
+
+// dh_draft's top-k for up to 16 rows, fused into the GEMV: each GEMV workgroup's tiles are a
+// chunk of the row, and the GEMV leaves each chunk's cut (launch_gemv's GemvCut: the keys of
+// the value bins at and above the bin of its m-th largest, at most `slots` of them, and a
+// floor above every key it left out).  One workgroup per row then merges: the k best of all
+// cuts, and the k-th of them, t; a chunk whose floor beats t may hold more keys above t, and
+// only then are such chunks' logits read back whole (at most k / m chunks: each holds m keys
+// of the k, unless its boundary bin was crowded).  Every key left out of the merge is below
+// its chunk's floor, which is at most t, so below k keys of the row: the result is exact.
+// m is set so a chunk rarely holds more than m of the row's k best (k / grid of them on
+// average, about k / 256 here): m = ceil(L + 4 sqrt(L) + 3) for L = k / 256, at most k.
+struct CutShape {
+    int m, slots;
+};
+CutShape cut_shape(int k);
+constexpr int kCutThreads = 1024;    // threads of a merging workgroup
+constexpr int kCutMaxFast = 8192 / kCutThreads;   // cut keys a merging thread holds (8192 in all)
+// the merge ranks more than kCountMax survivors with a wave per 64 of them
+static_assert(kCutThreads >= DH_MAX_K, "a merging workgroup has a wave per 64 of k survivors");
+// The cut's part of a workspace (launch_gemv's argument).
+GemvCut topk_cut(void *ws, int rows, int64_t vocab, int k);
+// The merge of the cuts a GEMV of `grid` workgroups left in ws (grid <= kCutMaxChunks,
+// grid * slots <= kCutThreads * kCutMaxFast); logits: that GEMV's output.  Outputs as
+// launch_topk's.
+hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
+                            const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                            void *ws, int grid, hipStream_t stream);
 
 // idmap: NULL, or the vocabulary id of each logit column (ids and argmax are mapped).
 // probs, lse: NULL, or the softmax probability of each kept entry [rows][k] and each row's

@@ -14,11 +14,11 @@
 // (image << 32) | (0xffffffff - id) is a 64-bit key that is distinct per entry and whose
 // numeric order is exactly the ordering above, so ties need no special case.  Ineligible
 // entries get the key 0.
-//  * One launch, a workgroup per (row, chunk of 2048 to 8192 logits).  Chunk pass: a radix
-//    select over the chunk's keys (most significant byte first, histograms in LDS, stopping
-//    as soon as the boundary byte's bin is taken whole) finds the chunk's best min(k, n);
-//    they go to the workspace in any order, the rest of the chunk's k slots as zeros.  Any
-//    entry of the row's top-k is in its chunk's top-k.
+//  * One launch, a workgroup per (row, chunk of 2048 to 8192 logits).  Chunk pass: a select
+//    over the chunk's keys (value bins, with a radix select for a crowded bin; see
+//    select_bins) finds the chunk's best min(k, n); they go to the workspace in any order,
+//    the rest of the chunk's k slots as zeros.  Any entry of the row's top-k is in its
+//    chunk's top-k.
 //  * Merge: each workgroup then takes a ticket on its row (an atomic count of the row's
 //    finished chunks, after a device-scope release of its list); the last one of the row
 //    (the "top-1 ... in parts and a join" of the pages, with the join done by whichever part
@@ -28,6 +28,10 @@
 //    (zeros, whose sign the image drops, are read from the logits, so -0 stays -0).  The
 //    tickets start at zero: the GEMV before the top-k zeroes them (dh_draft), else a small
 //    kernel does (the call stays free of memset, so it can be captured in a graph).
+//  * dh_draft up to 16 rows fuses the chunk pass into the GEMV (topk.h): each GEMV
+//    workgroup leaves a short cut of its tiles' logits, and cut_merge, one workgroup per row,
+//    runs the same select over the cuts, then reads back the logits of any chunk whose cut
+//    may have left out keys of the row's top k (exact for any input; rare for spread ones).
 // Softmax statistics (STATS, for dh_topk_softmax): pass 1 also writes each chunk's largest
 // eligible logit m_c and s_c = sum over its eligible logits of exp(l - m_c) (1 for l == m_c,
 // so +inf entries count 1 each); the merge combines them in chunk order into the row's m and
@@ -584,6 +588,160 @@ struct MergeLds {
     float row_m, row_z;
 };
 
+// The select of a merge: keeps the min(k, n) largest of the non-zero keys the workgroup holds
+// in registers (MPER a thread, distinct) and ranks them.  Returns kk = min(k, n); this
+// thread's survivor x (0 when it has none) and its rank (the number of survivors that beat
+// it, so the slot of x in the descending order).  Before the call the select's LDS may be
+// reused freely (the call clears what it needs; ml.sel is its output space); after it, a
+// barrier before the LDS is reused.
+template <int MPER, int NT>
+__device__ __forceinline__ int select_rank(const uint64_t (&key)[MPER], int k, SelectLds<NT> &sh,
+                                           MergeLds &ml, uint64_t &x, uint32_t &rank)
+{
+    uint64_t *sel = ml.sel;
+    const int i = threadIdx.x;
+    clear_select<NT>(sh);
+    publish_range<MPER, NT>(key, sh);
+    __syncthreads();
+    uint32_t bin[MPER];
+    Cut cut;
+    int kk = select_sorted<MPER, NT>(key, (uint32_t)k, sh, sel, cut, bin);
+    x = 0;
+    rank = 0;
+    if (kk >= 0) {
+        // the survivors sit in their bins' slots: a key of the boundary bin is in its place,
+        // one of a bin above it adds the keys of its bin that beat it (keys are distinct)
+        if (i < kk) {
+            x = sel[i];
+            const uint32_t b = sh.hist[kBinOfOff + i];
+            rank = (uint32_t)i;
+            if (b != kPlaced) {
+                const uint32_t s0 = sh.hist[kStartOff + b];
+                rank = s0 + count_above_at(sel, s0, sh.hist[b], x);
+            }
+        }
+        return kk;
+    }
+    // a crowded boundary bin (many equal or nearly equal values): the radix select among its
+    // keys, then the survivors ranked among themselves
+    kk = k;
+    __syncthreads();
+    for (int j = threadIdx.x; j < kHistWords; j += NT)
+        sh.hist[j] = 0;
+    __syncthreads();
+    uint32_t n2;
+    cut.P = select_top<MPER, NT>(key, cut.rem, sh, n2, [&](int j) { return bin[j] == cut.d; });
+    // the survivors, in any order, to sel[0..kk)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < MPER; j++)
+        mine += survives(cut, key[j], bin[j]);
+    uint32_t at = wave_reserve(mine, &sh.fill);
+    if (mine) {
+#pragma unroll
+        for (int j = 0; j < MPER; j++)
+            if (survives(cut, key[j], bin[j]) && at < (uint32_t)kk)   // exactly kk survive
+                sel[at++] = key[j];
+    }
+    __syncthreads();
+
+    // slot of a survivor = the number of survivors that beat it (keys are distinct)
+    if (kk <= kCountMax) {
+        // few survivors: count directly
+        if (i < kk) {
+            x = sel[i];
+            rank = count_above(sel, kk, x);
+        }
+    } else {
+        // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then a
+        // survivor's rank is its place in its run plus, for each other run, the number of
+        // that run's keys above it (a binary search); the workgroup has a wave per run
+        const int nruns = (kk + 63) >> 6;
+        const int w = i >> 6, l = i & 63;
+        uint64_t y0 = 0;
+        if (w < nruns)
+            y0 = wave_sort_desc(i < kk ? sel[i] : 0ull, l);
+        __syncthreads();
+        if (w < nruns)
+            sel[i] = y0;
+        __syncthreads();
+        if (w < nruns && y0 != 0) {
+            // the searches of all runs advance together (independent LDS reads per step);
+            // run q keeps run[0..lo) > y0 >= run[hi..64), and 7 halvings settle 64 keys
+            constexpr int kMaxRuns = DH_MAX_K / 64;
+            int lo[kMaxRuns], hi[kMaxRuns];
+#pragma unroll
+            for (int q = 0; q < kMaxRuns; q++) {
+                lo[q] = 0;
+                hi[q] = q < nruns && q != w ? 64 : 0;
+            }
+            // every run's probe is read each step, without a branch, so the step's eight LDS
+            // reads are in flight together (a settled or absent run reads a slot it ignores)
+#pragma unroll
+            for (int step = 0; step < 7; step++) {
+                int mid[kMaxRuns];
+                uint64_t y[kMaxRuns];
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++) {
+                    mid[q] = (lo[q] + hi[q]) >> 1;
+                    y[q] = sel[64 * q + (mid[q] & 63)];
+                }
+#pragma unroll
+                for (int q = 0; q < kMaxRuns; q++) {
+                    const bool open = lo[q] < hi[q], above = y[q] > y0;
+                    lo[q] = open && above ? mid[q] + 1 : lo[q];
+                    hi[q] = open && !above ? mid[q] : hi[q];
+                }
+            }
+            uint32_t rk = (uint32_t)l;
+#pragma unroll
+            for (int q = 0; q < kMaxRuns; q++)
+                rk += (uint32_t)lo[q];
+            if (rk < (uint32_t)kk) {
+                x = y0;
+                rank = rk;
+            }
+        }
+    }
+    return kk;
+}
+
+// The outputs of row r for a ranked survivor: its id (through idmap) and value at slot rank,
+// and the argmax from rank 0.  STATS: its softmax probability from ml.row_m and ml.row_z.
+template <bool STATS>
+__device__ __forceinline__ void emit_survivor(uint64_t x, uint32_t rank, const float *lrow,
+                                              const int32_t *idmap, int32_t *rid, float *rval,
+                                              float *rprob, int32_t *argmax, int r,
+                                              const MergeLds &ml)
+{
+    const uint32_t id = key_id(x);
+    // a subset head's entry id is vocabulary id idmap[id]
+    const int32_t out = idmap ? idmap[id] : (int32_t)id;
+    rid[rank] = out;
+    const float v = image_value(x, lrow + id);
+    rval[rank] = v;
+    if constexpr (STATS)
+        rprob[rank] = rel_exp(v, ml.row_m) / ml.row_z;
+    if (rank == 0 && argmax)
+        argmax[r] = out;
+}
+
+// The slots of row r past its kk survivors: id 0, value -inf (probability 0); argmax 0 when
+// the row has no eligible entry.
+template <bool STATS>
+__device__ __forceinline__ void emit_padding(int kk, int k, int32_t *rid, float *rval,
+                                             float *rprob, int32_t *argmax, int r)
+{
+    for (int p = kk + (int)threadIdx.x; p < k; p += blockDim.x) {
+        rid[p] = 0;
+        rval[p] = -__builtin_inff();
+        if constexpr (STATS)
+            rprob[p] = 0.f;
+    }
+    if (kk == 0 && argmax && threadIdx.x == 0)
+        argmax[r] = 0;
+}
+
 // The merge of row r: a thread holds MPER of the row's nchunks * k list slots
 // (MPER * NT >= nchunks * k), and the same select as the chunk pass keeps k of them.  STATS:
 // the row's softmax statistics from the chunks' (m_c, s_c): probs[r][slot] and lse[r].
@@ -595,7 +753,6 @@ __device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k,
 {
     const int slots = nchunks * k;
     const uint64_t *src = cand + (int64_t)r * slots;
-    uint64_t *sel = ml.sel;
 
     // all loads issued together (bounded buffer loads: slots past the end read as 0)
     const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
@@ -607,11 +764,10 @@ __device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k,
             ls, (uint32_t)(j * NT + threadIdx.x) * 8u, 0, kCacheDevice);
         key[j] = ((uint64_t)q.y << 32) | q.x;
     }
-    clear_select<NT>(sh);
-    publish_range<MPER, NT>(key, sh);
     if constexpr (STATS) {
         // wave 0: m = max_c m_c, then z = sum_c s_c exp(m_c - m), chunks c = lane, lane + 64,
-        // ... summed in that order per lane, then across lanes by a butterfly
+        // ... summed in that order per lane, then across lanes by a butterfly (published to
+        // the other waves by the select's first barrier)
         if (threadIdx.x < 64) {
             const uint64_t *st = reinterpret_cast<const uint64_t *>(stats + (int64_t)r * nchunks);
             constexpr int kMaxChunks = DH_MAX_VOCAB / 2048;
@@ -641,132 +797,16 @@ __device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k,
             }
         }
     }
-    __syncthreads();
-    uint32_t bin[MPER];
-    Cut cut;
-    int kk = select_sorted<MPER, NT>(key, (uint32_t)k, sh, sel, cut, bin);
+    uint64_t x;
+    uint32_t rank;
+    const int kk = select_rank<MPER, NT>(key, k, sh, ml, x, rank);
     int32_t *rid = ids + (int64_t)r * k;
     float *rval = vals + (int64_t)r * k;
-    const int i = threadIdx.x;
-    // one survivor to its slot of the output
-    auto emit = [&](uint64_t x, uint32_t rank) {
-        const uint32_t id = key_id(x);
-        // a subset head's entry id is vocabulary id idmap[id]
-        const int32_t out = idmap ? idmap[id] : (int32_t)id;
-        rid[rank] = out;
-        const float v = image_value(x, logits + (int64_t)r * V + id);
-        rval[rank] = v;
-        if constexpr (STATS)
-            probs[(int64_t)r * k + rank] = rel_exp(v, ml.row_m) / ml.row_z;
-        if (rank == 0 && argmax)
-            argmax[r] = out;
-    };
-
-    if (kk >= 0) {
-        // the survivors sit in their bins' slots: a key of the boundary bin is in its place,
-        // one of a bin above it adds the keys of its bin that beat it (keys are distinct)
-        if (i < kk) {
-            const uint64_t x = sel[i];
-            const uint32_t b = sh.hist[kBinOfOff + i];
-            uint32_t rank = (uint32_t)i;
-            if (b != kPlaced) {
-                const uint32_t s0 = sh.hist[kStartOff + b];
-                rank = s0 + count_above_at(sel, s0, sh.hist[b], x);
-            }
-            emit(x, rank);
-        }
-    } else {
-        // a crowded boundary bin (many equal or nearly equal values): the radix select among
-        // its keys, then the survivors ranked among themselves
-        kk = k;
-        __syncthreads();
-        for (int j = threadIdx.x; j < kHistWords; j += NT)
-            sh.hist[j] = 0;
-        __syncthreads();
-        uint32_t n2;
-        cut.P = select_top<MPER, NT>(key, cut.rem, sh, n2,
-                                     [&](int j) { return bin[j] == cut.d; });
-        // the survivors, in any order, to sel[0..kk)
-        uint32_t mine = 0;
-#pragma unroll
-        for (int j = 0; j < MPER; j++)
-            mine += survives(cut, key[j], bin[j]);
-        uint32_t at = wave_reserve(mine, &sh.fill);
-        if (mine) {
-#pragma unroll
-            for (int j = 0; j < MPER; j++)
-                if (survives(cut, key[j], bin[j]) && at < (uint32_t)kk)   // exactly kk survive
-                    sel[at++] = key[j];
-        }
-        __syncthreads();
-
-        // slot of a survivor = the number of survivors that beat it (keys are distinct)
-        uint32_t rank = 0;
-        uint64_t x = 0;
-        if (kk <= kCountMax) {
-            // few survivors: count directly
-            if (i < kk) {
-                x = sel[i];
-                rank = count_above(sel, kk, x);
-            }
-        } else {
-            // many: each wave sorts a run of 64 (descending, zero keys pad and sort last), then
-            // a survivor's rank is its place in its run plus, for each other run, the number of
-            // that run's keys above it (a binary search); the workgroup has a wave per run
-            const int nruns = (kk + 63) >> 6;
-            const int w = i >> 6, l = i & 63;
-            if (w < nruns) {
-                x = wave_sort_desc(i < kk ? sel[i] : 0ull, l);
-            }
-            __syncthreads();
-            if (w < nruns)
-                sel[i] = x;
-            __syncthreads();
-            if (w < nruns && x != 0) {
-                // the searches of all runs advance together (independent LDS reads per step);
-                // run q keeps run[0..lo) > x >= run[hi..64), and 7 halvings settle 64 keys
-                constexpr int kMaxRuns = DH_MAX_K / 64;
-                int lo[kMaxRuns], hi[kMaxRuns];
-#pragma unroll
-                for (int q = 0; q < kMaxRuns; q++) {
-                    lo[q] = 0;
-                    hi[q] = q < nruns && q != w ? 64 : 0;
-                }
-                // every run's probe is read each step, without a branch, so the step's eight LDS
-                // reads are in flight together (a settled or absent run reads a slot it ignores)
-#pragma unroll
-                for (int step = 0; step < 7; step++) {
-                    int mid[kMaxRuns];
-                    uint64_t y[kMaxRuns];
-#pragma unroll
-                    for (int q = 0; q < kMaxRuns; q++) {
-                        mid[q] = (lo[q] + hi[q]) >> 1;
-                        y[q] = sel[64 * q + (mid[q] & 63)];
-                    }
-#pragma unroll
-                    for (int q = 0; q < kMaxRuns; q++) {
-                        const bool open = lo[q] < hi[q], above = y[q] > x;
-                        lo[q] = open && above ? mid[q] + 1 : lo[q];
-                        hi[q] = open && !above ? mid[q] : hi[q];
-                    }
-                }
-                rank = (uint32_t)l;
-#pragma unroll
-                for (int q = 0; q < kMaxRuns; q++)
-                    rank += (uint32_t)lo[q];
-            }
-        }
-        if (x != 0 && rank < (uint32_t)kk)
-            emit(x, rank);
-    }
-    for (int p = kk + i; p < k; p += NT) {
-        rid[p] = 0;
-        rval[p] = -__builtin_inff();
-        if constexpr (STATS)
-            probs[(int64_t)r * k + p] = 0.f;
-    }
-    if (kk == 0 && argmax && i == 0)
-        argmax[r] = 0;
+    float *rprob = STATS ? probs + (int64_t)r * k : nullptr;
+    if (x != 0)
+        emit_survivor<STATS>(x, rank, logits + (int64_t)r * V, idmap, rid, rval, rprob, argmax,
+                             r, ml);
+    emit_padding<STATS>(kk, k, rid, rval, rprob, argmax, r);
 }
 
 struct TopkArgs {
@@ -814,7 +854,126 @@ __global__ __launch_bounds__(64) void zero_tickets(uint32_t *t, int n)
         t[threadIdx.x * kTicketStride] = 0u;
 }
 
+// The merge of the GEMV's cuts (topk.h, dh_draft's fused top-k).
+struct CutArgs {
+    const float *logits;    // [rows][V], as the GEMV wrote them
+    int64_t V, ntiles;      // ntiles: 16-row tiles of the head
+    int k, grid, slots;     // grid: the GEMV's workgroups (the chunks)
+    const uint64_t *keys;   // [rows][grid][slots]
+    const uint64_t *floors; // [rows][grid]
+    const int32_t *idmap;
+    int32_t *ids;
+    float *vals;
+    int32_t *argmax;
+};
+constexpr int kCutPass = 16;   // keys a thread holds in a pass over the re-read chunks
+
+struct CutLds {
+    uint64_t run[DH_MAX_K];          // the best k of the passes so far, by rank
+    uint64_t t;                      // the k-th best key of the cuts (0: fewer than k)
+    uint32_t nfail;
+    uint8_t failed[kCutMaxChunks];   // chunk c's floor beats t
+    uint16_t faillist[kCutMaxChunks];
+};
+
+// One workgroup per row: the k best of the row's cuts (MF keys a thread), the floors checked
+// against the k-th of them, and when a chunk's floor beats it, passes over the other chunks'
+// cuts and those chunks' logits (read back whole), each pass keeping the k best so far.
+template <int MF>
+__global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
+{
+    constexpr int NT = kCutThreads;
+    __shared__ __align__(16) SelectLds<NT> sh;
+    __shared__ __align__(16) MergeLds ml;
+    __shared__ CutLds cl;
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int nfast = a.grid * a.slots;
+    const uint64_t *src = a.keys + (int64_t)r * nfast;
+    // the GEMV before this kernel has ended, so plain loads see its cuts; bounded buffer
+    // loads, all issued together (slots past the cuts read as 0)
+    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)src, (short)0, nfast * 8, kRsrcWord3);
+    uint64_t key[MF];
+#pragma unroll
+    for (int j = 0; j < MF; j++) {
+        const v2u32 q = __builtin_amdgcn_raw_buffer_load_b64(
+            ls, (uint32_t)(j * NT + tid) * 8u, 0, 0);
+        key[j] = ((uint64_t)q.y << 32) | q.x;
+    }
+    const uint64_t fl = tid < a.grid ? a.floors[(int64_t)r * a.grid + tid] : 0ull;
+    if (tid == 0) {
+        cl.nfail = 0;
+        cl.t = 0;
+    }
+    uint64_t x;
+    uint32_t rank;
+    int kk = select_rank<MF, NT>(key, a.k, sh, ml, x, rank);
+    if (kk == a.k && x != 0 && rank == (uint32_t)a.k - 1u)
+        cl.t = x;
+    __syncthreads();
+    const bool fail = tid < a.grid && fl > cl.t;
+    if (tid < a.grid)
+        cl.failed[tid] = fail;
+    if (fail)
+        cl.faillist[atomicAdd(&cl.nfail, 1u)] = (uint16_t)tid;
+    __syncthreads();
+    const uint32_t nf = cl.nfail;
+    const float *lrow = a.logits + (int64_t)r * a.V;
+    int32_t *rid = a.ids + (int64_t)r * a.k;
+    float *rval = a.vals + (int64_t)r * a.k;
+    if (nf != 0) {
+        // the stream of the passes: the cuts of the chunks that stand, then every entry of
+        // the chunks that fell (chunk c did tiles c + j * grid, j < per); at most 8192 +
+        // 1024 * 1024 items, so 32-bit indices
+        const uint32_t per = (uint32_t)((a.ntiles + a.grid - 1) / a.grid);
+        const uint32_t C = per * 16u;
+        const uint32_t total = (uint32_t)nfast + nf * C;
+        auto item = [&](uint32_t q) -> uint64_t {
+            if (q < (uint32_t)nfast)
+                return cl.failed[q / (uint32_t)a.slots] ? 0ull : src[q];
+            const uint32_t e2 = q - (uint32_t)nfast;
+            const uint32_t f = e2 / C, e = e2 - f * C;
+            const int64_t tile = (int64_t)cl.faillist[f] + (int64_t)(e >> 4) * a.grid;
+            const int64_t v = tile * 16 + (e & 15);
+            if (tile >= a.ntiles || v >= a.V)
+                return 0ull;
+            const uint32_t im = order_key(lrow[v]);
+            return im ? entry_key(im, (uint32_t)v) : 0ull;
+        };
+        int nrun = 0;
+        uint32_t q0 = 0;
+        for (;;) {
+            uint64_t key2[kCutPass];
+#pragma unroll
+            for (int j = 0; j < kCutPass; j++) {
+                const int u = j * NT + tid;
+                const uint32_t q = q0 + (uint32_t)(u - nrun);
+                key2[j] = u < nrun ? cl.run[u] : q < total ? item(q) : 0ull;
+            }
+            q0 += (uint32_t)(kCutPass * NT - nrun);
+            kk = select_rank<kCutPass, NT>(key2, a.k, sh, ml, x, rank);
+            if (q0 >= total)
+                break;
+            if (x != 0)
+                cl.run[rank] = x;
+            nrun = kk;
+            __syncthreads();
+        }
+    }
+    if (x != 0)
+        emit_survivor<false>(x, rank, lrow, a.idmap, rid, rval, nullptr, a.argmax, r, ml);
+    emit_padding<false>(kk, a.k, rid, rval, nullptr, a.argmax, r);
+}
+
 }  // namespace
+
+CutShape cut_shape(int k)
+{
+    const double L = k / 256.0;
+    int m = (int)ceil(L + 4.0 * sqrt(L) + 3.0);
+    m = m > k ? k : m < 1 ? 1 : m;
+    return CutShape{m, m + (m / 2 > 4 ? m / 2 : 4)};
+}
 
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
 {
@@ -824,8 +983,65 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
     w.keys_off = 0;   // the chunk lists hold keys that carry both the value and the id
     w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
     w.tickets_off = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
-    w.bytes = w.tickets_off + up((size_t)kSyncKinds * rows * kTicketStride * sizeof(uint32_t));
+    const int64_t ntiles = (vocab + 15) / 16;
+    const size_t gcap = (size_t)(ntiles < kCutMaxChunks ? ntiles : kCutMaxChunks);
+    w.cut_keys_off =
+        w.tickets_off + up((size_t)kSyncKinds * rows * kTicketStride * sizeof(uint32_t));
+    w.cut_floors_off =
+        w.cut_keys_off + up((size_t)rows * gcap * (size_t)cut_shape(k).slots * sizeof(uint64_t));
+    w.bytes = w.cut_floors_off + up((size_t)rows * gcap * sizeof(uint64_t));
     return w;
+}
+
+GemvCut topk_cut(void *ws, int rows, int64_t vocab, int k)
+{
+    const TopkWs w = topk_ws_layout(rows, vocab, k);
+    const CutShape cs = cut_shape(k);
+    char *b = static_cast<char *>(ws);
+    return GemvCut{reinterpret_cast<uint64_t *>(b + w.cut_keys_off),
+                   reinterpret_cast<uint64_t *>(b + w.cut_floors_off), cs.m, cs.slots,
+                   kCutThreads * kCutMaxFast};
+}
+
+hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
+                            const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
+                            void *ws, int grid, hipStream_t stream)
+{
+    const GemvCut cut = topk_cut(ws, rows, vocab, k);
+    const int nfast = grid * cut.slots;
+    if (grid < 1 || grid > kCutMaxChunks || nfast > kCutThreads * kCutMaxFast)
+        return hipErrorInvalidValue;
+    CutArgs a;
+    a.logits = logits;
+    a.V = vocab;
+    a.ntiles = (vocab + 15) / 16;
+    a.k = k;
+    a.grid = grid;
+    a.slots = cut.slots;
+    a.keys = cut.keys;
+    a.floors = cut.floors;
+    a.idmap = idmap;
+    a.ids = ids;
+    a.vals = vals;
+    a.argmax = argmax;
+    const dim3 g(rows), b(kCutThreads);
+    // the smallest instance holding the cuts
+    const int mf = (nfast + kCutThreads - 1) / kCutThreads;
+    if (mf <= 1) return launch(cut_merge<1>, g, b, 0, stream, a);
+    if (mf <= 2) return launch(cut_merge<2>, g, b, 0, stream, a);
+    if (mf <= 3) return launch(cut_merge<3>, g, b, 0, stream, a);
+    if (mf <= 4) return launch(cut_merge<4>, g, b, 0, stream, a);
+    if (mf <= 6) return launch(cut_merge<6>, g, b, 0, stream, a);
+    if (mf <= 8 || kCutMaxFast <= 8) return launch(cut_merge<8>, g, b, 0, stream, a);
+    if constexpr (kCutMaxFast > 8) {
+        if (mf <= 12) return launch(cut_merge<12>, g, b, 0, stream, a);
+        if (mf <= 16 || kCutMaxFast <= 16) return launch(cut_merge<16>, g, b, 0, stream, a);
+    }
+    if constexpr (kCutMaxFast > 16) {
+        if (mf <= 24) return launch(cut_merge<24>, g, b, 0, stream, a);
+        return launch(cut_merge<32>, g, b, 0, stream, a);
+    }
+    return hipErrorInvalidValue;
 }
 
 uint32_t *topk_tickets(void *ws, int rows, int64_t vocab, int k)

@@ -6,7 +6,12 @@ being concentrated in one place:
  * planted heads whose best rows crowd into one 16-row tile (one GEMV workgroup, one top-k
    chunk holds up to 16 of a row's top-k): distinct values and exact ties (lower id first),
    and a row with fewer eligible logits than k;
- * the two-stage and the mapped (subset) drafts.
+ * the two-stage and the mapped (subset) drafts;
+ * for dh_draft's fused top-k (up to 16 rows: each GEMV workgroup leaves a short cut of its
+   logits, a per-row merge checks it and reads back the chunks whose cut may be short): rows
+   of exact ties everywhere (every cut empty, the whole row read back in passes), runs of
+   consecutive best ids spanning many tiles (one chunk per tile holding 16 of the k), and
+   k = 512 over 16 rows.
 """
 import numpy as np
 import pytest
@@ -128,3 +133,72 @@ def test_draft_topk_two_stage_and_mapped(k):
     assert np.array_equal(host(mo["ids"]), host(mi))
     assert host(mo["vals"]).tobytes() == host(mv).tobytes()
     assert np.array_equal(host(mo["draft"]), host(ma))
+
+
+@pytest.mark.parametrize("k", [1, 64, 512])
+def test_draft_topk_all_tied_rows(k):
+    """Rows of zero activations: every logit is a zero (ties everywhere), so the top-k is ids
+    0..k-1; every GEMV workgroup's cut is empty and the merge reads the row back in passes
+    (70,001 logits: several passes of 16,384)."""
+    need_gpu()
+    V, H = 70001, 256
+    say(f"all-tied rows k={k}")
+    w = synth.random_head(V, H, seed=151, std=0.02)
+    x = np.stack([np.zeros(H, np.uint16), synth.random_acts(1, H, seed=152)[0],
+                  np.zeros(H, np.uint16)])
+    gh = dh.Head(dh.BF16, dev_u16(w))
+    out = draft_vs_topk(gh, dev_u16(x), k, tile=True)
+    ids, vals = host(out["ids"]), host(out["vals"])
+    for r in (0, 2):
+        assert ids[r].tolist() == list(range(k))
+        assert np.all(vals[r] == 0)
+    want = oracle.gemv(oracle.FMT_BF16, w, None, x)
+    tols = check_logits(host(out["logits"]), want)
+    check_topk(ids, vals, want, k, tols)
+
+
+def clustered_head(V, H, lo, n, seed):
+    """A head whose rows lo..lo+n-1 are the activation row `base` scaled by 1 + j/256 (in bf16):
+    for x = base they are the row's n largest logits, over n / 16 tiles."""
+    w = synth.random_head(V, H, seed=seed, std=0.02).copy()
+    base = synth.random_acts(1, H, seed=seed + 1)[0]
+    scale = 1.0 + np.arange(n, dtype=np.float32) / 256
+    w[lo:lo + n] = synth.to_bf16_bits(synth.bf16_bits_to_f32(base)[None, :] * scale[:, None])
+    return w, base
+
+
+@pytest.mark.parametrize("k,n", [(64, 64), (64, 200), (512, 600)])
+def test_draft_topk_clustered_ids(k, n):
+    """The k best ids of a row are consecutive and span many 16-row tiles, so many GEMV
+    workgroups each hold 16 of them, more than their cuts keep: the merge reads those
+    workgroups' logits back and still returns the exact top-k, all from the planted run."""
+    need_gpu()
+    V, H, lo = 60000, 512, 1000
+    say(f"clustered ids k={k} n={n}")
+    w, base = clustered_head(V, H, lo, n, seed=161 + k)
+    x = np.stack([base, synth.random_acts(1, H, seed=162)[0]])
+    gh = dh.Head(dh.BF16, dev_u16(w))
+    out = draft_vs_topk(gh, dev_u16(x), k, tile=True)
+    want = oracle.gemv(oracle.FMT_BF16, w, None, x)
+    tols = check_logits(host(out["logits"]), want)
+    check_topk(host(out["ids"]), host(out["vals"]), want, k, tols)
+    # the planted rows' logits dwarf the others' (their order within the run is the oracle
+    # check's: bf16 rounding of base * (1 + j/256) ties or swaps neighbours)
+    top = host(out["ids"])[0]
+    assert np.all((top >= lo) & (top < lo + n))
+    if k == n:
+        assert sorted(top.tolist()) == list(range(lo, lo + n))
+
+
+@pytest.mark.parametrize("fmt", ["block", "row"])
+def test_draft_topk_512_sixteen_rows(fmt):
+    need_gpu()
+    V, H, R, k = 129280, 1024, 16, 512
+    say(f"top-512 of 16 rows {fmt}")
+    w = synth.random_head(V, H, seed=171, std=0.02)
+    x = synth.random_acts(R, H, seed=172)
+    gh, (ow, osc) = make_heads(fmt, w)
+    out = draft_vs_topk(gh, dev_u16(x), k, tile=True)
+    want = oracle.gemv(FMTS[fmt][1], ow, osc, x)
+    tols = check_logits(host(out["logits"]), want)
+    check_topk(host(out["ids"]), host(out["vals"]), want, k, tols)

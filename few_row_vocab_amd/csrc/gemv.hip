@@ -318,6 +318,103 @@ __device__ __forceinline__ void cut_rows(const GemvArgs &a, const uint32_t *stag
     }
 }
 
+// The writer and the draft's cut when every wave owns whole rows (R > nw / 2): wave w writes
+// the logits of rows w, w + nw, ... and cuts each (as cut_rows: the same bins, cut and floor),
+// with no workgroup barrier.  Lane l takes entries l + 64 j (tiles l / 16 + 4 j, head rows
+// 16 (blockIdx.x + t gridDim.x) + l % 16); the range stays in registers, the wave's own 256
+// histogram words and cut counter sit in ws (the free reduction buffer), and the floor is a
+// wave reduction.  The wave's LDS operations complete in order between its passes.
+template <int SST>
+__device__ __forceinline__ void write_cut_own_rows(const GemvArgs &a, float *stage, int ntl,
+                                                   uint32_t *ws)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    uint32_t *hist = ws + wave * 256;
+    uint32_t *cnt = ws + 16 * 256 + wave;
+    const int t0 = lane >> 4, i = lane & 15;
+    const uint32_t id0 = ((uint32_t)blockIdx.x + (uint32_t)t0 * gridDim.x) * 16u + (uint32_t)i;
+    const uint32_t idstep = 4u * gridDim.x * 16u;
+    const int slots = a.cut_slots;
+    for (int r = wave; r < a.R; r += nw) {
+        float *srow = stage + 16 * r + i;
+        const uint32_t *irow = reinterpret_cast<const uint32_t *>(srow);
+        // 1: the row's logits written, their images left in the stage; the range
+        uint32_t mn = ~0u, mx = 0;
+        {
+            uint32_t id = id0;
+            for (int t = t0; t < ntl; t += 4, id += idstep) {
+                float *sp = srow + t * SST;
+                uint32_t im = 0;
+                if ((int64_t)id < a.V) {
+                    const float s = row_scaled(a, id, *sp);
+                    store_out(a, r, id, s);
+                    im = order_key(s);
+                }
+                *reinterpret_cast<uint32_t *>(sp) = im;
+                mn = im != 0 && im < mn ? im : mn;
+                mx = im > mx ? im : mx;
+            }
+        }
+        wave_min_max32(mn, mx);
+        uint64_t *out = a.cut_keys + ((int64_t)r * gridDim.x + blockIdx.x) * slots;
+        uint64_t *floor = a.cut_floors + (int64_t)r * gridDim.x + blockIdx.x;
+        if (mx == 0) {                             // no eligible entry
+            for (int q = lane; q < slots; q += kWave)
+                out[q] = 0;
+            if (lane == 0)
+                *floor = 0;
+            continue;
+        }
+        const float lo = image_float(mn);
+        const float scale = 256.0f / (image_float(mx) - lo);
+        auto bin_of = [&](uint32_t x) -> uint32_t {
+            return (uint32_t)fminf((image_float(x) - lo) * scale, 255.0f);
+        };
+        reinterpret_cast<uint4 *>(hist)[lane] = uint4{0u, 0u, 0u, 0u};
+        if (lane == 0)
+            *cnt = 0;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // 2: the histogram
+#pragma unroll 2
+        for (int t = t0; t < ntl; t += 4) {
+            const uint32_t im = irow[t * SST];
+            if (im != 0)
+                atomicAdd(&hist[bin_of(im)], 1u);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // 3: the cut (every key when at most m, bins >= d, or bins > d) to the slots
+        uint32_t d, above, count;
+        const uint32_t total = locate<256>(hist, (uint32_t)a.cut_m, d, above, count);
+        bool all = total <= (uint32_t)a.cut_m;
+        uint32_t dmin = 0;
+        if (!all) {
+            dmin = above + count <= (uint32_t)slots ? d : d + 1;
+            all = dmin == d && above + count == total;
+        }
+        uint64_t kmin = ~0ull, kmax = 0;
+        {
+            uint32_t id = id0;
+#pragma unroll 2
+            for (int t = t0; t < ntl; t += 4, id += idstep) {
+                const uint32_t im = irow[t * SST];
+                if (im != 0 && (all || bin_of(im) >= dmin)) {
+                    const uint64_t key = entry_key(im, id);
+                    out[atomicAdd(cnt, 1u)] = key;
+                    kmin = key < kmin ? key : kmin;
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint32_t placed = *cnt;
+        for (int q = (int)placed + lane; q < slots; q += kWave)
+            out[q] = 0;
+        wave_min_max(kmin, kmax);                  // kmin: the cut's smallest key (~0: none)
+        if (lane == 0)
+            *floor = all ? 0ull : kmin;
+    }
+}
+
 // FULL: every wave's 64-column blocks lie inside the row (H a multiple of 64 and the
 // blocks split evenly over the waves), so no load needs a guard.
 // TR: 16-row MFMA groups per tile (a tile is 16 * TR head rows, inside one 32-row block
@@ -580,6 +677,12 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     static_assert(TR == 1, "the writer below assumes one 16-row group per tile");
     const bool cut = a.cut_m > 0 && NB == 1 && (int)gridDim.x <= kCutMaxChunks &&
                      (int)gridDim.x * a.cut_slots <= a.cut_max;
+    // from nw / 2 rows up every wave owns whole rows: it writes and cuts them alone
+    if (cut && (a.R << 1) > nw) {
+        static_assert(sizeof(red) >= 16 * 256 * sizeof(uint32_t) + 256, "the cut's LDS fits");
+        write_cut_own_rows<SST>(a, stage, it + 1, reinterpret_cast<uint32_t *>(&red[0][0][0][0][0]));
+        return;
+    }
     const int per_tile = a.R * 16;
     // the cut: the images' range of activation rows 4 q + lane / 16, q < 4, as they are written
     uint32_t rmn[4] = {~0u, ~0u, ~0u, ~0u}, rmx[4] = {0u, 0u, 0u, 0u};

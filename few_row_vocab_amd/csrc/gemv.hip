@@ -339,21 +339,37 @@ __device__ __forceinline__ void write_cut_own_rows(const GemvArgs &a, float *sta
     for (int r = wave; r < a.R; r += nw) {
         float *srow = stage + 16 * r + i;
         const uint32_t *irow = reinterpret_cast<const uint32_t *>(srow);
-        // 1: the row's logits written, their images left in the stage; the range
+        // 1: the row's logits written, their images left in the stage; the range.  Four
+        // entries at a time, their sums and row scales loaded before any of their stores
+        // (which the compiler may not move a row-scale load past)
         uint32_t mn = ~0u, mx = 0;
         {
             uint32_t id = id0;
-            for (int t = t0; t < ntl; t += 4, id += idstep) {
-                float *sp = srow + t * SST;
-                uint32_t im = 0;
-                if ((int64_t)id < a.V) {
-                    const float s = row_scaled(a, id, *sp);
-                    store_out(a, r, id, s);
-                    im = order_key(s);
+            for (int t = t0; t < ntl; t += 16, id += 4 * idstep) {
+                float sv[4], rs[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int tu = t + 4 * u;
+                    const uint32_t idu = id + (uint32_t)u * idstep;
+                    sv[u] = tu < ntl ? srow[tu * SST] : 0.f;
+                    rs[u] = a.rscale && tu < ntl && (int64_t)idu < a.V ? a.rscale[idu] : 1.0f;
                 }
-                *reinterpret_cast<uint32_t *>(sp) = im;
-                mn = im != 0 && im < mn ? im : mn;
-                mx = im > mx ? im : mx;
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int tu = t + 4 * u;
+                    const uint32_t idu = id + (uint32_t)u * idstep;
+                    if (tu < ntl) {
+                        uint32_t im = 0;
+                        if ((int64_t)idu < a.V) {
+                            const float s = a.rscale ? sv[u] * rs[u] : sv[u];   // row_scaled
+                            store_out(a, r, idu, s);
+                            im = order_key(s);
+                        }
+                        *reinterpret_cast<uint32_t *>(srow + tu * SST) = im;
+                        mn = im != 0 && im < mn ? im : mn;
+                        mx = im > mx ? im : mx;
+                    }
+                }
             }
         }
         wave_min_max32(mn, mx);
@@ -688,6 +704,10 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     uint32_t rmn[4] = {~0u, ~0u, ~0u, ~0u}, rmx[4] = {0u, 0u, 0u, 0u};
     for (int t = wave; t <= it; t += nw) {
         const int64_t v0 = (int64_t)(blockIdx.x + t * gridDim.x) * TILE;
+        // a lane's head row is v0 + lane % 16 for every activation row it writes, so its row
+        // scale is loaded once, before the stores (which the compiler may not move it past)
+        const int64_t vl = v0 + (lane & 15);
+        const float rs = a.rscale && vl < V ? a.rscale[vl] : 1.0f;
 #pragma unroll
         for (int q = 0; q < 32 * 16 / kWave; q++) {
             const int o = lane + kWave * q;
@@ -697,7 +717,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
                 float *sp = &stage[t * SST + c * 16 + i];
                 uint32_t im = 0;
                 if (v < V) {
-                    const float s = row_scaled(a, v, *sp);
+                    const float s = a.rscale ? *sp * rs : *sp;   // row_scaled
                     store_out(a, c, v, s);
                     im = order_key(s);               // the cut ranks the logits as written
                 }

@@ -481,15 +481,22 @@ def two_stage_sweep(dh, torch, wd, xd, V, H, n, dense=None):
     gen = torch.Generator(device=xd.device).manual_seed(404)
     sets = [torch.randint(0, V, (R, k), dtype=torch.int32, device=xd.device, generator=gen)
             for _ in range(4)]
+    # dh_rescore_sync (one launch: the candidates' workgroups pick the drafts), and
+    # dh_rescore (a second, small kernel picks them)
+    sync = dh.rescore_sync_buffer(xd.device)
     s_cold = back_to_back_us(lambda i: dh.rescore(dense, xd, sets[i % 4], exact=o["exact"],
-                                                   draft=o["draft"]), n)
+                                                   draft=o["draft"], sync=sync), n)
+    s_cold2 = back_to_back_us(lambda i: dh.rescore(dense, xd, sets[i % 4], exact=o["exact"],
+                                                    draft=o["draft"]), n)
     b = algorithmic_bytes("fp8_row", V, H, R) + R * k * H * 2
     log(f"two-stage: draft {d['median']:.1f} us per-call, {dbb:.1f} us back to back (gemv "
         f"{g['median']:.1f}, topk {t['median']:.1f}, rescore {s['median']:.1f}); rescore over "
-        f"rotated random candidates {s_cold:.1f} us")
+        f"rotated random candidates {s_cold:.1f} us (two launches {s_cold2:.1f})")
     return {"rows": R, "cand_k": k, "stage1_copies_rotated": NCOPY, "dh_draft_us": d,
             "dh_gemv_us": g, "dh_topk_us": t, "dh_rescore_us": s,
             "dh_draft_back_to_back_us": dbb, "dh_rescore_rotated_ids_us": s_cold,
+            "rescore_rotated_entry": "dh_rescore_sync (one launch)",
+            "dh_rescore_two_launch_rotated_ids_us": s_cold2,
             "rescore_rotated_GBps": round(R * k * H * 2 / (s_cold * 1e-6) / 1e9, 1),
             "draft_GBps_upper_bytes": round(b / (dbb * 1e-6) / 1e9, 1)}
 

@@ -371,6 +371,28 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                                             draft, (hipStream_t)stream));
 }
 
+dh_status dh_rescore_sync(const dh_head *dense, const uint16_t *x, int32_t rows,
+                          const int32_t *cand_ids, int32_t cand_k, float *exact,
+                          int32_t *draft, uint32_t *sync, void *stream)
+{
+    DH_TRY(check_rescore(dense, x, rows, cand_ids, cand_k, exact, draft));
+    if (!sync || !aligned(sync, 256))
+        return DH_ERR_INVALID;
+    const Span ss = span(sync, DH_RESCORE_SYNC_BYTES);
+    const Span others[] = {span(exact, (size_t)rows * cand_k * 4), span(draft, (size_t)rows * 4),
+                           span(cand_ids, (size_t)rows * cand_k * 4),
+                           span(x, (size_t)rows * (size_t)dense->hidden * 2),
+                           head_weight(*dense)};
+    for (const Span &o : others)
+        if (overlap(ss, o))
+            return DH_ERR_INVALID;
+    // the rows' ticket lines, then their best-key lines (2 * rows lines of 256 bytes)
+    static_assert(2 * DH_MAX_ROWS * dh::kTicketStride * 4 <= DH_RESCORE_SYNC_BYTES,
+                  "the sync buffer holds two lines a row");
+    return device_status(dh::launch_rescore(*dense, x, rows, cand_ids, nullptr, cand_k, exact,
+                                            draft, (hipStream_t)stream, sync));
+}
+
 // dh_draft, dh_draft_mapped, dh_draft_lowrank and dh_draft_noalloc: with an id map the head
 // is a subset head whose entry j is vocabulary id idmap[j], and the dense head spans the
 // whole vocabulary; with `down` the stage-1 head is low rank: t = bf16(x down^T), and

@@ -44,9 +44,10 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
                          const GemvCut *cut = nullptr, int *grid_used = nullptr);
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
 
-// sync: NULL (a second kernel picks the drafts), or the rescore's zeroed sync lines in a
-// top-k workspace (ticket lines, then best-key lines, `rows` of each, kTicketStride words
-// apart): the candidates' last workgroup of a row picks its draft.
+// sync: NULL (a second kernel picks the drafts), or zeroed sync lines (ticket lines, then
+// best-key lines, `rows` of each, kTicketStride words apart: a top-k workspace's, or
+// dh_rescore_sync's buffer): the candidates' last workgroup of a row picks its draft and
+// sets the row's two lines back to zero.
 hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
                           const int32_t *cand_ids, const float *cand_vals, int cand_k,
                           float *exact, int32_t *draft, hipStream_t stream,

@@ -5,16 +5,23 @@
 // the candidates' id map).
 //
 // Design: the work is a gather of rows*cand_k head rows (10 KB each at H = 5120) -- memory
-// bound, with one activation row per gathered head row, so plain FP32 FMAs on the vector
-// ALUs.  One wave per (row, slot), four waves a workgroup, all of one activation row: the
-// workgroup stages that row in LDS once (every wave reading it from L2 doubled the cache
-// traffic of the gather), while each wave's first round of head-row loads is already in
-// flight.  Each lane reads 16 bytes of the head row per step (a wave covers 1 KB of the row
-// per load), with five steps in flight, sums its products in order, and the wave sums lanes
-// with a fixed butterfly.  The winning candidate is picked either by a second small kernel,
-// or -- inside dh_draft, which has a workspace -- by the candidates' workgroups themselves:
-// each takes the 64-bit maximum of its candidates' (exact logit, token id) keys into the
-// row's best word, then a ticket, and the row's last workgroup writes the draft.
+// bound, with one activation row per gathered head row, so no matrix instructions: each lane
+// takes 32-bit pairs of bf16 products with the two-way bf16 dot instruction (v_dot2c_f32_bf16,
+// fp32 accumulation).  One wave per (row, slot), four waves a workgroup, all of one
+// activation row: the workgroup stages that row in LDS once (every wave reading it from L2
+// doubled the cache traffic of the gather).  The activation loads are issued first, then the
+// wave's first round of head-row loads, so the LDS stores wait only for the activations.
+// Each lane reads 16 bytes of the head row per step (a wave covers 1 KB of the row per load),
+// with five steps in flight, sums its products in order, and the wave sums lanes with a fixed
+// butterfly.  The winning candidate is picked either by a second small kernel, or -- when the
+// call brings zeroed sync lines (dh_draft's workspace, dh_rescore_sync's buffer) -- by the
+// candidates' workgroups themselves: each takes the 64-bit maximum of its candidates' (exact
+// logit, token id) keys into the row's best word, then a ticket, and the row's last workgroup
+// writes the draft and sets both words back to zero.  (A ticket per wave instead of per
+// workgroup was slower, 22.3 us against 15.8 for 16 x 512 candidates: four times the atomics
+// on each row's two lines.  Eight waves a workgroup measured the same as four.)
+#include <algorithm>
+
 #include "dh_internal.h"
 #include "keys.h"
 #include "launch.h"
@@ -24,17 +31,26 @@ namespace dh {
 namespace {
 
 constexpr int kRescoreWaves = 4;
-// 512-column steps a lane has in flight: a 10 KB row (H = 5120) is two rounds.  Over four
-// rotated sets of 16 x 512 random candidates (a cold gather) five measured 18.4 us, two
-// 18.4-18.7, four 19.0 and eight 20.1: with 32 waves a compute unit, more in flight only
-// queues.
+// 512-column steps a lane has in flight.  Over four rotated sets of 16 x 512 random
+// candidates (a cold gather), one round of five steps at a time measured best; eight or ten
+// steps were slower, with more waves than registers allow at once (20.7, 20.6 us against
+// 18.3), and so was a second round kept in flight (18.7).
 constexpr int kSteps = 5;
+// activation vectors a thread loads before the head rows: 8192 columns a workgroup
+constexpr int kXPre = 8192 / (8 * kRescoreWaves * kWave);
+constexpr size_t kXLds = (size_t)kXPre * kRescoreWaves * kWave * 16;   // 16 KiB
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + the two products of a 32-bit pair of bf16 values each
+__device__ inline float dot2(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
 
 struct RescoreArgs {
     const uint16_t *W;      // dense bf16 head [V][H]
@@ -56,21 +72,35 @@ struct RescoreArgs {
 template <bool PICK>
 __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(RescoreArgs a)
 {
-    extern __shared__ __align__(16) uint16_t xs[];   // the activation row, H of them
+    extern __shared__ __align__(16) uint16_t xs[];   // the activation row (H, at least 8192)
     __shared__ uint64_t wbest[kRescoreWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
     const int slot = blockIdx.x * kRescoreWaves + wave;
     const int r = blockIdx.y;
     const int H = a.H;
     const int64_t t = (int64_t)r * a.ck + slot;
+    // the activation row's first kXPre * 256 16-byte vectors (bounded: past the row, 0),
+    // loaded before anything else, so that neither the candidate's id nor its head row waits
+    // on them
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.x + (int64_t)r * H), (short)0, H * 2, kRsrcWord3);
+    u32x4 xv[kXPre];
+#pragma unroll
+    for (int u = 0; u < kXPre; u++)
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+            xrs, (uint32_t)(u * kRescoreWaves * kWave + threadIdx.x) * 16u, 0, 0);
     const bool live = slot < a.ck;
-    const int64_t id = live ? a.cand[t] : -1;
+    // the wave's candidate (uniform over the wave: taken from lane 0, so the head row's
+    // buffer descriptor is scalar)
+    const int64_t id = __builtin_amdgcn_readfirstlane(live ? a.cand[t] : -1);
     // a pad of the stage-1 list is not a candidate; an id outside the head is not read
-    const bool pad = live && a.cand_vals && !(a.cand_vals[t] > -__builtin_inff());
+    const bool pad = __builtin_amdgcn_readfirstlane(
+        live && a.cand_vals && !(a.cand_vals[t] > -__builtin_inff()));
     const bool read = live && !pad && id >= 0 && id < a.V;
 
-    // bounded buffer loads (bytes past the row read as 0, adding nothing), kSteps steps of
-    // 512 columns a round; the first round is issued before the activations are staged
+    // the head row in rounds of kSteps steps of 512 columns (bounded buffer loads: bytes past
+    // the row read as 0, adding nothing)
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(a.W + (read ? id : 0) * H), (short)0, read ? H * 2 : 0, kRsrcWord3);
     u32x4 wq[kSteps];
@@ -81,33 +111,30 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(RescoreArgs
                 wrs, (uint32_t)(h0 + j * 8 * kWave + lane * 8) * 2u, 0, 0);
     };
     issue(0);
+    // (unconditional: the LDS holds at least kXPre * 256 vectors)
+#pragma unroll
+    for (int u = 0; u < kXPre; u++)
+        reinterpret_cast<u32x4 *>(xs)[u * kRescoreWaves * kWave + threadIdx.x] = xv[u];
+    const int nx = H / 8;
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(a.x + (int64_t)r * H);
-    for (int i = threadIdx.x; i < H / 8; i += kRescoreWaves * kWave)
-        reinterpret_cast<u32x4 *>(xs)[i] = xg[i];
+    for (int i = kXPre * kRescoreWaves * kWave + threadIdx.x; i < nx; i += kRescoreWaves * kWave)
+        reinterpret_cast<u32x4 *>(xs)[i] = xg[i];   // H > 8192
     __syncthreads();
 
     float acc = 0.f;
     constexpr int kRound = kSteps * 8 * kWave;
     for (int h0 = 0; h0 < H; h0 += kRound) {
-        u32x4 cur[kSteps];
-#pragma unroll
-        for (int j = 0; j < kSteps; j++)
-            cur[j] = wq[j];
-        if (h0 + kRound < H)
-            issue(h0 + kRound);          // the next round in flight while this one is summed
+        if (h0)
+            issue(h0);
 #pragma unroll
         for (int j = 0; j < kSteps; j++) {
             const int c = h0 + j * 8 * kWave + lane * 8;
             const u32x4 xq = c < H ? *reinterpret_cast<const u32x4 *>(&xs[c])
                                    : u32x4{0u, 0u, 0u, 0u};
-            acc = __builtin_fmaf(lo_bf16(xq.x), lo_bf16(cur[j].x), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.x), hi_bf16(cur[j].x), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.y), lo_bf16(cur[j].y), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.y), hi_bf16(cur[j].y), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.z), lo_bf16(cur[j].z), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.z), hi_bf16(cur[j].z), acc);
-            acc = __builtin_fmaf(lo_bf16(xq.w), lo_bf16(cur[j].w), acc);
-            acc = __builtin_fmaf(hi_bf16(xq.w), hi_bf16(cur[j].w), acc);
+            acc = dot2(xq.x, wq[j].x, acc);
+            acc = dot2(xq.y, wq[j].y, acc);
+            acc = dot2(xq.z, wq[j].z, acc);
+            acc = dot2(xq.w, wq[j].w, acc);
         }
     }
     for (int off = 32; off > 0; off >>= 1)
@@ -133,10 +160,14 @@ __global__ __launch_bounds__(kRescoreWaves * kWave) void rescore_dot(RescoreArgs
                 atomicMax((unsigned long long *)bw, (unsigned long long)m);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the maximum is in place
             const uint32_t nb = (uint32_t)gridDim.x;   // the row's workgroups
-            if (atomicAdd(&a.tickets[(int64_t)r * kTicketStride], 1u) == nb - 1u) {
+            uint32_t *tw = &a.tickets[(int64_t)r * kTicketStride];
+            if (atomicAdd(tw, 1u) == nb - 1u) {
+                // every other workgroup of the row is done with both words
                 const uint64_t b = __hip_atomic_load(bw, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
                 a.draft[r] = b ? (int32_t)key_id(b) : 0;
+                __hip_atomic_store(bw, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(tw, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -217,7 +248,8 @@ hipError_t launch_rescore(const dh_head &dense, const uint16_t *x, int rows,
     a.best = sync ? reinterpret_cast<uint64_t *>(sync + (size_t)rows * kTicketStride) : nullptr;
     a.draft = draft;
     const dim3 grid((cand_k + kRescoreWaves - 1) / kRescoreWaves, rows);
-    const size_t lds = (size_t)a.H * sizeof(uint16_t);   // up to 64 KiB (H <= 32768)
+    // the activation row, at least the kXPre vectors a thread stores (up to 64 KiB)
+    const size_t lds = std::max((size_t)a.H * sizeof(uint16_t), kXLds);
     static int lds_set[64];                              // per device: the limit raised
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

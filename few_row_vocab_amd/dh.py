@@ -30,6 +30,7 @@ MAX_HIDDEN_WIDE = 5120   # 4096 for a row-major bf16 head
 MAX_K = 512
 MAX_HIDDEN = 32768
 MAX_VOCAB = 262144
+RESCORE_SYNC_BYTES = MAX_ROWS * 2 * 256   # DH_RESCORE_SYNC_BYTES
 
 STATUS = {0: "DH_OK", 1: "DH_ERR_INVALID", 2: "DH_ERR_UNSUPPORTED", 3: "DH_ERR_WORKSPACE",
           4: "DH_ERR_DEVICE", 5: "DH_ERR_SCRATCH"}
@@ -64,6 +65,7 @@ def lib():
         L.dh_gemv.argtypes = [hp, vp, i32, vp, vp]
         L.dh_topk.argtypes = [vp, i32, i64, i32, vp, vp, vp, vp, sz, vp]
         L.dh_rescore.argtypes = [hp, vp, i32, vp, i32, vp, vp, vp]
+        L.dh_rescore_sync.argtypes = [hp, vp, i32, vp, i32, vp, vp, vp, vp]
         L.dh_draft.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dh_draft_noalloc.argtypes = [hp, hp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
         L.dh_quantize.argtypes = [i32, vp, i64, i64, vp, vp, vp]
@@ -84,7 +86,8 @@ def lib():
         L.dh_workspace_bytes.restype = sz
         L.dh_status_string.argtypes = [i32]
         L.dh_status_string.restype = c.c_char_p
-        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_draft, L.dh_draft_noalloc,
+        for f in (L.dh_gemv, L.dh_topk, L.dh_rescore, L.dh_rescore_sync, L.dh_draft,
+                  L.dh_draft_noalloc,
                   L.dh_quantize,
                   L.dh_gather_rows, L.dh_topk_mapped, L.dh_draft_mapped, L.dh_linear,
                   L.dh_draft_lowrank, L.dh_topk_softmax, L.dh_sample, L.dh_tile_head,
@@ -385,9 +388,15 @@ def gather_rows(head: Head, ids, out: Optional[Head] = None, stream=None):
     return Head(head.format, weight, scale)
 
 
+def rescore_sync_buffer(device="cuda"):
+    """A zero-filled sync buffer for rescore(..., sync=) (dh_rescore_sync)."""
+    return torch.zeros(RESCORE_SYNC_BYTES, dtype=torch.uint8, device=device)
+
+
 @_on_stream
-def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
-    """(exact fp32 [R][cand_k], draft int32 [R])."""
+def rescore(dense: Head, x, cand_ids, exact=None, draft=None, sync=None, stream=None):
+    """(exact fp32 [R][cand_k], draft int32 [R]).  With `sync` (rescore_sync_buffer()), one
+    launch: dh_rescore_sync; calls sharing it must be ordered (one stream)."""
     _want(cand_ids, torch.int32, "cand_ids")
     R, ck = cand_ids.shape
     _shaped(x, (R, dense.hidden), BF16_BITS, "x")
@@ -397,8 +406,13 @@ def rescore(dense: Head, x, cand_ids, exact=None, draft=None, stream=None):
     _shaped(exact, (R, ck), torch.float32, "exact")
     _shaped(draft, (R,), torch.int32, "draft")
     h = dense._c()
-    _check(lib().dh_rescore(ctypes.byref(h), _ptr(x), R, _ptr(cand_ids), ck, _ptr(exact),
-                            _ptr(draft), _stream(stream)))
+    if sync is not None:
+        _shaped(sync, (RESCORE_SYNC_BYTES,), torch.uint8, "sync")
+        _check(lib().dh_rescore_sync(ctypes.byref(h), _ptr(x), R, _ptr(cand_ids), ck,
+                                     _ptr(exact), _ptr(draft), _ptr(sync), _stream(stream)))
+    else:
+        _check(lib().dh_rescore(ctypes.byref(h), _ptr(x), R, _ptr(cand_ids), ck, _ptr(exact),
+                                _ptr(draft), _stream(stream)))
     return exact, draft
 
 

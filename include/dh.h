@@ -175,6 +175,19 @@ dh_status dh_rescore(const dh_head *dense, const uint16_t *x, int32_t rows,
                      const int32_t *cand_ids, int32_t cand_k, float *exact, int32_t *draft,
                      void *stream);
 
+/* dh_rescore_sync -- dh_rescore in one launch, with the same results bit for bit: the
+ * candidates' workgroups pick the draft themselves (dh_rescore runs a second, small kernel
+ * for the pick), counting finished workgroups in `sync`.  Same passages as dh_rescore.
+ * sync: device, 256-byte aligned, DH_RESCORE_SYNC_BYTES bytes, owned by the caller; it must
+ * be all zero when the call's kernel starts -- zero-fill it once when it is allocated: every
+ * call leaves it all zero again when its kernel ends.  Calls that share a sync buffer must
+ * not run at the same time (order them on one stream).  It must not overlap any other
+ * argument's buffer.  Other arguments and errors as dh_rescore. */
+#define DH_RESCORE_SYNC_BYTES (DH_MAX_ROWS * 2 * 256)
+dh_status dh_rescore_sync(const dh_head *dense, const uint16_t *x, int32_t rows,
+                          const int32_t *cand_ids, int32_t cand_k, float *exact,
+                          int32_t *draft, uint32_t *sync, void *stream);
+
 /* dh_draft -- the whole projection in one call: dh_gemv, then dh_topk (k), then -- when
  * `dense` is not NULL -- the two-stage rescore of the top k candidates.  [TFE] two_stage
  * commit note: a draft pass's vocabulary head gives each row its draft, either the argmax

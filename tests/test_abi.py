@@ -23,7 +23,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     L = dh.lib()
     names = declared_functions()
-    assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_draft", "dh_quantize",
+    assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_rescore_sync", "dh_draft",
+                          "dh_quantize",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
                           "dh_topk_mapped", "dh_draft_mapped", "dh_linear",
                           "dh_draft_lowrank", "dh_topk_softmax", "dh_sample"}
@@ -175,6 +176,37 @@ def test_rescore_and_draft_refusals(no_device):
     assert draft(wsb=100) == 3
     assert draft(rows=33) == 2
     for b in (ids, vals, ex, dr, lg):
+        assert b.untouched()
+
+
+def test_rescore_sync_refusals(no_device):
+    """dh_rescore_sync refuses what dh_rescore refuses, and a missing, misaligned or
+    overlapping sync buffer, on the host."""
+    R, V, H, k = 2, 600, 64, 16
+    wd, x, ids, ex, dr = (HostBuf(V * H * 2), HostBuf(R * H * 2), HostBuf(R * k * 4),
+                          HostBuf(R * k * 4), HostBuf(R * 4))
+    sync = HostBuf(dh.RESCORE_SYNC_BYTES)
+    big = HostBuf(dh.RESCORE_SYNC_BYTES + 4096)
+    L = dh.lib()
+    dense = head(dh.BF16, V, H, wd)
+
+    def call(d=dense, rows=R, kk=k, exact=ex, sp=None):
+        return L.dh_rescore_sync(ctypes.byref(d), x.p, rows, ids.p, kk, exact.p, dr.p,
+                                 sync.p if sp is None else sp, None)
+
+    assert call(d=head(dh.FP8_ROW, V, H, wd, HostBuf(V * 4))) == 1   # dense head not bf16
+    assert call(d=head(dh.BF16 | dh.TILED, V, H, wd)) == 1            # tiled dense head
+    assert call(kk=0) == 1 and call(kk=513) == 2
+    assert call(rows=0) == 1 and call(rows=33) == 2
+    assert call(exact=ids) == 1                                        # exact overlaps ids
+    assert L.dh_rescore_sync(ctypes.byref(dense), x.p, R, ids.p, k, ex.p, dr.p, None,
+                             None) == 1                                # no sync buffer
+    assert call(sp=ctypes.c_void_p(big.a.ctypes.data + 16)) == 1       # misaligned
+    assert call(sp=ex.p) == 1                                          # sync overlaps exact
+    assert call(sp=dr.p) == 1                                          # sync overlaps draft
+    assert call(sp=wd.p) == 1                                          # sync in the weight
+    assert call(sp=x.p) == 1                                           # sync overlaps x
+    for b in (ids, ex, dr, sync, big):
         assert b.untouched()
 
 

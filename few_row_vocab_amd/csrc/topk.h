@@ -70,25 +70,31 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k);
 struct CutShape {
     int m, slots;
 };
-CutShape cut_shape(int k);
+// With `chunks` chunks a row (the GEMV's about 256 workgroups by default): L = k / chunks.
+constexpr int kCutShapeChunks = 256;
+CutShape cut_shape(int k, int chunks = kCutShapeChunks);
 constexpr int kCutThreads = 1024;    // threads of a merging workgroup
 constexpr int kCutMaxFast = 8192 / kCutThreads;   // cut keys a merging thread holds (8192 in all)
 // the merge ranks more than kCountMax survivors with a wave per 64 of them
 static_assert(kCutThreads >= DH_MAX_K, "a merging workgroup has a wave per 64 of k survivors");
 // The cut's part of a workspace (launch_gemv's argument).
 GemvCut topk_cut(void *ws, int rows, int64_t vocab, int k);
-// The merge of the cuts a GEMV of `grid` workgroups left in ws (grid <= kCutMaxChunks,
-// grid * slots <= kCutThreads * kCutMaxFast); logits: that GEMV's output.  Outputs as
-// launch_topk's.
+// The merge of the cuts a GEMV of `grid` workgroups (chunk 0: chunk c is the tiles c + j *
+// grid) or the standalone top-k's cut pass (chunk c: the `chunk` entries from c * chunk on)
+// left in ws, `slots` keys a chunk (0: cut_shape(k)'s); grid <= kCutMaxChunks, grid * slots
+// <= kCutThreads * kCutMaxFast.  logits: the cut logits.  Outputs as launch_topk's.
 hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
                             const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                            void *ws, int grid, hipStream_t stream);
+                            void *ws, int grid, hipStream_t stream, int slots = 0,
+                            int64_t chunk = 0);
 
+// Without probs: the cut pass over the logits' chunks, then cut_merge (two launches, no
+// tickets).  With probs: topk_kernel (one launch, after a small kernel that zeroes the
+// tickets unless tickets_zeroed: the previous kernel on `stream` has zeroed them, as the
+// GEMV does, see launch_gemv).
 // idmap: NULL, or the vocabulary id of each logit column (ids and argmax are mapped).
 // probs, lse: NULL, or the softmax probability of each kept entry [rows][k] and each row's
-// log-sum-exp [rows] (both or neither).  tickets_zeroed: the previous kernel on `stream` has
-// zeroed the workspace's tickets (the GEMV does, see launch_gemv); otherwise a small kernel
-// zeroes them first.
+// log-sum-exp [rows] (both or neither).
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
                        void *ws, hipStream_t stream, float *probs = nullptr,

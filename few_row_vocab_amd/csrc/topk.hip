@@ -14,11 +14,13 @@
 // (image << 32) | (0xffffffff - id) is a 64-bit key that is distinct per entry and whose
 // numeric order is exactly the ordering above, so ties need no special case.  Ineligible
 // entries get the key 0.
-//  * One launch, a workgroup per (row, chunk of 2048 to 8192 logits).  Chunk pass: a select
-//    over the chunk's keys (value bins, with a radix select for a crowded bin; see
-//    select_bins) finds the chunk's best min(k, n); they go to the workspace in any order,
-//    the rest of the chunk's k slots as zeros.  Any entry of the row's top-k is in its
-//    chunk's top-k.
+//  * dh_topk and dh_topk_mapped: a cut pass over each row's chunks (cut_pass, as the
+//    draft's fused cut below), then cut_merge; two launches, exact for any input.
+//  * dh_topk_softmax (topk_kernel): one launch, a workgroup per (row, chunk of 2048 to 8192
+//    logits).  Chunk pass: a select over the chunk's keys (value bins, with a radix select
+//    for a crowded bin; see select_bins) finds the chunk's best min(k, n); they go to the
+//    workspace in any order, the rest of the chunk's k slots as zeros.  Any entry of the
+//    row's top-k is in its chunk's top-k.
 //  * Merge: each workgroup then takes a ticket on its row (an atomic count of the row's
 //    finished chunks, after a device-scope release of its list); the last one of the row
 //    (the "top-1 ... in parts and a join" of the pages, with the join done by whichever part
@@ -859,6 +861,7 @@ struct CutArgs {
     const float *logits;    // [rows][V], as the GEMV wrote them
     int64_t V, ntiles;      // ntiles: 16-row tiles of the head
     int k, grid, slots;     // grid: the GEMV's workgroups (the chunks)
+    int64_t chunk;          // 0: chunk c is tiles c + j * grid; else entries [c chunk, +chunk)
     const uint64_t *keys;   // [rows][grid][slots]
     const uint64_t *floors; // [rows][grid]
     const int32_t *idmap;
@@ -926,7 +929,7 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
         // the chunks that fell (chunk c did tiles c + j * grid, j < per); at most 8192 +
         // 1024 * 1024 items, so 32-bit indices
         const uint32_t per = (uint32_t)((a.ntiles + a.grid - 1) / a.grid);
-        const uint32_t C = per * 16u;
+        const uint32_t C = a.chunk ? (uint32_t)a.chunk : per * 16u;
         const uint32_t total = (uint32_t)nfast + nf * C;
         auto item = [&](uint32_t q) -> uint64_t {
             if (q < (uint32_t)nfast)
@@ -934,8 +937,8 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
             const uint32_t e2 = q - (uint32_t)nfast;
             const uint32_t f = e2 / C, e = e2 - f * C;
             const int64_t tile = (int64_t)cl.faillist[f] + (int64_t)(e >> 4) * a.grid;
-            const int64_t v = tile * 16 + (e & 15);
-            if (tile >= a.ntiles || v >= a.V)
+            const int64_t v = a.chunk ? (int64_t)cl.faillist[f] * a.chunk + e : tile * 16 + (e & 15);
+            if ((!a.chunk && tile >= a.ntiles) || v >= a.V)
                 return 0ull;
             const uint32_t im = order_key(lrow[v]);
             return im ? entry_key(im, (uint32_t)v) : 0ull;
@@ -965,11 +968,124 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
     emit_padding<false>(kk, a.k, rid, rval, nullptr, a.argmax, r);
 }
 
+// The standalone top-k's cut (dh_topk and dh_topk_mapped without softmax statistics): the
+// work of the GEMV's fused cut, on logits already in memory.  Workgroup (c, r) takes row r's
+// chunk c -- the `chunk` entries from c * chunk on -- and cuts it as the GEMV does (256 value
+// bins over the chunk's range of eligible images, d the bin of the m-th largest key; the keys
+// of bins >= d, or of bins > d when those would not fit the slots; the floor the smallest key
+// cut, 0 when none was left out).  cut_merge then merges the cuts and re-reads any chunk
+// whose floor beats the row's k-th key, so the result is exact for any input.  A thread
+// holds PER entries (thread t takes entries t + 256 u of the chunk), all loaded before any
+// is used.  (Chunks of the GEMV's layout -- every grid-th 16-entry tile -- read 64-byte
+// pieces and took 8.2 us at 16 rows against 3.3 us at one row.)
+struct CutPassArgs {
+    const float *logits;    // [rows][V]
+    int64_t V, chunk;       // chunk: entries a chunk
+    int m, slots;
+    uint64_t *keys;         // [rows][grid][slots]
+    uint64_t *floors;       // [rows][grid]
+};
+constexpr int kCutPassThreads = 256;
+constexpr int kCutPassMaxPer = 16;    // entries a thread holds, at most
+constexpr int kCutPassMaxGrid = 256;  // chunks a row, at most and at least (when the
+constexpr int kCutPassMinGrid = 64;   // row has that many tiles)
+
+template <int PER>
+__global__ __launch_bounds__(kCutPassThreads) void cut_pass(CutPassArgs a)
+{
+    constexpr int NW = kCutPassThreads / kWave;
+    __shared__ __align__(16) uint32_t hist[256];
+    __shared__ uint32_t wmn[NW], wmx[NW];
+    __shared__ uint32_t cnt;
+    __shared__ unsigned long long gfloor;
+    const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const int G = gridDim.x;
+    const float *lrow = a.logits + (int64_t)r * a.V;
+    const int64_t c0 = (int64_t)c * a.chunk;
+    const int64_t c1 = c0 + a.chunk < a.V ? c0 + a.chunk : a.V;   // the chunk's end
+    auto entry = [&](int u) -> int64_t { return c0 + u * kCutPassThreads + tid; };
+    float l[PER];
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        const int64_t v = entry(u);
+        l[u] = v < c1 ? lrow[v] : __builtin_nanf("");
+    }
+    hist[tid] = 0;   // 256 threads, 256 bins
+    if (tid == 0) {
+        cnt = 0;
+        gfloor = ~0ull;
+    }
+    // 1: the chunk's range of eligible images
+    uint32_t im[PER];
+    uint32_t mn = ~0u, mx = 0;
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        im[u] = order_key(l[u]);
+        mn = im[u] != 0 && im[u] < mn ? im[u] : mn;
+        mx = im[u] > mx ? im[u] : mx;
+    }
+    wave_min_max32(mn, mx);
+    if ((tid & 63) == 0) {
+        wmn[tid >> 6] = mn;
+        wmx[tid >> 6] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+        mn = wmn[w] < mn ? wmn[w] : mn;
+        mx = wmx[w] > mx ? wmx[w] : mx;
+    }
+    uint64_t *out = a.keys + ((int64_t)r * G + c) * a.slots;
+    uint64_t *floor = a.floors + (int64_t)r * G + c;
+    if (mx == 0) {   // no eligible entry (the same for the whole workgroup)
+        for (int q = tid; q < a.slots; q += kCutPassThreads)
+            out[q] = 0;
+        if (tid == 0)
+            *floor = 0;
+        return;
+    }
+    // 2: the histogram (the select's bin map; a NaN product, from a zero or infinite width,
+    // goes to 255)
+    const float lo = image_float(mn);
+    const float scale = 256.0f / (image_float(mx) - lo);
+    auto bin_of = [&](uint32_t x) -> uint32_t {
+        return (uint32_t)fminf((image_float(x) - lo) * scale, 255.0f);
+    };
+#pragma unroll
+    for (int u = 0; u < PER; u++)
+        if (im[u] != 0)
+            atomicAdd(&hist[bin_of(im[u])], 1u);
+    __syncthreads();
+    // 3: the cut (every key when at most m, bins >= d, or bins > d) to the slots
+    uint32_t d, above, count;
+    const uint32_t total = locate<256>(hist, (uint32_t)a.m, d, above, count);
+    bool all = total <= (uint32_t)a.m;
+    uint32_t dmin = 0;
+    if (!all) {
+        dmin = above + count <= (uint32_t)a.slots ? d : d + 1;
+        all = dmin == d && above + count == total;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+        if (im[u] != 0 && (all || bin_of(im[u]) >= dmin)) {
+            const uint64_t key = entry_key(im[u], (uint32_t)entry(u));
+            out[atomicAdd(&cnt, 1u)] = key;
+            atomicMin(&gfloor, (unsigned long long)key);
+        }
+    }
+    __syncthreads();
+    // 4: zeros after the cut; the floor
+    for (int q = (int)cnt + tid; q < a.slots; q += kCutPassThreads)
+        out[q] = 0;
+    if (tid == 0)
+        *floor = all ? 0ull : gfloor;
+}
+
 }  // namespace
 
-CutShape cut_shape(int k)
+CutShape cut_shape(int k, int chunks)
 {
-    const double L = k / 256.0;
+    const double L = (double)k / chunks;
     int m = (int)ceil(L + 4.0 * sqrt(L) + 3.0);
     m = m > k ? k : m < 1 ? 1 : m;
     return CutShape{m, m + (m / 2 > 4 ? m / 2 : 4)};
@@ -987,8 +1103,12 @@ TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
     const size_t gcap = (size_t)(ntiles < kCutMaxChunks ? ntiles : kCutMaxChunks);
     w.cut_keys_off =
         w.tickets_off + up((size_t)kSyncKinds * rows * kTicketStride * sizeof(uint32_t));
-    w.cut_floors_off =
-        w.cut_keys_off + up((size_t)rows * gcap * (size_t)cut_shape(k).slots * sizeof(uint64_t));
+    // a row's cuts: those of up to gcap GEMV workgroups, or of the standalone top-k's chunks
+    // (at most the merge's kCutThreads * kCutMaxFast keys)
+    size_t per_row = gcap * (size_t)cut_shape(k).slots;
+    per_row = per_row > (size_t)kCutThreads * kCutMaxFast ? per_row
+                                                          : (size_t)kCutThreads * kCutMaxFast;
+    w.cut_floors_off = w.cut_keys_off + up((size_t)rows * per_row * sizeof(uint64_t));
     w.bytes = w.cut_floors_off + up((size_t)rows * gcap * sizeof(uint64_t));
     return w;
 }
@@ -1005,9 +1125,11 @@ GemvCut topk_cut(void *ws, int rows, int64_t vocab, int k)
 
 hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
                             const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                            void *ws, int grid, hipStream_t stream)
+                            void *ws, int grid, hipStream_t stream, int slots, int64_t chunk)
 {
-    const GemvCut cut = topk_cut(ws, rows, vocab, k);
+    GemvCut cut = topk_cut(ws, rows, vocab, k);
+    if (slots > 0)
+        cut.slots = slots;
     const int nfast = grid * cut.slots;
     if (grid < 1 || grid > kCutMaxChunks || nfast > kCutThreads * kCutMaxFast)
         return hipErrorInvalidValue;
@@ -1018,6 +1140,7 @@ hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
     a.k = k;
     a.grid = grid;
     a.slots = cut.slots;
+    a.chunk = chunk;
     a.keys = cut.keys;
     a.floors = cut.floors;
     a.idmap = idmap;
@@ -1106,6 +1229,40 @@ hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
     a.argmax = argmax;
     a.probs = probs;
     a.lse = lse;
+    if (!probs) {
+        // the cut of every chunk, then their merge (two launches, no tickets).  Chunks a row:
+        // 256 for up to 4 rows, then fewer and larger ones, so that the call has about 1024
+        // workgroups (at 16 rows, 4096 workgroups of 512 entries took 8.6 us against 3.4 us
+        // for the 256 of one row); each chunk's cut is sized for its share of the k.
+        const int64_t ntiles = (vocab + 15) / 16;
+        int G = 1024 / rows;
+        G = G < kCutPassMinGrid ? kCutPassMinGrid : G > kCutPassMaxGrid ? kCutPassMaxGrid : G;
+        G = (int)(ntiles < G ? ntiles : G);
+        const CutShape cs = cut_shape(k, G);
+        const int64_t chunk = (ntiles + G - 1) / G * 16;   // whole tiles, so G chunks cover V
+        const int pt = (int)((chunk + kCutPassThreads - 1) / kCutPassThreads);
+        const GemvCut cut = topk_cut(ws, rows, vocab, k);
+        if (pt <= kCutPassMaxPer && (int64_t)G * cs.slots <= kCutThreads * kCutMaxFast) {
+            CutPassArgs c;
+            c.logits = logits;
+            c.V = vocab;
+            c.chunk = chunk;
+            c.m = cs.m;
+            c.slots = cs.slots;
+            c.keys = cut.keys;
+            c.floors = cut.floors;
+            const dim3 g((unsigned)G, (unsigned)rows), b(kCutPassThreads);
+            hipError_t e = pt <= 1   ? launch(cut_pass<1>, g, b, 0, stream, c)
+                           : pt <= 2 ? launch(cut_pass<2>, g, b, 0, stream, c)
+                           : pt <= 4 ? launch(cut_pass<4>, g, b, 0, stream, c)
+                           : pt <= 8 ? launch(cut_pass<8>, g, b, 0, stream, c)
+                                     : launch(cut_pass<16>, g, b, 0, stream, c);
+            if (e != hipSuccess)
+                return e;
+            return launch_cut_merge(logits, rows, vocab, k, idmap, ids, vals, argmax, ws, G,
+                                    stream, cs.slots, chunk);
+        }
+    }
     if (!tickets_zeroed) {
         const hipError_t e = launch(zero_tickets, dim3(1), dim3(64), 0, stream, a.tickets, rows);
         if (e != hipSuccess)

@@ -182,7 +182,8 @@ __device__ inline void write_out(const GemvArgs &a, int c, int64_t v, float s)
 // holding them in registers (unrolled into registers, the code grew several-fold and
 // measured several microseconds slower).
 // ws: 16 KiB + 256 B of free LDS (the reduction buffer), set up by cut_init.
-constexpr int kCutLgWavesPerRow = 2;   // log2 of the waves that cut one row, at most
+constexpr int kCutLgWavesPerRow = 2;
+constexpr int kRscPre = 1024;   // row scales a block prefetches, at most (one a thread)   // log2 of the waves that cut one row, at most
 // The smallest non-zero and the largest of (mn, mx) over each row of 16 lanes, in the row's
 // last lane (DPP row shifts; lanes with no source keep the identity).
 __device__ __forceinline__ void row_min_max32(uint32_t &mn, uint32_t &mx)
@@ -320,13 +321,14 @@ __device__ __forceinline__ void cut_rows(const GemvArgs &a, const uint32_t *stag
 
 // The writer and the draft's cut when every wave owns whole rows (R > nw / 2): wave w writes
 // the logits of rows w, w + nw, ... and cuts each (as cut_rows: the same bins, cut and floor),
-// with no workgroup barrier.  Lane l takes entries l + 64 j (tiles l / 16 + 4 j, head rows
+// with no workgroup barrier (rsc: the block's row scales in LDS, or NULL to load them).
+// Lane l takes entries l + 64 j (tiles l / 16 + 4 j, head rows
 // 16 (blockIdx.x + t gridDim.x) + l % 16); the range stays in registers, the wave's own 256
 // histogram words and cut counter sit in ws (the free reduction buffer), and the floor is a
 // wave reduction.  The wave's LDS operations complete in order between its passes.
 template <int SST>
 __device__ __forceinline__ void write_cut_own_rows(const GemvArgs &a, float *stage, int ntl,
-                                                   uint32_t *ws)
+                                                   uint32_t *ws, const float *rsc)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
@@ -352,7 +354,8 @@ __device__ __forceinline__ void write_cut_own_rows(const GemvArgs &a, float *sta
                     const int tu = t + 4 * u;
                     const uint32_t idu = id + (uint32_t)u * idstep;
                     sv[u] = tu < ntl ? srow[tu * SST] : 0.f;
-                    rs[u] = a.rscale && tu < ntl && (int64_t)idu < a.V ? a.rscale[idu] : 1.0f;
+                    rs[u] = rsc && tu < ntl ? rsc[tu * 16 + i]
+                            : a.rscale && tu < ntl && (int64_t)idu < a.V ? a.rscale[idu] : 1.0f;
                 }
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
@@ -466,6 +469,12 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
     extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
     __shared__ uint32_t cut_rng[2][16];          // the cut: each row's image range (min, max)
+    // FP8 row scale: the row scales of this block's tiles (entry 16 t + i: head row 16 (tile
+    // t) + i), loaded at the start -- one a thread, held in a register through the loop --
+    // and put in LDS for the writer, when the block's tiles have at most kRscPre rows; else
+    // the writer loads them itself (a dependent global load per tile, which cost about
+    // 1.5 us at the end of the kernel)
+    __shared__ float rsc[FMT == DH_FP8_ROW ? kRscPre : 1];
 
     static_assert(!CH || !FULL, "a chunked launch guards its loads");
     const int lane = threadIdx.x & 63;
@@ -482,6 +491,16 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int g = lane >> 4;
     const int H = a.H;
     const int64_t V = a.V;
+    const int ntl = (a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const bool rpre = FMT == DH_FP8_ROW && ntl * 16 <= (int)blockDim.x &&
+                      ntl * 16 <= kRscPre;
+    float rsv = 1.0f;
+    if constexpr (FMT == DH_FP8_ROW) {
+        const int64_t vr = (int64_t)(blockIdx.x + (threadIdx.x >> 4) * gridDim.x) * TILE +
+                           (threadIdx.x & 15);
+        if (rpre && (int)(threadIdx.x >> 4) < ntl && vr < V)
+            rsv = a.rscale[vr];
+    }
     constexpr int CB = kMaxWaves * KBW;          // CH: blocks a chunk
     const int nch = CH ? (a.nkb + CB - 1) / CB : 1;
     int it = 0, buf = 0;
@@ -687,6 +706,9 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             wcur[r] = wr[r];
     }
     }   // chunks
+    if constexpr (FMT == DH_FP8_ROW)
+        if (rpre && (int)threadIdx.x < ntl * 16)
+            rsc[threadIdx.x] = rsv;
     __syncthreads();
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave
     // w writes tiles w, w + nw, ...; a lane takes (activation row c, head row i) pairs.
@@ -696,7 +718,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // from nw / 2 rows up every wave owns whole rows: it writes and cuts them alone
     if (cut && (a.R << 1) > nw) {
         static_assert(sizeof(red) >= 16 * 256 * sizeof(uint32_t) + 256, "the cut's LDS fits");
-        write_cut_own_rows<SST>(a, stage, it + 1, reinterpret_cast<uint32_t *>(&red[0][0][0][0][0]));
+        write_cut_own_rows<SST>(a, stage, it + 1, reinterpret_cast<uint32_t *>(&red[0][0][0][0][0]),
+                                rpre ? rsc : nullptr);
         return;
     }
     const int per_tile = a.R * 16;
@@ -707,7 +730,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
         // a lane's head row is v0 + lane % 16 for every activation row it writes, so its row
         // scale is loaded once, before the stores (which the compiler may not move it past)
         const int64_t vl = v0 + (lane & 15);
-        const float rs = a.rscale && vl < V ? a.rscale[vl] : 1.0f;
+        const float rs = rpre ? rsc[t * 16 + (lane & 15)]
+                              : a.rscale && vl < V ? a.rscale[vl] : 1.0f;
 #pragma unroll
         for (int q = 0; q < 32 * 16 / kWave; q++) {
             const int o = lane + kWave * q;

@@ -923,6 +923,15 @@ hipError_t run(GemvArgs a, hipStream_t stream, int *grid_used)
         grid = min_grid;
     if (grid > a.ntiles)
         grid = a.ntiles;
+    // the draft's cut: at most as many workgroups as the merge takes cuts of (a small-H GEMV
+    // runs several workgroups a compute unit; rank 512, 16 rows: 1024 of them left the top-k
+    // to a launch of its own, and capping them at 512 took 58.7 us a draft against 62.5)
+    if (a.cut_m > 0 && NB == 1) {
+        int64_t cap = a.cut_max / a.cut_slots;
+        cap = cap < kCutMaxChunks ? cap : kCutMaxChunks;
+        if (grid > cap && cap >= min_grid)
+            grid = cap;
+    }
     const int64_t per = (a.ntiles + grid - 1) / grid;
     if (grid_used)
         *grid_used = (int)grid;

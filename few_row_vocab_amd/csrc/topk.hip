@@ -985,7 +985,8 @@ struct CutPassArgs {
     uint64_t *keys;         // [rows][grid][slots]
     uint64_t *floors;       // [rows][grid]
 };
-constexpr int kCutPassThreads = 256;
+constexpr int kCutPassThreads = 256;   // one histogram bin a thread (512 measured slower)
+static_assert(kCutPassThreads == 256, "a thread clears one of the 256 bins");
 constexpr int kCutPassMaxPer = 16;    // entries a thread holds, at most
 constexpr int kCutPassMaxGrid = 256;  // chunks a row, at most and at least (when the
 constexpr int kCutPassMinGrid = 64;   // row has that many tiles)

@@ -141,9 +141,10 @@ def main():
                          "workload, the others the row-sweep workload's first rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["subset", "lowrank", "twostage", "widelinear"],
+    ap.add_argument("--only", choices=["subset", "lowrank", "twostage", "widelinear", "topk"],
                     help="only the draft-vocabulary subset comparison, the low-rank "
-                         "two-stage head or the two-stage head (for profiling)")
+                         "two-stage head, the two-stage head, the wide linear or the "
+                         "standalone top-k (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the projection "
@@ -167,6 +168,9 @@ def main():
     if args.only == "lowrank":
         print(json.dumps({"lowrank_two_stage": lowrank_sweep(dh, torch, args.calls)}),
               flush=True)
+        return
+    if args.only == "topk":
+        print(json.dumps({"topk": topk_sweep(dh, torch, args.calls)}), flush=True)
         return
     if args.only == "widelinear":
         print(json.dumps({"wide_linear": wide_linear(dh, torch, args.calls)}), flush=True)
@@ -326,6 +330,7 @@ def main():
         out["subset_head"] = subset_sweep(dh, torch, args.calls)
         out["wide_linear"] = wide_linear(dh, torch, args.calls)
         out["lowrank_two_stage"] = lowrank_sweep(dh, torch, args.calls)
+        out["topk_standalone"] = topk_sweep(dh, torch, args.calls)
         out["device_ceiling"] = copy_ceiling(torch)
     print(json.dumps(out), flush=True)
 
@@ -565,6 +570,34 @@ def wide_linear(dh, torch, n):
     del ws
     torch.cuda.empty_cache()
     return res
+
+
+def topk_sweep(dh, torch, n):
+    """dh_topk alone (the cut pass over each row's chunks, then the merge) on the row-sweep
+    workload's own logits (FP8 E4M3 + E8M0 32x32 head, H=5120, V=129280): 1 and 16 rows,
+    k = 64 and 512; back to back, and inside a HIP graph (no host launch cost)."""
+    import synth
+    c = synth.CONFIGS["row_sweep"]
+    V, H = c["V"], c["H"]
+    dev = torch.device("cuda:0")
+    wd = torch.from_numpy(synth.head_bf16("row_sweep").view(np.int16)).to(dev)
+    head = dh.tile(dh.Head(dh.FP8_BLOCK32, *dh.quantize(wd, dh.FP8_BLOCK32)))
+    del wd
+    xd = torch.from_numpy(synth.activations("row_sweep", 16).view(np.int16)).to(dev)
+    lg16 = dh.gemv(head, xd)
+    res = {}
+    for R in (1, 16):
+        lg = lg16[:R].contiguous()
+        for k in (64, 512):
+            ws = dh.workspace(R, V, k)
+            o = [torch.empty((R, k), dtype=torch.int32, device=dev),
+                 torch.empty((R, k), dtype=torch.float32, device=dev),
+                 torch.empty((R,), dtype=torch.int32, device=dev)]
+            f = lambda i: dh.topk(lg, k, ws=ws, ids=o[0], vals=o[1], argmax=o[2])
+            res[f"rows{R}_k{k}"] = {"back_to_back_us": back_to_back_us(f, n),
+                                    "graph_us": graph_us(f, n)}
+    log("dh_topk: " + ", ".join(f"{key} {v['graph_us']:.1f} us (graph)" for key, v in res.items()))
+    return {"workload": f"logits of the FP8 block head H={H} V={V}", **res}
 
 
 def subset_sweep(dh, torch, n):

@@ -474,7 +474,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // and put in LDS for the writer, when the block's tiles have at most kRscPre rows; else
     // the writer loads them itself (a dependent global load per tile, which cost about
     // 1.5 us at the end of the kernel)
-    __shared__ float rsc[FMT == DH_FP8_ROW ? kRscPre : 1];
+    __shared__ float rsc[FMT == DH_FP8_ROW && (TL || VW * KBW < 8) ? kRscPre : 1];
 
     static_assert(!CH || !FULL, "a chunked launch guards its loads");
     const int lane = threadIdx.x & 63;
@@ -491,11 +491,14 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int g = lane >> 4;
     const int H = a.H;
     const int64_t V = a.V;
-    const int ntl = (a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const bool rpre = FMT == DH_FP8_ROW && ntl * 16 <= (int)blockDim.x &&
-                      ntl * 16 <= kRscPre;
+    // (not for the row-major 8-block instance, whose registers are full: it spilled)
+    constexpr bool RPRE = FMT == DH_FP8_ROW && (TL || KW < 8);
+    int ntl = 0;
+    bool rpre = false;
     float rsv = 1.0f;
-    if constexpr (FMT == DH_FP8_ROW) {
+    if constexpr (RPRE) {
+        ntl = (a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+        rpre = ntl * 16 <= (int)blockDim.x && ntl * 16 <= kRscPre;
         const int64_t vr = (int64_t)(blockIdx.x + (threadIdx.x >> 4) * gridDim.x) * TILE +
                            (threadIdx.x & 15);
         if (rpre && (int)(threadIdx.x >> 4) < ntl && vr < V)
@@ -706,7 +709,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             wcur[r] = wr[r];
     }
     }   // chunks
-    if constexpr (FMT == DH_FP8_ROW)
+    if constexpr (RPRE)
         if (rpre && (int)threadIdx.x < ntl * 16)
             rsc[threadIdx.x] = rsv;
     __syncthreads();

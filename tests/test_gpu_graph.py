@@ -126,3 +126,57 @@ def test_graph_subset_and_lowrank():
         got = {**{"s_" + a: b for a, b in _snap(os_).items()},
                **{"l_" + a: b for a, b in _snap(ol).items()}}
         _same(want, got)
+
+
+@pytest.mark.parametrize("R,k", [(1, 64), (16, 512)])
+def test_graph_topk_standalone(R, k):
+    """dh_topk (the cut pass, then the merge), dh_topk_softmax (its tickets zeroed by a small
+    kernel of the call) and dh_rescore_sync (its sync buffer left zero by every call) in one
+    graph: every replay equals the eager results."""
+    need_gpu()
+    V, H = 50000, 256
+    rng = np.random.default_rng(R + k)
+    lg = dev(rng.standard_normal((R, V)).astype(np.float32))
+    wd = synth.random_head(V, H, seed=21, std=0.02)
+    dense = dh.Head(dh.BF16, dev_u16(wd))
+    x = dev_u16(synth.random_acts(R, H, seed=22))
+    ws = dh.workspace(R, V, k)
+    ws2 = dh.workspace(R, V, k)
+    sync = dh.rescore_sync_buffer()
+    o = {"ids": torch.empty((R, k), dtype=torch.int32, device="cuda"),
+         "vals": torch.empty((R, k), dtype=torch.float32, device="cuda"),
+         "am": torch.empty((R,), dtype=torch.int32, device="cuda"),
+         "exact": torch.empty((R, k), dtype=torch.float32, device="cuda"),
+         "draft": torch.empty((R,), dtype=torch.int32, device="cuda")}
+    s = {}
+
+    def step():
+        dh.topk(lg, k, ws=ws, ids=o["ids"], vals=o["vals"], argmax=o["am"])
+        i2, v2, a2, p2, l2 = dh.topk_softmax(lg, k, ws=ws2)
+        s.update(i2=i2, v2=v2, p2=p2, l2=l2)
+        dh.rescore(dense, x, o["ids"], exact=o["exact"], draft=o["draft"], sync=sync)
+
+    step()
+    torch.cuda.synchronize()
+    want = _snap(o)
+    want_s = _snap(s)
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in list(o.values()) + list(s.values()):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(want, _snap(o))
+        _same(want_s, _snap(s))
+        assert not host(sync).any(), rep
+        dh.topk(lg, k, ws=ws)                # eager work between replays
+        torch.cuda.synchronize()

@@ -926,8 +926,8 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
     float *rval = a.vals + (int64_t)r * a.k;
     if (nf != 0) {
         // the stream of the passes: the cuts of the chunks that stand, then every entry of
-        // the chunks that fell (chunk c did tiles c + j * grid, j < per); at most 8192 +
-        // 1024 * 1024 items, so 32-bit indices
+        // the chunks that fell (chunk c: tiles c + j * grid, j < per, or the `chunk` entries
+        // from c * chunk); at most 8192 + 1024 * 1024 items, so 32-bit indices
         const uint32_t per = (uint32_t)((a.ntiles + a.grid - 1) / a.grid);
         const uint32_t C = a.chunk ? (uint32_t)a.chunk : per * 16u;
         const uint32_t total = (uint32_t)nfast + nf * C;
@@ -937,7 +937,8 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
             const uint32_t e2 = q - (uint32_t)nfast;
             const uint32_t f = e2 / C, e = e2 - f * C;
             const int64_t tile = (int64_t)cl.faillist[f] + (int64_t)(e >> 4) * a.grid;
-            const int64_t v = a.chunk ? (int64_t)cl.faillist[f] * a.chunk + e : tile * 16 + (e & 15);
+            const int64_t v =
+                a.chunk ? (int64_t)cl.faillist[f] * a.chunk + e : tile * 16 + (e & 15);
             if ((!a.chunk && tile >= a.ntiles) || v >= a.V)
                 return 0ull;
             const uint32_t im = order_key(lrow[v]);
@@ -977,7 +978,7 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
 // whose floor beats the row's k-th key, so the result is exact for any input.  A thread
 // holds PER entries (thread t takes entries t + 256 u of the chunk), all loaded before any
 // is used.  (Chunks of the GEMV's layout -- every grid-th 16-entry tile -- read 64-byte
-// pieces and took 8.2 us at 16 rows against 3.3 us at one row.)
+// pieces: 8.2 us for the pass at 16 rows, against 6.6 us with contiguous chunks.)
 struct CutPassArgs {
     const float *logits;    // [rows][V]
     int64_t V, chunk;       // chunk: entries a chunk
@@ -988,8 +989,8 @@ struct CutPassArgs {
 constexpr int kCutPassThreads = 256;   // one histogram bin a thread (512 measured slower)
 static_assert(kCutPassThreads == 256, "a thread clears one of the 256 bins");
 constexpr int kCutPassMaxPer = 16;    // entries a thread holds, at most
-constexpr int kCutPassMaxGrid = 256;  // chunks a row, at most and at least (when the
-constexpr int kCutPassMinGrid = 64;   // row has that many tiles)
+constexpr int kCutPassMaxGrid = 256;  // chunks a row: 1024 / rows within these bounds (fewer
+constexpr int kCutPassMinGrid = 64;   // when the row has fewer tiles)
 
 template <int PER>
 __global__ __launch_bounds__(kCutPassThreads) void cut_pass(CutPassArgs a)

@@ -84,3 +84,28 @@ def test_topk_cut_mapped_and_largest_vocab():
     x[3, -300:] = 7.0
     check(x, 512)
     check(x, 1)
+
+
+def _shapes():
+    """Seeded (rows, V, k) cases across the cut's chunk rule (1024 / rows chunks, between 64
+    and 256, fewer when the row has fewer 16-entry tiles): ragged V, tiny V, V just past a
+    chunk boundary, every row count from 1 to 32."""
+    rng = np.random.default_rng(2024)
+    out = [(1, 17, 17), (2, 1023, 64), (5, 4111, 512), (8, 16385, 100), (17, 9000, 33),
+           (32, 2049, 64), (3, 262144, 1), (12, 131071, 255)]
+    for _ in range(8):
+        R = int(rng.integers(1, 33))
+        V = int(rng.integers(20, 200000))
+        k = int(min(V, rng.choice([1, 7, 64, 65, 200, 512])))
+        out.append((R, V, k))
+    return out
+
+
+@pytest.mark.parametrize("R,V,k", _shapes())
+def test_topk_cut_random_shapes(R, V, k):
+    """Planted rows (NaN, -inf, ties, +-0, subnormals, ascending, descending, few eligible,
+    winners straddling chunks or in one chunk) at seeded shapes: bit-exact."""
+    need_gpu()
+    from test_gpu_core import _planted
+    say(f"topk cut: R={R} V={V} k={k}")
+    check(_planted(R, V, seed=R * 7919 + V + k), k)

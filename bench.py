@@ -545,7 +545,8 @@ def wide_linear(dh, torch, n):
     N=5120 outputs, K=18432 inputs, FP8 E4M3 with a row scale (tiled), fp32 and bf16-add
     outputs, 1 and 16 rows, back to back over three rotated weight copies (device-generated
     N(0, 0.02) weights; timing only, its parity is a test).  The GEMV streams the 18432 columns
-    in chunks of 8192."""
+    in chunks of 8192: dh_linear one chunk after another, dh_linear_ws (with a workspace) every
+    (tile, chunk) at once."""
     N, K = 5120, 18432
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(808)
@@ -559,14 +560,23 @@ def wide_linear(dh, torch, n):
         x = torch.randn((R, K), device=dev, generator=g).to(torch.bfloat16)
         out = torch.empty((R, N), dtype=torch.float32, device=dev)
         r16 = torch.zeros((R, N), dtype=torch.bfloat16, device=dev)
+        lws = dh.linear_workspace(R, N, K)
         tf = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_F32, out=out), n)
         ta = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_ADD_BF16,
                                                  residual=r16, out=r16), n)
+        wf = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_F32, out=out,
+                                                 ws=lws), n)
+        wa = back_to_back_us(lambda i: dh.linear(ws[i % NCOPY], x, dh.OUT_ADD_BF16,
+                                                 residual=r16, out=r16, ws=lws), n)
         b = N * K + N * 4 + R * K * 2 + R * N * 4
         res["rows"].append({"rows": R, "f32_us": tf, "f32_GBps": round(b / (tf * 1e-6) / 1e9, 1),
-                            "add_bf16_us": ta, "frac_of_8TBps": round(b / (tf * 1e-6) / 8e12, 4)})
+                            "add_bf16_us": ta, "frac_of_8TBps": round(b / (tf * 1e-6) / 8e12, 4),
+                            "ws_f32_us": wf, "ws_f32_GBps": round(b / (wf * 1e-6) / 1e9, 1),
+                            "ws_add_bf16_us": wa,
+                            "ws_frac_of_8TBps": round(b / (wf * 1e-6) / 8e12, 4)})
         log(f"wide linear R={R}: f32 {tf:.1f} us ({b / (tf * 1e-6) / 1e9:.0f} GB/s), "
-            f"bf16 add {ta:.1f} us")
+            f"bf16 add {ta:.1f} us; with a workspace {wf:.1f} us "
+            f"({b / (wf * 1e-6) / 1e9:.0f} GB/s), bf16 add {wa:.1f} us")
     del ws
     torch.cuda.empty_cache()
     return res

@@ -192,8 +192,8 @@ dh_status dh_gemv(const dh_head *head, const uint16_t *x, int32_t rows, float *l
     return device_status(dh::launch_gemv(*head, x, rows, logits, (hipStream_t)stream));
 }
 
-dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
-                    const uint16_t *residual, void *out, void *stream)
+static dh_status check_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                              const uint16_t *residual, void *out)
 {
     DH_TRY(check_head(w));
     DH_TRY(check_gemv_rows(rows, w->hidden));
@@ -210,8 +210,44 @@ dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t m
         return DH_ERR_INVALID;
     if (residual && (const void *)residual != out && overlap(so, span(residual, so.hi - so.lo)))
         return DH_ERR_INVALID;
+    return DH_OK;
+}
+
+dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                    const uint16_t *residual, void *out, void *stream)
+{
+    DH_TRY(check_linear(w, x, rows, mode, residual, out));
     return device_status(
         dh::launch_linear(*w, x, rows, mode, residual, out, (hipStream_t)stream));
+}
+
+size_t dh_linear_workspace_bytes(int32_t rows, int64_t n, int64_t k)
+{
+    if (check_rows(rows) != DH_OK || n < 1 || n > DH_MAX_GEMV_VOCAB || k < 32 || k % 32 != 0 ||
+        k > DH_MAX_HIDDEN)
+        return 0;
+    const size_t b = dh::linear_ws_bytes(n, k, rows);
+    return (b + 255) & ~(size_t)255;
+}
+
+dh_status dh_linear_ws(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                       const uint16_t *residual, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    DH_TRY(check_linear(w, x, rows, mode, residual, out));
+    const size_t need = dh_linear_workspace_bytes(rows, w->vocab, w->hidden);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+        return DH_ERR_WORKSPACE;
+    const size_t ob = mode == DH_OUT_F32 ? 4 : 2;
+    const Span sw = span(workspace, need);
+    const Span others[] = {span(out, (size_t)rows * (size_t)w->vocab * ob), head_weight(*w),
+                           head_scale(*w), span(x, (size_t)rows * (size_t)w->hidden * 2),
+                           span(residual, residual ? (size_t)rows * (size_t)w->vocab * 2 : 0)};
+    for (const Span &o : others)
+        if (overlap(sw, o))
+            return DH_ERR_INVALID;
+    return device_status(dh::launch_linear(*w, x, rows, mode, residual, out, (hipStream_t)stream,
+                                           workspace, workspace_bytes));
 }
 
 size_t dh_workspace_bytes(int32_t rows, int64_t vocab, int32_t k)

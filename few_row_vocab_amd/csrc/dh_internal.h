@@ -43,6 +43,8 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
                          uint32_t *zero = nullptr, int nzero = 0, int zstride = 1,
                          const GemvCut *cut = nullptr, int *grid_used = nullptr);
 size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows);
+// The scratch dh_linear_ws takes: the few-tile split's partials, or the wide split's.
+size_t linear_ws_bytes(int64_t vocab, int64_t hidden, int rows);
 
 // sync: NULL (a second kernel picks the drafts), or zeroed sync lines (ticket lines, then
 // best-key lines, `rows` of each, kTicketStride words apart: a top-k workspace's, or

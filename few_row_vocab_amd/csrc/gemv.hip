@@ -95,6 +95,7 @@ struct GemvArgs {
     // the draft's fused top-k cut (GemvCut; cut_m == 0: none)
     uint64_t *cut_keys, *cut_floors;
     int cut_m, cut_slots, cut_max;
+    float *part;            // SPL: the chunks' partial sums, fp32 [chunks][R][V]
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -449,11 +450,17 @@ __device__ __forceinline__ void write_cut_own_rows(const GemvArgs &a, float *sta
 // chunk's activations, every tile of the block streams that chunk of its rows, and the
 // tile's reduced sums are added to its running sums in LDS, chunk after chunk (so a row's
 // sums still do not depend on how many rows share the call).
+// SPL (with CH): one launch over (tile, chunk) pairs instead -- workgroup (x, y) streams
+// chunk y of its tiles and stores that chunk's sums to part[y]; gemv_chunk_reduce then adds
+// the chunks in order, as the stage does, so the bits are those of the one-chunk-at-a-time
+// launch.  For heads with few tiles (a linear's N), where chunks in turn leave most compute
+// units idle.
 // TL: the head is tiled (DH_TILED): a tile's 64-column block is RQ KiB in which lane l's
 // 16 bytes sit at 16 l, so a wave's load reads 1 KiB of whole lines, with the non-temporal
 // hint; rows past V and columns past H are zeros in the tiled copy.  The lanes receive the
 // same bytes as from the row-major head, so the sums and their bits are the same.
-template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false>
+template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false,
+          bool SPL = false>
 __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(GemvArgs a)
 {
     constexpr int RQ = FMT == DH_BF16 ? 2 : 1;   // 16-byte loads per lane per 64 columns
@@ -474,9 +481,10 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // and put in LDS for the writer, when the block's tiles have at most kRscPre rows; else
     // the writer loads them itself (a dependent global load per tile, which cost about
     // 1.5 us at the end of the kernel)
-    __shared__ float rsc[FMT == DH_FP8_ROW && (TL || VW * KBW < 8) ? kRscPre : 1];
+    __shared__ float rsc[FMT == DH_FP8_ROW && (TL || VW * KBW < 8) && !SPL ? kRscPre : 1];
 
     static_assert(!CH || !FULL, "a chunked launch guards its loads");
+    static_assert(!SPL || (CH && NB == 1), "a split launch is a chunked one, up to 16 rows");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     const int H = a.H;
     const int64_t V = a.V;
     // (not for the row-major 8-block instance, whose registers are full: it spilled)
-    constexpr bool RPRE = FMT == DH_FP8_ROW && (TL || KW < 8);
+    constexpr bool RPRE = FMT == DH_FP8_ROW && (TL || KW < 8) && !SPL;
     int ntl = 0;
     bool rpre = false;
     float rsv = 1.0f;
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     constexpr int CB = kMaxWaves * KBW;          // CH: blocks a chunk
     const int nch = CH ? (a.nkb + CB - 1) / CB : 1;
     int it = 0, buf = 0;
-    for (int ch = 0; ch < nch; ch++) {
+    for (int ch = SPL ? (int)blockIdx.y : 0; ch < (SPL ? (int)blockIdx.y + 1 : nch); ch++) {
     const int cb = CH ? ch * CB : 0;            // the chunk's first 64-column block
     const int nkbc = CH ? (a.nkb - cb < CB ? a.nkb - cb : CB) : a.nkb;
     const int nvw = (nkbc + KBW - 1) / KBW;   // virtual waves: the waves of a 16-row launch
@@ -695,7 +703,7 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
             float s = 0.f;
             for (int w = 0; w < nvw; w++)
                 s += red[buf][w][c >> 4][j][src];
-            if (CH && ch > 0)
+            if (CH && !SPL && ch > 0)
                 s = stage[it * SST + o] + s;      // the earlier chunks' sums, then this one's
             stage[it * SST + o] = s;
         }
@@ -713,6 +721,19 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
         if (rpre && (int)threadIdx.x < ntl * 16)
             rsc[threadIdx.x] = rsv;
     __syncthreads();
+    if constexpr (SPL) {
+        // this chunk's sums of every tile of the block, unscaled, to part[chunk][c][v]
+        float *pc = a.part + (int64_t)blockIdx.y * a.R * V;
+        for (int t = wave; t <= it; t += nw) {
+            const int64_t v0 = (int64_t)(blockIdx.x + t * gridDim.x) * TILE;
+            for (int o = lane; o < a.R * 16; o += kWave) {
+                const int c = o >> 4, i = o & 15;
+                if (v0 + i < V)
+                    pc[(int64_t)c * V + v0 + i] = stage[t * SST + c * 16 + i];
+            }
+        }
+        return;
+    }
     // it + 1 tiles were done by this block: tile blockIdx.x + t * gridDim.x for t <= it.  Wave
     // w writes tiles w, w + nw, ...; a lane takes (activation row c, head row i) pairs.
     static_assert(TR == 1, "the writer below assumes one 16-row group per tile");
@@ -894,6 +915,23 @@ __global__ __launch_bounds__(256) void gemv_reduce(GemvArgs a, int nvw, const fl
     write_out(a, c, v, s);
 }
 
+// The split chunked launch's sums: for each (row c, head row v), part[0] + part[1] + ... in
+// chunk order (the stage's order in the one-launch form), then the row scale and the output
+// mode, as the writer applies them.
+__global__ __launch_bounds__(256) void gemv_chunk_reduce(GemvArgs a, int nch, const float *part)
+{
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t rv = (int64_t)a.R * a.V;
+    if (n >= rv)
+        return;
+    const int c = (int)(n / a.V);
+    const int64_t v = n - (int64_t)c * a.V;
+    float s = part[n];
+    for (int ch = 1; ch < nch; ch++)
+        s = s + part[(int64_t)ch * rv + n];
+    write_out(a, c, v, s);
+}
+
 template <int FMT, int KBW, bool FULL, int TR, int NB, int VW, bool TL, bool CH = false>
 hipError_t run(GemvArgs a, hipStream_t stream, int *grid_used)
 {
@@ -1025,6 +1063,21 @@ size_t linear_split_bytes(int64_t vocab, int64_t hidden, int rows)
     return (size_t)nvw * (size_t)rows * (size_t)vocab * sizeof(float);
 }
 
+// The split chunked launch's partials: one fp32 [R][V] a column chunk.
+static size_t chunk_split_bytes(int64_t vocab, int64_t hidden, int rows)
+{
+    constexpr int CB = kMaxWaves * kChunkKbw;
+    const int64_t nch = ((hidden + 63) / 64 + CB - 1) / CB;
+    return (size_t)nch * (size_t)rows * (size_t)vocab * sizeof(float);
+}
+
+size_t linear_ws_bytes(int64_t vocab, int64_t hidden, int rows)
+{
+    const size_t a = linear_split_bytes(vocab, hidden, rows);
+    const size_t b = chunk_split_bytes(vocab, hidden, rows);
+    return a > b ? a : b;
+}
+
 template <int FMT, bool TL>
 hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
 {
@@ -1040,6 +1093,30 @@ hipError_t run_split(const GemvArgs &a, float *part, hipStream_t stream)
     const int64_t n = (int64_t)a.R * a.V;
     return launch(gemv_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a, nvw,
                   (const float *)part);
+}
+
+template <int FMT, bool TL>
+hipError_t run_chunk_split(GemvArgs a, float *part, hipStream_t stream)
+{
+    constexpr int VW = TL ? 1 : 2;                 // as the one-chunk-at-a-time launch
+    constexpr int CB = kMaxWaves * kChunkKbw;
+    a.ntiles = (int)((a.V + 15) / 16);
+    a.part = part;
+    const int nch = (a.nkb + CB - 1) / CB;
+    // about one workgroup per compute unit in all: each keeps its chunk's activations and
+    // streams several tiles, one ahead of the other (a workgroup per (tile, chunk) pays the
+    // start of a stream for each 128 KiB tile)
+    int gx = device_cus() / nch;
+    gx = gx < 1 ? 1 : gx > a.ntiles ? a.ntiles : gx;
+    const int per = (a.ntiles + gx - 1) / gx;
+    hipError_t e = launch(gemv_kernel<FMT, kChunkKbw, false, 1, 1, VW, TL, true, true>,
+                          dim3((unsigned)gx, (unsigned)nch), dim3(kMaxWaves / VW * kWave),
+                          (size_t)per * stage_stride(256) * sizeof(float), stream, a);
+    if (e != hipSuccess)
+        return e;
+    const int64_t n = (int64_t)a.R * a.V;
+    return launch(gemv_chunk_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a,
+                  nch, (const float *)part);
 }
 
 hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int mode,
@@ -1072,6 +1149,7 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
     a.cut_m = with_cut ? cut->m : 0;
     a.cut_slots = with_cut ? cut->slots : 0;
     a.cut_max = with_cut ? cut->max_keys : 0;
+    a.part = nullptr;
     if (grid_used)
         *grid_used = 0;
     // few tiles and room for the partials: split by virtual wave (the same bits)
@@ -1086,6 +1164,24 @@ hipError_t launch_linear(const dh_head &head, const uint16_t *x, int rows, int m
         case DH_BF16 | DH_TILED: return run_split<DH_BF16, true>(a, part, stream);
         case DH_FP8_BLOCK32 | DH_TILED: return run_split<DH_FP8_BLOCK32, true>(a, part, stream);
         case DH_FP8_ROW | DH_TILED: return run_split<DH_FP8_ROW, true>(a, part, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    // wider than a chunk, few tiles and room for the chunks' partials: every (tile, chunk)
+    // at once, then their sum in chunk order (the same bits); N = 5120, K = 18,432: 320 tiles
+    // of 3 chunks in turn left most compute units idle
+    constexpr int kCB = kMaxWaves * kChunkKbw;
+    const int64_t nch = (a.nkb + kCB - 1) / kCB;
+    if (scratch && !with_cut && rows <= 16 && nch > 1 && ntiles * nch <= 4 * device_cus() &&
+        scratch_bytes >= chunk_split_bytes(a.V, head.hidden, rows)) {
+        float *part = static_cast<float *>(scratch);
+        switch (head.format) {
+        case DH_BF16: return run_chunk_split<DH_BF16, false>(a, part, stream);
+        case DH_FP8_BLOCK32: return run_chunk_split<DH_FP8_BLOCK32, false>(a, part, stream);
+        case DH_FP8_ROW: return run_chunk_split<DH_FP8_ROW, false>(a, part, stream);
+        case DH_BF16 | DH_TILED: return run_chunk_split<DH_BF16, true>(a, part, stream);
+        case DH_FP8_BLOCK32 | DH_TILED: return run_chunk_split<DH_FP8_BLOCK32, true>(a, part, stream);
+        case DH_FP8_ROW | DH_TILED: return run_chunk_split<DH_FP8_ROW, true>(a, part, stream);
         default: return hipErrorInvalidValue;
         }
     }

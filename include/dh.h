@@ -132,6 +132,23 @@ typedef enum { DH_OUT_F32 = 0, DH_OUT_BF16 = 1, DH_OUT_ADD_BF16 = 2 } dh_out_mod
 dh_status dh_linear(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
                     const uint16_t *residual, void *out, void *stream);
 
+/* dh_linear_ws -- dh_linear with a workspace, for linears with few output rows: with up to
+ * 16 rows and K above 8192 columns the column chunks of every output tile run at once (a
+ * partial sum per chunk in the workspace, then their sum in chunk order); with K up to 8192
+ * and few tiles, each tile's sum is split by its 64-column parts the same way.  The results
+ * are bitwise dh_linear's.  Same passages as dh_linear.
+ * workspace: device, 256-byte aligned, at least dh_linear_workspace_bytes(rows, N, K) bytes,
+ * scratch (no state between calls); it must not overlap any other argument's buffer.
+ * Other arguments and errors as dh_linear; a missing or short workspace is
+ * DH_ERR_WORKSPACE. */
+dh_status dh_linear_ws(const dh_head *w, const uint16_t *x, int32_t rows, int32_t mode,
+                       const uint16_t *residual, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* The workspace dh_linear_ws needs for `rows` rows, N = n outputs and K = k inputs (0 for
+ * sizes outside the limits). */
+size_t dh_linear_workspace_bytes(int32_t rows, int64_t n, int64_t k);
+
 /* dh_topk -- per row, the k best logits in order: entry u beats entry v iff u is eligible
  * and (v is not, or l_u > l_v, or l_u == l_v and u < v); NaN and -inf are not eligible, so
  * they are never returned; -0 == +0.  Slot j holds the entry that exactly j others beat.

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     L = dh.lib()
     names = declared_functions()
     assert set(names) >= {"dh_gemv", "dh_topk", "dh_rescore", "dh_rescore_sync", "dh_draft",
-                          "dh_quantize",
+                          "dh_quantize", "dh_linear_ws", "dh_linear_workspace_bytes",
                           "dh_workspace_bytes", "dh_status_string", "dh_gather_rows",
                           "dh_topk_mapped", "dh_draft_mapped", "dh_linear",
                           "dh_draft_lowrank", "dh_topk_softmax", "dh_sample"}
@@ -434,4 +434,33 @@ def test_draft_noalloc_refusals(no_device):
     assert call(h=big, rows=32) == 5
     assert dh.workspace_bytes(32, 200000, k) > dh.NOALLOC_SCRATCH_BYTES
     for b in (ids, vals, dr):
+        assert b.untouched()
+
+
+def test_linear_ws_refusals(no_device):
+    """dh_linear_ws refuses what dh_linear refuses, and a missing, short, misaligned or
+    overlapping workspace, on the host."""
+    N, K, R = 300, 16384, 2
+    L = dh.lib()
+    nb = L.dh_linear_workspace_bytes(R, N, K)
+    assert nb >= 2 * R * N * 4 and nb % 256 == 0
+    assert L.dh_linear_workspace_bytes(0, N, K) == 0 and L.dh_linear_workspace_bytes(33, N, K) == 0
+    assert L.dh_linear_workspace_bytes(R, N, 48) == 0 and L.dh_linear_workspace_bytes(R, 0, K) == 0
+    assert L.dh_linear_workspace_bytes(R, N, 32768 + 32) == 0
+    w, s, x, out = HostBuf(N * K), HostBuf(N * 4), HostBuf(R * K * 2), HostBuf(R * N * 4)
+    ws = HostBuf(nb + 512)
+    h = head(dh.FP8_ROW, N, K, w, s)
+
+    def call(mode=dh.OUT_F32, wsp=None, wsb=None, o=out):
+        return L.dh_linear_ws(ctypes.byref(h), x.p, R, mode, None, o.p,
+                              ws.p if wsp is None else wsp, nb if wsb is None else wsb, None)
+
+    assert call(mode=3) == 1                                            # unknown mode
+    assert L.dh_linear_ws(ctypes.byref(h), x.p, R, dh.OUT_F32, None, out.p, None, nb,
+                          None) == 3                                    # no workspace
+    assert call(wsb=nb - 256) == 3                                      # short
+    assert call(wsp=ctypes.c_void_p(ws.a.ctypes.data + 64)) == 3        # misaligned
+    assert call(o=ws) == 1                                              # output in the workspace
+    assert call(wsp=w.p, wsb=N * K) == 1                                # over the weight
+    for b in (w, s, x, out, ws):
         assert b.untouched()

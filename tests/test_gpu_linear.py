@@ -133,3 +133,55 @@ def test_linear_refusals_on_device():
         dh.linear(gh, xd, dh.OUT_ADD_BF16, residual=big[8:].view(R, N), out=big[:R * N].view(R, N))
     torch.cuda.synchronize()
     assert not host(out).any() and not host(big).any()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
+@pytest.mark.parametrize("N,K,R", [(2051, 16384, 3), (5120, 18432, 16), (300, 32768, 16),
+                                   (77, 8256, 1), (320, 5120, 5), (40000, 9024, 2),
+                                   (300, 32768, 20)])
+def test_linear_ws_equals_linear(fmt, N, K, R):
+    """dh_linear_ws gives dh_linear's bits in every mode, on both layouts: with K above 8192
+    and few output tiles the column chunks of every tile run at once (partials in the
+    workspace, summed in chunk order); with K up to 8192 and few tiles, the split by 64-column
+    parts; otherwise (many tiles, or more than 16 rows) the workspace goes unused."""
+    need_gpu()
+    say(f"linear_ws {fmt} N={N} K={K} R={R}")
+    w = synth.random_head(N, K, seed=N + 3 * K, std=0.02)
+    x = dev_u16(synth.random_acts(R, K, seed=R + 5 * K))
+    res = dev_u16(synth.random_acts(R, N, seed=N + R + 1, std=0.5))
+    gh, _ = make_heads(fmt, w)
+    ws = dh.linear_workspace(R, N, K)
+    ws.fill_(0xFF)                                   # stale contents must not matter
+    for head in (gh, dh.tile(gh)):
+        for mode in (dh.OUT_F32, dh.OUT_BF16, dh.OUT_ADD_BF16):
+            r = res if mode == dh.OUT_ADD_BF16 else None
+            a = dh.linear(head, x, mode, residual=r)
+            b = dh.linear(head, x, mode, residual=r, ws=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(a).view(np.uint8), host(b).view(np.uint8)), mode
+    # in place: out == residual
+    acc = res.clone()
+    dh.linear(gh, x, dh.OUT_ADD_BF16, residual=acc, out=acc, ws=ws)
+    want = dh.linear(gh, x, dh.OUT_ADD_BF16, residual=res)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc).view(np.uint16), host(want).view(np.uint16))
+
+
+def test_linear_ws_refusals_on_device():
+    need_gpu()
+    N, K, R = 300, 16384, 2
+    w = synth.random_head(N, K, seed=15, std=0.02)
+    gh, _ = make_heads("row", w)
+    xd = dev_u16(synth.random_acts(R, K, seed=16))
+    out = torch.zeros((R, N), dtype=torch.float32, device="cuda")
+    nb = dh.linear_workspace_bytes(R, N, K)
+    assert nb >= 2 * R * N * 4                       # two column chunks of partials
+    with pytest.raises(dh.DHError):                  # short
+        dh.linear(gh, xd, dh.OUT_F32, out=out, ws=torch.empty(nb - 256, dtype=torch.uint8,
+                                                               device="cuda"))
+    big = torch.zeros(nb + R * N * 4 + 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(dh.DHError):                  # the output inside the workspace
+        dh.linear(gh, xd, dh.OUT_F32, out=big[:R * N * 4].view(torch.float32).view(R, N),
+                  ws=big[:nb])
+    torch.cuda.synchronize()
+    assert not host(out).any()

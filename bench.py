@@ -82,14 +82,14 @@ def measured_traffic(rows):
 
 def gemv_kernel_name(fmt_code, H, tiled=True):
     """The template instance the library launches for this head width (up to 8192) and up to
-    16 rows (its rule for the per-wave K blocks and the unguarded tile loop; one K chunk), as
-    rocprofv3 names it."""
+    16 rows (its rule for the per-wave K blocks and the unguarded tile loop; one K chunk, not
+    split), as rocprofv3 names it."""
     nkb = (H + 63) // 64
     kbw = -(-nkb // 16)
     vw = 2 if fmt_code == 0 and kbw == 5 else 1        # bf16 tiles of 5 blocks: 8 waves
     full = H % 64 == 0 and nkb % (vw * kbw) == 0
     tf = lambda b: "true" if b else "false"
-    return f"gemv_kernel<{fmt_code}, {kbw}, {tf(full)}, 1, 1, {vw}, {tf(tiled)}, false>"
+    return f"gemv_kernel<{fmt_code}, {kbw}, {tf(full)}, 1, 1, {vw}, {tf(tiled)}, false, false>"
 
 
 def copy_calibration():

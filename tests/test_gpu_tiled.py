@@ -3,7 +3,8 @@
  * dh_tile_head writes exactly the layout include/dh.h states (checked against a numpy
    re-arrangement of the row-major bytes, zero padding included);
  * every GEMV form gives bitwise the same results from the tiled head as from the row-major
-   one (dh_gemv at 1..32 rows, ragged V and H, all three formats; dh_linear's modes; the
+   one (dh_gemv at 1..32 rows, ragged V and H, all three formats; narrow heads of up to 512
+   columns with the draft's cut after them; dh_linear's modes; the
    dh_draft family including the few-tile split of the low-rank down linear), and the tiled
    logits meet the oracle's tolerance;
  * heads that must stay row-major (a rescore's dense head, a gather's source) are refused.
@@ -78,6 +79,36 @@ def test_tiled_gemv_bit_equal(fmt, V, H, R):
     torch.cuda.synchronize()
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     check_logits(b, oracle.gemv(FMTS[fmt][1], ow, osc, x), what="tiled gemv")
+
+
+# narrow heads (H <= 512: a tile is at most 16 KiB, several workgroups a compute unit): a
+# head of one tile (V = 5), H short of a whole 64-column block, tile counts that are not a
+# multiple of the grid, heads whose tiles outnumber the row-scale prefetch; the draft's cut
+# after them against the row-major head's draft
+@pytest.mark.parametrize("fmt", ["bf16", "block", "row"])
+@pytest.mark.parametrize("V,H,R", [(5, 512, 16), (100, 32, 3), (4133, 480, 16),
+                                   (40000, 512, 1), (40000, 160, 7), (262144, 448, 16)])
+def test_tiled_narrow_heads_bit_equal(fmt, V, H, R):
+    need_gpu()
+    say(f"narrow tiled gemv {fmt} V={V} H={H} R={R}")
+    w = synth.random_head(V, H, seed=V + 3 * H, std=0.05)
+    x = synth.random_acts(R, H, seed=R + 5 * H)
+    gh, (ow, osc) = make_heads(fmt, w)
+    th = dh.tile(gh)
+    xd = dev_u16(x)
+    a = host(dh.gemv(gh, xd))
+    b = host(dh.gemv(th, xd))
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    if V * H <= 25_000_000:
+        check_logits(b, oracle.gemv(FMTS[fmt][1], ow, osc, x), what="narrow tiled gemv")
+    for k in (1, 64, 512):
+        if k <= V:
+            c = dh.draft(gh, xd, k, keep_logits=True)
+            d = dh.draft(th, xd, k, keep_logits=True)
+            torch.cuda.synchronize()
+            for n in ("logits", "ids", "vals", "draft"):
+                assert host(c[n]).tobytes() == host(d[n]).tobytes(), (k, n)
 
 
 @pytest.mark.parametrize("R", [16, 32])

@@ -531,12 +531,10 @@ static dh_status run_draft(const dh_head *head, const dh_head *down, uint16_t *t
         e = cut_made ? dh::launch_cut_merge(L, rows, head->vocab, k, idmap, ids, vals,
                                             dense ? nullptr : draft, workspace, grid, st)
                      : dh::launch_topk(L, rows, head->vocab, k, idmap, ids, vals,
-                                       dense ? nullptr : draft, workspace, st, nullptr, nullptr,
-                                       true);
-    if (e == hipSuccess && dense)   // its sync lines were zeroed by the GEMV as well
+                                       dense ? nullptr : draft, workspace, st);
+    if (e == hipSuccess && dense)   // its sync lines were zeroed by the GEMV
         e = dh::launch_rescore(*dense, x, rows, ids, vals, k, exact, draft, st,
-                               dh::topk_tickets(workspace, rows, head->vocab, k) +
-                                   (size_t)rows * dh::kTicketStride);
+                               dh::topk_tickets(workspace, rows, head->vocab, k));
     return device_status(e);
 }
 

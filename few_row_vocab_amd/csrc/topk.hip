@@ -14,31 +14,22 @@
 // (image << 32) | (0xffffffff - id) is a 64-bit key that is distinct per entry and whose
 // numeric order is exactly the ordering above, so ties need no special case.  Ineligible
 // entries get the key 0.
-//  * dh_topk and dh_topk_mapped: a cut pass over each row's chunks (cut_pass, as the
-//    draft's fused cut below), then cut_merge; two launches, exact for any input.
-//  * dh_topk_softmax (topk_kernel): one launch, a workgroup per (row, chunk of 2048 to 8192
-//    logits).  Chunk pass: a select over the chunk's keys (value bins, with a radix select
-//    for a crowded bin; see select_bins) finds the chunk's best min(k, n); they go to the
-//    workspace in any order, the rest of the chunk's k slots as zeros.  Any entry of the
-//    row's top-k is in its chunk's top-k.
-//  * Merge: each workgroup then takes a ticket on its row (an atomic count of the row's
-//    finished chunks, after a device-scope release of its list); the last one of the row
-//    (the "top-1 ... in parts and a join" of the pages, with the join done by whichever part
-//    ends last instead of a second launch) acquires the other lists and runs the same select
-//    over the row's chunk lists to keep k; each survivor's slot is the number of survivors
-//    that beat it (the pages' rank-by-count order).  Values come back from the images
-//    (zeros, whose sign the image drops, are read from the logits, so -0 stays -0).  The
-//    tickets start at zero: the GEMV before the top-k zeroes them (dh_draft), else a small
-//    kernel does (the call stays free of memset, so it can be captured in a graph).
-//  * dh_draft up to 16 rows fuses the chunk pass into the GEMV (topk.h): each GEMV
-//    workgroup leaves a short cut of its tiles' logits, and cut_merge, one workgroup per row,
-//    runs the same select over the cuts, then reads back the logits of any chunk whose cut
-//    may have left out keys of the row's top k (exact for any input; rare for spread ones).
-// Softmax statistics (STATS, for dh_topk_softmax): pass 1 also writes each chunk's largest
-// eligible logit m_c and s_c = sum over its eligible logits of exp(l - m_c) (1 for l == m_c,
-// so +inf entries count 1 each); the merge combines them in chunk order into the row's m and
-// z = sum_c s_c exp(m_c - m), and gives each kept entry exp(l - m) / z and the row
-// log(z) + m.  Sums are in fp32 in a fixed order (deterministic).
+//  * dh_topk, dh_topk_mapped and dh_topk_softmax: the pages' top-1 "in parts and a join",
+//    for k keys.  The parts: a cut pass over each row's chunks (cut_pass, a workgroup per
+//    chunk of a row; the same cut as the draft's below) keeps each chunk's keys of the value
+//    bins at and above the bin of its m-th largest, with a floor above every key it left out.
+//    The join: cut_merge, a workgroup per row, selects the k best of the cuts, and re-reads
+//    the logits of any chunk whose floor beats the k-th of them, so the result is exact for
+//    any input.  Each kept key's slot is the number of kept keys that beat it (the pages'
+//    rank-by-count order).  Values come back from the images (zeros, whose sign the image
+//    drops, are read from the logits, so -0 stays -0).
+//  * dh_draft up to 16 rows fuses the cut pass into the GEMV (topk.h): each GEMV workgroup
+//    leaves the cut of its tiles' logits, and cut_merge joins them the same way.
+// Softmax statistics (STATS, for dh_topk_softmax): the cut pass also writes each chunk's
+// largest eligible logit m_c and s_c = sum over its eligible logits of exp(l - m_c) (1 for
+// l == m_c, so +inf entries count 1 each); the merge combines them in chunk order into the
+// row's m and z = sum_c s_c exp(m_c - m), and gives each kept entry exp(l - m) / z and the
+// row log(z) + m.  Sums are in fp32 in a fixed order (deterministic).
 // These kernels are short chains of dependent steps, so the design counts barriers and LDS
 // round trips: every thread issues all of its global loads before using any, keys stay in
 // registers, a select round costs one barrier (every wave scans the round's histogram
@@ -53,36 +44,19 @@ namespace dh {
 namespace {
 
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9-family raw buffer: 32-bit data format
-constexpr int kCacheDevice = 16;         // gfx950 cache policy SC1: device-scope coherent
 typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 
-// The lists a workgroup hands to the merging workgroup of its row, which may run on another
-// of the chip's dies (each has its own L2).  They are stored at device scope (SC1: written
-// through to where the dies' caches are coherent) and read back at device scope (SC1 loads,
-// which take no stale line from the reader's L2).  A wave's vmcnt reaching 0 means its
-// stores have been acknowledged there, so a wave waits for that before its workgroup takes
-// its ticket.  This avoids the release fence's write-back of the whole L2, which measured
-// many times the cost of the top-k itself.
-__device__ __forceinline__ void publish(uint64_t *p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t fetch(const uint64_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Two selects over the 64-bit keys a workgroup holds in registers (all distinct, 0 for an
-// ineligible entry); each finds the keys of the min(k, n) largest, n being the number of
-// non-zero keys.
-//  * select_bins (the usual one): one histogram round over the keys' values, in 256 bins of
-//    equal width between the smallest and the largest value (a monotone map, so a higher bin
-//    only holds larger values).  Logits spread over such bins; their order-preserving bits
-//    do not (the best logits of a row share their exponent, so a first round on the top
-//    byte of the bits puts most of them in one bin and serializes its LDS atomics).  The
-//    bin holding the k-th key is then resolved exactly: its keys are gathered in LDS and each
-//    counts the keys of the bin above it.
+// The merge's select over the 64-bit keys a workgroup holds in registers (all distinct, 0
+// for an ineligible entry) finds the keys of the min(k, n) largest, n being the number of
+// non-zero keys, in two ways:
+//  * usually one histogram round over the keys' values, in 256 bins of equal width between
+//    the smallest and the largest value (a monotone map, so a higher bin only holds larger
+//    values).  Logits spread over such bins; their order-preserving bits do not (the best
+//    logits of a row share their exponent, so a first round on the top byte of the bits puts
+//    most of them in one bin and serializes its LDS atomics).  The bin holding the k-th key
+//    is then resolved exactly: its keys are gathered in LDS and each counts the keys of the
+//    bin above it;
 //  * select_top, the fallback for a crowded boundary bin (many equal or nearly equal
 //    values): a radix select over the keys' bytes from the top, a round per byte, stopping as
 //    soon as the boundary byte's bin is taken whole.  Each round has a histogram of its own,
@@ -96,7 +70,6 @@ template <int NT>
 struct SelectLds {
     uint32_t hist[kHistWords];                     // round histograms; [256..) the bin's keys
     uint32_t imin[NT / 64], imax[NT / 64];         // per-wave extremes of the non-zero images
-    float smax[NT / 64], ssum[NT / 64];            // per-wave softmax statistics (STATS)
     uint64_t bkey;                                 // the boundary bin's cut
     uint32_t fill, bfill;                          // survivors / boundary keys placed so far
 };
@@ -123,7 +96,7 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Clears what select_bins needs (its round's histogram and the counters); the fallback
+// Clears what the value-bin round needs (its histogram and the counters); the fallback
 // clears the other rounds' histograms itself.
 template <int NT>
 __device__ __forceinline__ void clear_select(SelectLds<NT> &sh)
@@ -213,9 +186,9 @@ __device__ __forceinline__ uint64_t select_top(const uint64_t (&key)[N], uint32_
     return base;                                   // not reached: shift 0 ends by then
 }
 
-// The outcome of select_bins: the survivors are the non-zero keys whose bin is above d, or
-// is d with a key >= P (rem of them); when not binned, every non-zero key.  Unless crowded
-// (the fallback ran), hist[0..256) still holds every bin's count of non-zero keys.
+// The outcome of the value-bin round: the survivors are the non-zero keys whose bin is above
+// d, or is d with a key >= P (rem of them); when not binned, every non-zero key.  Unless
+// crowded (the fallback ran), hist[0..256) still holds every bin's count of non-zero keys.
 struct Cut {
     bool binned, crowded;
     uint32_t d, rem;
@@ -227,166 +200,6 @@ __device__ __forceinline__ bool survives(const Cut &c, uint64_t key, uint32_t bi
     return key != 0 && (!c.binned || bin > c.d || (bin == c.d && key >= c.P));
 }
 
-// Before the call: clear_select, publish_range, a barrier.  bin[i] receives key i's bin.
-template <int N, int NT>
-__device__ __forceinline__ Cut select_bins(const uint64_t (&key)[N], uint32_t k, SelectLds<NT> &sh,
-                           uint32_t &total, uint32_t (&bin)[N])
-{
-    uint32_t mn = ~0u, mx = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; w++) {
-        mn = sh.imin[w] < mn ? sh.imin[w] : mn;
-        mx = sh.imax[w] > mx ? sh.imax[w] : mx;
-    }
-    Cut c{false, false, 0u, 0u, 1ull};
-    total = 0;
-#pragma unroll
-    for (int i = 0; i < N; i++)
-        bin[i] = 0;
-    if (mx == 0)
-        return c;                                  // no eligible entry
-    // bin(x) = min(255, floor((x - lo) * scale)): monotone in x.  Degenerate ranges stay
-    // monotone: a zero width (scale +inf) or a +inf maximum (scale 0) send the values that
-    // make (x - lo) * scale NaN or infinite to bin 255 (fminf drops a NaN) and the rest to 0.
-    const float lo = image_float(mn);
-    const float scale = 256.0f / (image_float(mx) - lo);
-    uint32_t *h = sh.hist;
-#pragma unroll
-    for (int i = 0; i < N; i++) {
-        bin[i] = (uint32_t)fminf((image_float((uint32_t)(key[i] >> 32)) - lo) * scale, 255.0f);
-        if (key[i] != 0)
-            atomicAdd(&h[bin[i]], 1u);
-    }
-    __syncthreads();
-    uint32_t d, above, count;
-    total = locate<256>(h, k, d, above, count);
-    if (total <= k)
-        return c;                                  // every non-zero key
-    c.binned = true;
-    c.d = d;
-    const uint32_t rem = k - above;
-    c.rem = rem;
-    if (count == rem)
-        return c;                                  // the boundary bin is taken whole
-    if (count <= (uint32_t)kBoundMax && count <= (uint32_t)NT) {
-        // the bin's keys to LDS; the key with exactly rem - 1 of them above it is the cut
-        uint64_t *list = reinterpret_cast<uint64_t *>(sh.hist + 256);
-        uint32_t mine = 0;
-#pragma unroll
-        for (int i = 0; i < N; i++)
-            mine += key[i] != 0 && bin[i] == d;
-        uint32_t at = wave_reserve(mine, &sh.bfill);
-        if (mine) {
-#pragma unroll
-            for (int i = 0; i < N; i++)
-                if (key[i] != 0 && bin[i] == d)
-                    list[at++] = key[i];
-        }
-        __syncthreads();
-        if (threadIdx.x < count) {
-            const uint64_t x = list[threadIdx.x];
-            if (count_above(list, (int)count, x) == rem - 1)
-                sh.bkey = x;
-        }
-        __syncthreads();
-        c.P = sh.bkey;
-        return c;
-    }
-    // a crowded boundary bin: the radix select among its keys
-    c.crowded = true;
-    __syncthreads();
-    for (int i = threadIdx.x; i < kHistWords; i += NT)
-        sh.hist[i] = 0;
-    __syncthreads();
-    uint32_t n2;
-    c.P = select_top<N, NT>(key, rem, sh, n2, [&](int i) { return bin[i] == d; });
-    return c;
-}
-
-// The chunk pass: the best min(k, n) of chunk c of row r (its NT * PER logits; thread t
-// holds entries base + j * NT + t) to the row's list slots cand[r][c][0..k), in any order,
-// the remaining slots zero.  STATS: the chunk's (m_c, s_c) to stats[r][c].
-template <int NT, int PER, bool STATS>
-__device__ __forceinline__ void chunk_pass(const float *logits, int64_t V, int k, int nchunks, int r,
-                                  int c, uint64_t *cand, float2 *stats, SelectLds<NT> &sh)
-{
-    const int64_t base = (int64_t)c * (NT * PER);
-
-    // coalesced buffer loads bounded by the row, all issued before any is used; entries
-    // past V read as 0 and are masked by their index
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(logits + (int64_t)r * V), (short)0, (int)(V * 4), kRsrcWord3);
-    uint32_t u[PER];
-#pragma unroll
-    for (int j = 0; j < PER; j++)
-        u[j] = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (uint32_t)(base + j * NT + threadIdx.x) * 4u, 0, 0);
-    clear_select<NT>(sh);
-    uint64_t key[PER];
-#pragma unroll
-    for (int j = 0; j < PER; j++) {
-        const int64_t id = base + j * NT + threadIdx.x;
-        const uint32_t im = id < V ? order_key(__uint_as_float(u[j])) : 0u;
-        key[j] = im ? entry_key(im, (uint32_t)id) : 0ull;
-    }
-    publish_range<PER, NT>(key, sh);
-    float lmax = -__builtin_inff();
-    if constexpr (STATS) {
-#pragma unroll
-        for (int j = 0; j < PER; j++) {
-            const float f = __uint_as_float(u[j]);
-            if (key[j] != 0 && f > lmax)
-                lmax = f;
-        }
-        lmax = wave_max(lmax);
-        if ((threadIdx.x & 63) == 0)
-            sh.smax[threadIdx.x >> 6] = lmax;
-    }
-    __syncthreads();
-    if constexpr (STATS) {
-        // the chunk's maximum, then this wave's sum; the select's first barrier publishes it
-        lmax = sh.smax[0];
-#pragma unroll
-        for (int w = 1; w < NT / 64; w++)
-            lmax = sh.smax[w] > lmax ? sh.smax[w] : lmax;
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < PER; j++)
-            if (key[j] != 0)
-                s += rel_exp(__uint_as_float(u[j]), lmax);
-        s = wave_sum(s);
-        if ((threadIdx.x & 63) == 0)
-            sh.ssum[threadIdx.x >> 6] = s;
-    }
-    uint32_t n, bin[PER];
-    const Cut cut = select_bins<PER, NT>(key, (uint32_t)k, sh, n, bin);
-    if constexpr (STATS) {
-        if (threadIdx.x == 0) {
-            float s = 0.f;
-            for (int w = 0; w < NT / 64; w++)
-                s += sh.ssum[w];
-            publish(reinterpret_cast<uint64_t *>(stats + (int64_t)r * nchunks + c),
-                    ((uint64_t)__float_as_uint(s) << 32) | __float_as_uint(lmax));
-        }
-    }
-    const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
-
-    // survivors in any order (the merge takes the lists as sets)
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < PER; j++)
-        mine += survives(cut, key[j], bin[j]);
-    uint64_t *out = cand + ((int64_t)r * nchunks + c) * k;
-    uint32_t at = wave_reserve(mine, &sh.fill);
-    if (mine) {
-#pragma unroll
-        for (int j = 0; j < PER; j++)
-            if (survives(cut, key[j], bin[j]) && at < (uint32_t)k)   // exactly `kept` survive
-                publish(&out[at++], key[j]);
-    }
-    for (int s = kept + threadIdx.x; s < k; s += NT)
-        publish(&out[s], 0ull);                    // empty slots
-}
 
 // One step of a descending bitonic network on the key x held by slot i (a lane): the
 // partner is slot i ^ stride, and in a block of `size` whose size bit is clear the lower
@@ -448,15 +261,15 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x, int l)
     return bitonic<64, 1>(x, l);
 }
 
-// The merge's select, select_sorted: select_bins that also puts the survivors in order.  The
-// histogram's atomics return each key's index among its bin's keys; bin b's survivors then
-// take the slots [start[b], start[b] + s(b)) of the output, s(b) being the bin's count above
-// the boundary bin d and rem in it (start: a suffix sum over the bins).  A survivor of a bin
-// above d goes to start[b] + its index, and the final pass counts the keys of its bin above
-// it; the survivors of bin d are picked by ranking its keys against each other (as
-// select_bins resolves its boundary), and that rank is already their place.  Bins are narrow,
-// so the final counts are short.  start and the bin of each slot live in the histogram words
-// past the boundary keys.
+// The merge's select, select_sorted: the value-bin round that also puts the survivors in
+// order.  The histogram's atomics return each key's index among its bin's keys; bin b's
+// survivors then take the slots [start[b], start[b] + s(b)) of the output, s(b) being the
+// bin's count above the boundary bin d and rem in it (start: a suffix sum over the bins).  A
+// survivor of a bin above d goes to start[b] + its index, and the final pass counts the keys
+// of its bin above it; the survivors of bin d are picked by ranking its keys against each
+// other (the exact resolution of the boundary bin above), and that rank is already their
+// place.  Bins are narrow, so the final counts are short.  start and the bin of each slot
+// live in the histogram words past the boundary keys.
 constexpr int kStartOff = 256 + 2 * kBoundMax;
 constexpr int kBinOfOff = kStartOff + 256;
 constexpr uint32_t kPlaced = 0xffffffffu;   // a slot's bin when its key is already in order
@@ -522,7 +335,7 @@ __device__ __forceinline__ int select_sorted(const uint64_t (&key)[N], uint32_t 
         bin[i] = 0;
     if (mx == 0)
         return 0;                                  // no eligible entry
-    const float lo = image_float(mn);              // the value bins, as select_bins
+    const float lo = image_float(mn);              // the value bins
     const float scale = 256.0f / (image_float(mx) - lo);
     uint32_t *h = sh.hist;
     uint32_t idx[N];
@@ -744,118 +557,6 @@ __device__ __forceinline__ void emit_padding(int kk, int k, int32_t *rid, float 
         argmax[r] = 0;
 }
 
-// The merge of row r: a thread holds MPER of the row's nchunks * k list slots
-// (MPER * NT >= nchunks * k), and the same select as the chunk pass keeps k of them.  STATS:
-// the row's softmax statistics from the chunks' (m_c, s_c): probs[r][slot] and lse[r].
-template <int MPER, int NT, bool STATS>
-__device__ __forceinline__ void merge_row(const float *logits, int64_t V, int k, int nchunks, int r,
-                                 const uint64_t *cand, const int32_t *idmap, int32_t *ids,
-                                 float *vals, int32_t *argmax, const float2 *stats,
-                                 float *probs, float *lse, SelectLds<NT> &sh, MergeLds &ml)
-{
-    const int slots = nchunks * k;
-    const uint64_t *src = cand + (int64_t)r * slots;
-
-    // all loads issued together (bounded buffer loads: slots past the end read as 0)
-    const __amdgpu_buffer_rsrc_t ls = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)src, (short)0, slots * 8, kRsrcWord3);
-    uint64_t key[MPER];
-#pragma unroll
-    for (int j = 0; j < MPER; j++) {
-        const v2u32 q = __builtin_amdgcn_raw_buffer_load_b64(
-            ls, (uint32_t)(j * NT + threadIdx.x) * 8u, 0, kCacheDevice);
-        key[j] = ((uint64_t)q.y << 32) | q.x;
-    }
-    if constexpr (STATS) {
-        // wave 0: m = max_c m_c, then z = sum_c s_c exp(m_c - m), chunks c = lane, lane + 64,
-        // ... summed in that order per lane, then across lanes by a butterfly (published to
-        // the other waves by the select's first barrier)
-        if (threadIdx.x < 64) {
-            const uint64_t *st = reinterpret_cast<const uint64_t *>(stats + (int64_t)r * nchunks);
-            constexpr int kMaxChunks = DH_MAX_VOCAB / 2048;
-            float cm[kMaxChunks / 64], cs[kMaxChunks / 64];   // this lane's chunks' (m_c, s_c)
-#pragma unroll
-            for (int j = 0; j < kMaxChunks / 64; j++) {
-                const int c = threadIdx.x + 64 * j;
-                const uint64_t v = c < nchunks ? fetch(&st[c]) : 0ull;
-                cm[j] = c < nchunks ? __uint_as_float((uint32_t)v) : -__builtin_inff();
-                cs[j] = __uint_as_float((uint32_t)(v >> 32));
-            }
-            float m = -__builtin_inff();
-#pragma unroll
-            for (int j = 0; j < kMaxChunks / 64; j++)
-                m = cm[j] > m ? cm[j] : m;
-            m = wave_max(m);
-            float z = 0.f;
-#pragma unroll
-            for (int j = 0; j < kMaxChunks / 64; j++)
-                if (cs[j] > 0.f)
-                    z += cs[j] * rel_exp(cm[j], m);
-            z = wave_sum(z);
-            if (threadIdx.x == 0) {
-                ml.row_m = m;
-                ml.row_z = z;
-                lse[r] = z > 0.f ? m + logf(z) : -__builtin_inff();
-            }
-        }
-    }
-    uint64_t x;
-    uint32_t rank;
-    const int kk = select_rank<MPER, NT>(key, k, sh, ml, x, rank);
-    int32_t *rid = ids + (int64_t)r * k;
-    float *rval = vals + (int64_t)r * k;
-    float *rprob = STATS ? probs + (int64_t)r * k : nullptr;
-    if (x != 0)
-        emit_survivor<STATS>(x, rank, logits + (int64_t)r * V, idmap, rid, rval, rprob, argmax,
-                             r, ml);
-    emit_padding<STATS>(kk, k, rid, rval, rprob, argmax, r);
-}
-
-struct TopkArgs {
-    const float *logits;
-    int64_t V;
-    int k, nchunks;
-    uint64_t *cand;
-    float2 *stats;          // STATS only
-    uint32_t *tickets;      // [rows], zero at the start
-    const int32_t *idmap;
-    int32_t *ids;
-    float *vals;
-    int32_t *argmax;
-    float *probs, *lse;     // STATS only
-};
-
-// The whole top-k in one launch: a workgroup of NT threads per (chunk, row) runs the chunk
-// pass; the row's last workgroup to finish runs the merge.  Every wave's list stores are
-// acknowledged at device scope (publish, stores_done) before the workgroup takes its ticket;
-// the last workgroup reads the row's lists at device scope.  Nothing waits on another
-// workgroup: every workgroup either ends after its ticket or merges.
-template <int NT, int PER, int MPER, bool STATS>
-__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a)
-{
-    __shared__ __align__(16) SelectLds<NT> sh;
-    __shared__ __align__(16) MergeLds ml;
-    __shared__ uint32_t last;
-    const int r = blockIdx.y, c = blockIdx.x;
-    chunk_pass<NT, PER, STATS>(a.logits, a.V, a.k, a.nchunks, r, c, a.cand, a.stats, sh);
-    stores_done();
-    __syncthreads();
-    if (threadIdx.x == 0)
-        last = atomicAdd(&a.tickets[(int64_t)r * kTicketStride], 1u) == (uint32_t)a.nchunks - 1u;
-    __syncthreads();
-    if (!last)
-        return;
-    merge_row<MPER, NT, STATS>(a.logits, a.V, a.k, a.nchunks, r, a.cand, a.idmap,
-                                       a.ids, a.vals, a.argmax, a.stats, a.probs, a.lse, sh,
-                                       ml);
-}
-
-__global__ __launch_bounds__(64) void zero_tickets(uint32_t *t, int n)
-{
-    if ((int)threadIdx.x < n)
-        t[threadIdx.x * kTicketStride] = 0u;
-}
-
 // The merge of the GEMV's cuts (topk.h, dh_draft's fused top-k).
 struct CutArgs {
     const float *logits;    // [rows][V], as the GEMV wrote them
@@ -868,8 +569,11 @@ struct CutArgs {
     int32_t *ids;
     float *vals;
     int32_t *argmax;
+    const float2 *stats;    // STATS: the chunks' (m_c, s_c), [rows][grid]
+    float *probs, *lse;     // STATS: [rows][k], [rows]
 };
 constexpr int kCutPass = 16;   // keys a thread holds in a pass over the re-read chunks
+constexpr int kStatsMaxChunks = 256;   // STATS: chunks a row, at most (cut_pass's grid)
 
 struct CutLds {
     uint64_t run[DH_MAX_K];          // the best k of the passes so far, by rank
@@ -879,10 +583,45 @@ struct CutLds {
     uint16_t faillist[kCutMaxChunks];
 };
 
+// The row's softmax statistics from its chunks' (m_c, s_c), by wave 0: m = max_c m_c, then
+// z = sum_c s_c exp(m_c - m) over the chunks c = lane + 64 j of each lane in j order, then
+// across the lanes by a fixed butterfly, so the sums are reproducible.  m and z go to ml (for
+// the probabilities; the select's first barrier publishes them), log-sum-exp m + log z to lse.
+template <int J>
+__device__ __forceinline__ void row_stats(const float2 *st, int nchunks, float *lse, MergeLds &ml)
+{
+    float cm[J], cs[J];
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+        const int c = (int)threadIdx.x + 64 * j;
+        const float2 v = c < nchunks ? st[c] : float2{-__builtin_inff(), 0.f};
+        cm[j] = v.x;
+        cs[j] = v.y;
+    }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < J; j++)
+        m = cm[j] > m ? cm[j] : m;
+    m = wave_max(m);
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; j++)
+        if (cs[j] > 0.f)
+            z += cs[j] * rel_exp(cm[j], m);
+    z = wave_sum(z);
+    if (threadIdx.x == 0) {
+        ml.row_m = m;
+        ml.row_z = z;
+        *lse = z > 0.f ? m + logf(z) : -__builtin_inff();
+    }
+}
+
 // One workgroup per row: the k best of the row's cuts (MF keys a thread), the floors checked
 // against the k-th of them, and when a chunk's floor beats it, passes over the other chunks'
 // cuts and those chunks' logits (read back whole), each pass keeping the k best so far.
-template <int MF>
+// STATS: the row's softmax statistics as well (the chunks' (m_c, s_c) from cut_pass), each
+// kept entry's probability and the row's log-sum-exp.
+template <int MF, bool STATS>
 __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
 {
     constexpr int NT = kCutThreads;
@@ -908,6 +647,10 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
         cl.nfail = 0;
         cl.t = 0;
     }
+    if constexpr (STATS)
+        if (tid < kWave)
+            row_stats<kStatsMaxChunks / kWave>(a.stats + (int64_t)r * a.grid, a.grid, a.lse + r,
+                                               ml);
     uint64_t x;
     uint32_t rank;
     int kk = select_rank<MF, NT>(key, a.k, sh, ml, x, rank);
@@ -964,9 +707,10 @@ __global__ __launch_bounds__(kCutThreads) void cut_merge(CutArgs a)
             __syncthreads();
         }
     }
+    float *rprob = STATS ? a.probs + (int64_t)r * a.k : nullptr;
     if (x != 0)
-        emit_survivor<false>(x, rank, lrow, a.idmap, rid, rval, nullptr, a.argmax, r, ml);
-    emit_padding<false>(kk, a.k, rid, rval, nullptr, a.argmax, r);
+        emit_survivor<STATS>(x, rank, lrow, a.idmap, rid, rval, rprob, a.argmax, r, ml);
+    emit_padding<STATS>(kk, a.k, rid, rval, rprob, a.argmax, r);
 }
 
 // The standalone top-k's cut (dh_topk and dh_topk_mapped without softmax statistics): the
@@ -985,19 +729,25 @@ struct CutPassArgs {
     int m, slots;
     uint64_t *keys;         // [rows][grid][slots]
     uint64_t *floors;       // [rows][grid]
+    float2 *stats;          // STATS: [rows][grid]
 };
 constexpr int kCutPassThreads = 256;   // one histogram bin a thread (512 measured slower)
 static_assert(kCutPassThreads == 256, "a thread clears one of the 256 bins");
 constexpr int kCutPassMaxPer = 16;    // entries a thread holds, at most
 constexpr int kCutPassMaxGrid = 256;  // chunks a row: 1024 / rows within these bounds (fewer
 constexpr int kCutPassMinGrid = 64;   // when the row has fewer tiles)
+static_assert(kCutPassMaxGrid <= kStatsMaxChunks, "the merge reads every chunk's statistics");
 
-template <int PER>
+// STATS: the chunk's largest eligible logit m_c and s_c = the sum of exp(l - m_c) over its
+// eligible logits (a thread's entries in order, then the wave's butterfly, then the waves in
+// order) to stats[r][c]; (-inf, 0) for a chunk with no eligible logit.
+template <int PER, bool STATS>
 __global__ __launch_bounds__(kCutPassThreads) void cut_pass(CutPassArgs a)
 {
     constexpr int NW = kCutPassThreads / kWave;
     __shared__ __align__(16) uint32_t hist[256];
     __shared__ uint32_t wmn[NW], wmx[NW];
+    __shared__ float wlm[NW], wls[NW];   // STATS: per-wave largest logit, then sum
     __shared__ uint32_t cnt;
     __shared__ unsigned long long gfloor;
     const int c = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
@@ -1027,24 +777,48 @@ __global__ __launch_bounds__(kCutPassThreads) void cut_pass(CutPassArgs a)
         mx = im[u] > mx ? im[u] : mx;
     }
     wave_min_max32(mn, mx);
+    float lmax = -__builtin_inff();
+    if constexpr (STATS) {
+#pragma unroll
+        for (int u = 0; u < PER; u++)
+            lmax = im[u] != 0 && l[u] > lmax ? l[u] : lmax;
+        lmax = wave_max(lmax);
+    }
     if ((tid & 63) == 0) {
         wmn[tid >> 6] = mn;
         wmx[tid >> 6] = mx;
+        if constexpr (STATS)
+            wlm[tid >> 6] = lmax;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; w++) {
         mn = wmn[w] < mn ? wmn[w] : mn;
         mx = wmx[w] > mx ? wmx[w] : mx;
+        if constexpr (STATS)
+            lmax = wlm[w] > lmax ? wlm[w] : lmax;
     }
     uint64_t *out = a.keys + ((int64_t)r * G + c) * a.slots;
     uint64_t *floor = a.floors + (int64_t)r * G + c;
     if (mx == 0) {   // no eligible entry (the same for the whole workgroup)
         for (int q = tid; q < a.slots; q += kCutPassThreads)
             out[q] = 0;
-        if (tid == 0)
+        if (tid == 0) {
             *floor = 0;
+            if constexpr (STATS)
+                a.stats[(int64_t)r * G + c] = float2{-__builtin_inff(), 0.f};
+        }
         return;
+    }
+    if constexpr (STATS) {
+        float sum = 0.f;
+#pragma unroll
+        for (int u = 0; u < PER; u++)
+            if (im[u] != 0)
+                sum += rel_exp(l[u], lmax);
+        sum = wave_sum(sum);
+        if ((tid & 63) == 0)
+            wls[tid >> 6] = sum;   // read after the histogram's barrier
     }
     // 2: the histogram (the select's bin map; a NaN product, from a zero or infinite width,
     // goes to 255)
@@ -1058,6 +832,14 @@ __global__ __launch_bounds__(kCutPassThreads) void cut_pass(CutPassArgs a)
         if (im[u] != 0)
             atomicAdd(&hist[bin_of(im[u])], 1u);
     __syncthreads();
+    if constexpr (STATS)
+        if (tid == 0) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; w++)
+                sum += wls[w];
+            a.stats[(int64_t)r * G + c] = float2{lmax, sum};
+        }
     // 3: the cut (every key when at most m, bins >= d, or bins > d) to the slots
     uint32_t d, above, count;
     const uint32_t total = locate<256>(hist, (uint32_t)a.m, d, above, count);
@@ -1096,11 +878,9 @@ CutShape cut_shape(int k, int chunks)
 TopkWs topk_ws_layout(int rows, int64_t vocab, int k)
 {
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
-    const size_t nc = (size_t)topk_shape(rows, vocab, k).nchunks;
     TopkWs w;
-    w.keys_off = 0;   // the chunk lists hold keys that carry both the value and the id
-    w.stats_off = up((size_t)rows * nc * (size_t)k * sizeof(uint64_t));
-    w.tickets_off = w.stats_off + up((size_t)rows * nc * 2 * sizeof(float));
+    w.stats_off = 0;
+    w.tickets_off = up((size_t)rows * kStatsMaxChunks * sizeof(float2));
     const int64_t ntiles = (vocab + 15) / 16;
     const size_t gcap = (size_t)(ntiles < kCutMaxChunks ? ntiles : kCutMaxChunks);
     w.cut_keys_off =
@@ -1125,15 +905,32 @@ GemvCut topk_cut(void *ws, int rows, int64_t vocab, int k)
                    kCutThreads * kCutMaxFast};
 }
 
+template <bool STATS>
+hipError_t launch_merge(const CutArgs &a, int rows, int nfast, hipStream_t stream)
+{
+    const dim3 g(rows), b(kCutThreads);
+    // the smallest instance holding the cuts
+    const int mf = (nfast + kCutThreads - 1) / kCutThreads;
+    if (mf <= 1) return launch(cut_merge<1, STATS>, g, b, 0, stream, a);
+    if (mf <= 2) return launch(cut_merge<2, STATS>, g, b, 0, stream, a);
+    if (mf <= 3) return launch(cut_merge<3, STATS>, g, b, 0, stream, a);
+    if (mf <= 4) return launch(cut_merge<4, STATS>, g, b, 0, stream, a);
+    if (mf <= 6) return launch(cut_merge<6, STATS>, g, b, 0, stream, a);
+    static_assert(kCutMaxFast == 8, "the instances above and below cover the fast keys");
+    return launch(cut_merge<8, STATS>, g, b, 0, stream, a);
+}
+
 hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
                             const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                            void *ws, int grid, hipStream_t stream, int slots, int64_t chunk)
+                            void *ws, int grid, hipStream_t stream, int slots, int64_t chunk,
+                            float *probs, float *lse)
 {
     GemvCut cut = topk_cut(ws, rows, vocab, k);
     if (slots > 0)
         cut.slots = slots;
     const int nfast = grid * cut.slots;
-    if (grid < 1 || grid > kCutMaxChunks || nfast > kCutThreads * kCutMaxFast)
+    if (grid < 1 || grid > kCutMaxChunks || nfast > kCutThreads * kCutMaxFast ||
+        (probs && grid > kStatsMaxChunks))
         return hipErrorInvalidValue;
     CutArgs a;
     a.logits = logits;
@@ -1149,24 +946,17 @@ hipError_t launch_cut_merge(const float *logits, int rows, int64_t vocab, int k,
     a.ids = ids;
     a.vals = vals;
     a.argmax = argmax;
-    const dim3 g(rows), b(kCutThreads);
-    // the smallest instance holding the cuts
-    const int mf = (nfast + kCutThreads - 1) / kCutThreads;
-    if (mf <= 1) return launch(cut_merge<1>, g, b, 0, stream, a);
-    if (mf <= 2) return launch(cut_merge<2>, g, b, 0, stream, a);
-    if (mf <= 3) return launch(cut_merge<3>, g, b, 0, stream, a);
-    if (mf <= 4) return launch(cut_merge<4>, g, b, 0, stream, a);
-    if (mf <= 6) return launch(cut_merge<6>, g, b, 0, stream, a);
-    if (mf <= 8 || kCutMaxFast <= 8) return launch(cut_merge<8>, g, b, 0, stream, a);
-    if constexpr (kCutMaxFast > 8) {
-        if (mf <= 12) return launch(cut_merge<12>, g, b, 0, stream, a);
-        if (mf <= 16 || kCutMaxFast <= 16) return launch(cut_merge<16>, g, b, 0, stream, a);
-    }
-    if constexpr (kCutMaxFast > 16) {
-        if (mf <= 24) return launch(cut_merge<24>, g, b, 0, stream, a);
-        return launch(cut_merge<32>, g, b, 0, stream, a);
-    }
-    return hipErrorInvalidValue;
+    a.stats = probs ? topk_stats(ws, rows, vocab, k) : nullptr;
+    a.probs = probs;
+    a.lse = lse;
+    return probs ? launch_merge<true>(a, rows, nfast, stream)
+                 : launch_merge<false>(a, rows, nfast, stream);
+}
+
+float2 *topk_stats(void *ws, int rows, int64_t vocab, int k)
+{
+    return reinterpret_cast<float2 *>(static_cast<char *>(ws) +
+                                      topk_ws_layout(rows, vocab, k).stats_off);
 }
 
 uint32_t *topk_tickets(void *ws, int rows, int64_t vocab, int k)
@@ -1175,104 +965,52 @@ uint32_t *topk_tickets(void *ws, int rows, int64_t vocab, int k)
                                         topk_ws_layout(rows, vocab, k).tickets_off);
 }
 
-template <int NT, int PER, int MPER, bool STATS>
-hipError_t launch_shape(const TopkArgs &a, int rows, hipStream_t stream)
-{
-    return launch(topk_kernel<NT, PER, MPER, STATS>, dim3(a.nchunks, rows), dim3(NT), 0,
-                  stream, a);
-}
-
-template <int NT, int PER, bool STATS>
-hipError_t launch_nt(const TopkArgs &a, int rows, hipStream_t stream)
-{
-    const int64_t slots = (int64_t)a.nchunks * a.k;   // <= kMergePer * NT by the shape rule
-    if (slots <= NT)
-        return launch_shape<NT, PER, 1, STATS>(a, rows, stream);
-    if (slots <= 2 * NT)
-        return launch_shape<NT, PER, 2, STATS>(a, rows, stream);
-    if (slots <= 4 * NT)
-        return launch_shape<NT, PER, 4, STATS>(a, rows, stream);
-    if (slots <= 8 * NT)
-        return launch_shape<NT, PER, 8, STATS>(a, rows, stream);
-    return launch_shape<NT, PER, kMergePer, STATS>(a, rows, stream);
-}
-
 template <bool STATS>
-hipError_t launch_stats(const TopkArgs &a, const TopkShape &sh, int rows, hipStream_t stream)
+hipError_t launch_pass(int pt, dim3 g, dim3 b, const CutPassArgs &c, hipStream_t stream)
 {
-    switch (sh.nt * 16 + sh.per) {
-    case 512 * 16 + 4: return launch_nt<512, 4, STATS>(a, rows, stream);
-    case 1024 * 16 + 4: return launch_nt<1024, 4, STATS>(a, rows, stream);
-    case 256 * 16 + 8: return launch_nt<256, 8, STATS>(a, rows, stream);
-    case 512 * 16 + 8: return launch_nt<512, 8, STATS>(a, rows, stream);
-    default: return launch_nt<1024, 8, STATS>(a, rows, stream);
-    }
+    return pt <= 1   ? launch(cut_pass<1, STATS>, g, b, 0, stream, c)
+           : pt <= 2 ? launch(cut_pass<2, STATS>, g, b, 0, stream, c)
+           : pt <= 4 ? launch(cut_pass<4, STATS>, g, b, 0, stream, c)
+           : pt <= 8 ? launch(cut_pass<8, STATS>, g, b, 0, stream, c)
+                     : launch(cut_pass<16, STATS>, g, b, 0, stream, c);
 }
 
 hipError_t launch_topk(const float *logits, int rows, int64_t vocab, int k,
                        const int32_t *idmap, int32_t *ids, float *vals, int32_t *argmax,
-                       void *ws, hipStream_t stream, float *probs, float *lse,
-                       bool tickets_zeroed)
+                       void *ws, hipStream_t stream, float *probs, float *lse)
 {
-    const TopkWs w = topk_ws_layout(rows, vocab, k);
-    TopkArgs a;
-    a.logits = logits;
-    a.V = vocab;
-    a.k = k;
-    const TopkShape shape = topk_shape(rows, vocab, k);
-    a.nchunks = (int)shape.nchunks;
-    a.cand = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + w.keys_off);
-    a.stats = probs ? reinterpret_cast<float2 *>(static_cast<char *>(ws) + w.stats_off)
-                    : nullptr;
-    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + w.tickets_off);
-    a.idmap = idmap;
-    a.ids = ids;
-    a.vals = vals;
-    a.argmax = argmax;
-    a.probs = probs;
-    a.lse = lse;
-    if (!probs) {
-        // the cut of every chunk, then their merge (two launches, no tickets).  Chunks a row:
-        // 256 for up to 4 rows, then fewer and larger ones, so that the call has about 1024
-        // workgroups (at 16 rows, 4096 workgroups of 512 entries took 8.6 us against 3.4 us
-        // for the 256 of one row); each chunk's cut is sized for its share of the k.
-        const int64_t ntiles = (vocab + 15) / 16;
-        int G = 1024 / rows;
-        G = G < kCutPassMinGrid ? kCutPassMinGrid : G > kCutPassMaxGrid ? kCutPassMaxGrid : G;
-        G = (int)(ntiles < G ? ntiles : G);
-        const CutShape cs = cut_shape(k, G);
-        const int64_t chunk = (ntiles + G - 1) / G * 16;   // whole tiles, so G chunks cover V
-        const int pt = (int)((chunk + kCutPassThreads - 1) / kCutPassThreads);
-        const GemvCut cut = topk_cut(ws, rows, vocab, k);
-        if (pt <= kCutPassMaxPer && (int64_t)G * cs.slots <= kCutThreads * kCutMaxFast) {
-            CutPassArgs c;
-            c.logits = logits;
-            c.V = vocab;
-            c.chunk = chunk;
-            c.m = cs.m;
-            c.slots = cs.slots;
-            c.keys = cut.keys;
-            c.floors = cut.floors;
-            const dim3 g((unsigned)G, (unsigned)rows), b(kCutPassThreads);
-            hipError_t e = pt <= 1   ? launch(cut_pass<1>, g, b, 0, stream, c)
-                           : pt <= 2 ? launch(cut_pass<2>, g, b, 0, stream, c)
-                           : pt <= 4 ? launch(cut_pass<4>, g, b, 0, stream, c)
-                           : pt <= 8 ? launch(cut_pass<8>, g, b, 0, stream, c)
-                                     : launch(cut_pass<16>, g, b, 0, stream, c);
-            if (e != hipSuccess)
-                return e;
-            return launch_cut_merge(logits, rows, vocab, k, idmap, ids, vals, argmax, ws, G,
-                                    stream, cs.slots, chunk);
-        }
-    }
-    if (!tickets_zeroed) {
-        const hipError_t e = launch(zero_tickets, dim3(1), dim3(64), 0, stream, a.tickets, rows);
-        if (e != hipSuccess)
-            return e;
-    }
-    if (probs)
-        return launch_stats<true>(a, shape, rows, stream);
-    return launch_stats<false>(a, shape, rows, stream);
+    // the cut of every chunk, then their merge (two launches, no tickets).  Chunks a row: 256
+    // for up to 4 rows, then fewer and larger ones, so that the call has about 1024
+    // workgroups (at 16 rows, 4096 workgroups of 512 entries took 8.6 us against 3.4 us for
+    // the 256 of one row); each chunk's cut is sized for its share of the k.
+    const int64_t ntiles = (vocab + 15) / 16;
+    int G = 1024 / rows;
+    G = G < kCutPassMinGrid ? kCutPassMinGrid : G > kCutPassMaxGrid ? kCutPassMaxGrid : G;
+    G = (int)(ntiles < G ? ntiles : G);
+    const CutShape cs = cut_shape(k, G);
+    const int64_t chunk = (ntiles + G - 1) / G * 16;   // whole tiles, so G chunks cover V
+    const int pt = (int)((chunk + kCutPassThreads - 1) / kCutPassThreads);
+    // within the library's limits (V <= 2^18: at most 4096 entries a chunk; k <= 512: at
+    // most 64 x 34 or 256 x 16 cut keys a row) both always hold
+    if (pt > kCutPassMaxPer || (int64_t)G * cs.slots > kCutThreads * kCutMaxFast)
+        return hipErrorInvalidValue;
+    const GemvCut cut = topk_cut(ws, rows, vocab, k);
+    CutPassArgs c;
+    c.logits = logits;
+    c.V = vocab;
+    c.chunk = chunk;
+    c.m = cs.m;
+    c.slots = cs.slots;
+    c.keys = cut.keys;
+    c.floors = cut.floors;
+    c.stats = probs ? topk_stats(ws, rows, vocab, k) : nullptr;
+    const dim3 g((unsigned)G, (unsigned)rows), b(kCutPassThreads);
+    hipError_t e = probs ? launch_pass<true>(pt, g, b, c, stream)
+                         : launch_pass<false>(pt, g, b, c, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_cut_merge(logits, rows, vocab, k, idmap, ids, vals, argmax, ws, G, stream,
+                            cs.slots, chunk, probs, lse);
 }
 
 }  // namespace dh

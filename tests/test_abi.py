@@ -49,7 +49,8 @@ def test_workspace_bytes_limits():
     assert dh.workspace_bytes(1, dh.MAX_VOCAB + 1, 8) == 0
     # grows with each size
     assert dh.workspace_bytes(2, 5000, 8) > dh.workspace_bytes(1, 5000, 8)
-    assert dh.workspace_bytes(1, 5000, 64) > dh.workspace_bytes(1, 5000, 8)
+    assert dh.workspace_bytes(1, 5000, 64) >= dh.workspace_bytes(1, 5000, 8)
+    assert dh.workspace_bytes(1, 129280, 512) > dh.workspace_bytes(1, 129280, 8)
 
 
 @pytest.fixture

@@ -5,8 +5,8 @@ oracle's O16, through the C ABI.
  * probabilities within a relative 2e-5 of the oracle's, plus one subnormal quantum (2^-149)
    for probabilities below 2^-126 (pads exactly 0), lse within
    2e-5 * max(1, |lse|), infinities equal.  The bound: z is an fp32 sum of at most 2^18
-   positive terms along a path of at most ~60 additions (8 per thread, 6 butterfly levels,
-   up to 32 waves, 2 chunks per lane, 6 levels), about 4e-6 relative, plus expf's 1 ulp and
+   positive terms along a path of at most ~40 additions (16 a thread, 6 butterfly levels, 4
+   waves of a chunk, 4 chunks a lane, 6 levels), about 3e-6 relative, plus expf's 1 ulp and
    the rounding of l - m, which is |l - m| * 2^-24 relative (6e-6 at |l - m| = 100);
  * planted rows of every kind (NaN, +-inf, ties, subnormals, rows without an eligible
    logit) and the FP8 head's own logits at 16 rows.

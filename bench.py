@@ -585,7 +585,8 @@ def wide_linear(dh, torch, n):
 def topk_sweep(dh, torch, n):
     """dh_topk alone (the cut pass over each row's chunks, then the merge) on the row-sweep
     workload's own logits (FP8 E4M3 + E8M0 32x32 head, H=5120, V=129280): 1 and 16 rows,
-    k = 64 and 512; back to back, and inside a HIP graph (no host launch cost)."""
+    k = 64 and 512; back to back, and inside a HIP graph (no host launch cost); then
+    dh_topk_softmax (the same two kernels with the softmax statistics) the same way."""
     import synth
     c = synth.CONFIGS["row_sweep"]
     V, H = c["V"], c["H"]
@@ -606,7 +607,21 @@ def topk_sweep(dh, torch, n):
             f = lambda i: dh.topk(lg, k, ws=ws, ids=o[0], vals=o[1], argmax=o[2])
             res[f"rows{R}_k{k}"] = {"back_to_back_us": back_to_back_us(f, n),
                                     "graph_us": graph_us(f, n)}
+    for R in (1, 16):
+        lg = lg16[:R].contiguous()
+        for k in (64, 512):
+            ws = dh.workspace(R, V, k)
+            o = {"ids": torch.empty((R, k), dtype=torch.int32, device=dev),
+                 "vals": torch.empty((R, k), dtype=torch.float32, device=dev),
+                 "probs": torch.empty((R, k), dtype=torch.float32, device=dev),
+                 "lse": torch.empty((R,), dtype=torch.float32, device=dev),
+                 "argmax": torch.empty((R,), dtype=torch.int32, device=dev)}
+            f = lambda i: dh.topk_softmax(lg, k, ws=ws, out=o)
+            res[f"rows{R}_k{k}"]["softmax_back_to_back_us"] = back_to_back_us(f, n)
+            res[f"rows{R}_k{k}"]["softmax_graph_us"] = graph_us(f, n)
     log("dh_topk: " + ", ".join(f"{key} {v['graph_us']:.1f} us (graph)" for key, v in res.items()))
+    log("dh_topk_softmax: " + ", ".join(f"{key} {v['softmax_graph_us']:.1f} us (graph)"
+                                         for key, v in res.items()))
     return {"workload": f"logits of the FP8 block head H={H} V={V}", **res}
 
 

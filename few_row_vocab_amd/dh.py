@@ -345,17 +345,30 @@ def topk_mapped(logits, k, idmap, ws=None, ids=None, vals=None, argmax=None,
 
 
 @_on_stream
-def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None):
+def topk_softmax(logits, k, ws=None, with_argmax=True, stream=None, out=None):
     """(ids, vals, argmax, probs fp32 [R][k], lse fp32 [R]): dh_topk plus each row's softmax
-    statistics (probs[:, 0] is the top-1's confidence)."""
+    statistics (probs[:, 0] is the top-1's confidence).  `out`: a dict of preallocated
+    outputs (ids, vals, probs, lse, argmax), any of them."""
     _want(logits, torch.float32, "logits")
     R, V = logits.shape
     dev = logits.device
-    ids = torch.empty((R, k), dtype=torch.int32, device=dev)
-    vals = torch.empty((R, k), dtype=torch.float32, device=dev)
-    probs = torch.empty((R, k), dtype=torch.float32, device=dev)
-    lse = torch.empty((R,), dtype=torch.float32, device=dev)
-    argmax = torch.empty((R,), dtype=torch.int32, device=dev) if with_argmax else None
+    o = {} if out is None else out
+    ids = o.get("ids")
+    ids = torch.empty((R, k), dtype=torch.int32, device=dev) if ids is None else ids
+    vals = o.get("vals")
+    vals = torch.empty((R, k), dtype=torch.float32, device=dev) if vals is None else vals
+    probs = o.get("probs")
+    probs = torch.empty((R, k), dtype=torch.float32, device=dev) if probs is None else probs
+    lse = o.get("lse")
+    lse = torch.empty((R,), dtype=torch.float32, device=dev) if lse is None else lse
+    argmax = o.get("argmax")
+    if argmax is None and with_argmax:
+        argmax = torch.empty((R,), dtype=torch.int32, device=dev)
+    _shaped(ids, (R, k), torch.int32, "ids")
+    _shaped(vals, (R, k), torch.float32, "vals")
+    _shaped(probs, (R, k), torch.float32, "probs")
+    _shaped(lse, (R,), torch.float32, "lse")
+    _shaped(argmax, (R,), torch.int32, "argmax")
     ws = workspace(R, V, k, dev) if ws is None else ws
     _check(lib().dh_topk_softmax(_ptr(logits), R, V, k, _ptr(ids), _ptr(vals), _ptr(argmax),
                                  _ptr(probs), _ptr(lse), _ptr(ws), _ws_bytes(ws),

@@ -130,8 +130,8 @@ def test_graph_subset_and_lowrank():
 
 @pytest.mark.parametrize("R,k", [(1, 64), (16, 512)])
 def test_graph_topk_standalone(R, k):
-    """dh_topk (the cut pass, then the merge), dh_topk_softmax (its tickets zeroed by a small
-    kernel of the call) and dh_rescore_sync (its sync buffer left zero by every call) in one
+    """dh_topk (the cut pass, then the merge), dh_topk_softmax (the same two kernels with the
+    softmax statistics) and dh_rescore_sync (its sync buffer left zero by every call) in one
     graph: every replay equals the eager results."""
     need_gpu()
     V, H = 50000, 256

@@ -93,3 +93,26 @@ def test_topk_softmax_refusals():
                              ws.numel(), st) == 1            # lse overlaps ids
     torch.cuda.synchronize()
     assert bool((probs == 7.0).all())
+
+
+def test_topk_softmax_preallocated_outputs():
+    """The binding's `out` dict: the same bits as freshly allocated outputs, written in place
+    (what a graph-captured caller passes), two calls in a row on different k."""
+    need_gpu()
+    R, V = 16, 20000
+    logits = _planted(R, V, seed=77)
+    d = dev(logits)
+    for k in (64, 512):
+        ws = dh.workspace(R, V, k)
+        o = {"ids": torch.empty((R, k), dtype=torch.int32, device="cuda"),
+             "vals": torch.empty((R, k), dtype=torch.float32, device="cuda"),
+             "probs": torch.empty((R, k), dtype=torch.float32, device="cuda"),
+             "lse": torch.empty((R,), dtype=torch.float32, device="cuda"),
+             "argmax": torch.empty((R,), dtype=torch.int32, device="cuda")}
+        got = dh.topk_softmax(d, k, ws=ws, out=o)
+        ref = dh.topk_softmax(d, k)
+        torch.cuda.synchronize()
+        assert got[0] is o["ids"] and got[3] is o["probs"] and got[4] is o["lse"]
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        check_softmax(logits, k, got)

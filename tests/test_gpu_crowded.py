@@ -202,3 +202,42 @@ def test_draft_topk_512_sixteen_rows(fmt):
     want = oracle.gemv(FMTS[fmt][1], ow, osc, x)
     tols = check_logits(host(out["logits"]), want)
     check_topk(host(out["ids"]), host(out["vals"]), want, k, tols)
+
+
+@pytest.mark.parametrize("tile", [False, True])
+@pytest.mark.parametrize("k", [17, 64, 512])
+def test_draft_topk_32_rows(tile, k):
+    """32 rows (one GEMV launch of two 16-row column blocks, then the top-k's own cut pass
+    and merge) of a clustered head: the first 8 along its planted run (their best keys crowd
+    a few chunks, whose cuts are short), the next 8 zero (every logit tied, every cut
+    empty), the rest random."""
+    need_gpu()
+    V, H, lo, n = 60000, 512, 1000, 600
+    say(f"32 rows tile={tile} k={k}")
+    w, base = clustered_head(V, H, lo, n, seed=181 + k)
+    x = np.concatenate([np.repeat(base[None, :], 8, axis=0), np.zeros((8, H), np.uint16),
+                        synth.random_acts(16, H, seed=182)])
+    gh = dh.Head(dh.BF16, dev_u16(w))
+    out = draft_vs_topk(gh, dev_u16(x), k, tile=tile)
+    want = oracle.gemv(oracle.FMT_BF16, w, None, x)
+    tols = check_logits(host(out["logits"]), want)
+    check_topk(host(out["ids"]), host(out["vals"]), want, k, tols)
+    ids = host(out["ids"])
+    for r in range(8, 16):
+        assert ids[r].tolist() == list(range(k))
+
+
+@pytest.mark.parametrize("fmt", ["block", "bf16"])
+def test_draft_topk_two_launch_rows(fmt):
+    """More than 16 rows of a head too wide for one launch (H = 7168; a row-major bf16 head
+    at H = 5120) take two GEMV launches (rows 0..15, then the rest), then the top-k."""
+    need_gpu()
+    V, H, R, k = 9000, 7168 if fmt == "block" else 5120, 20, 64
+    say(f"two-launch rows {fmt} H={H}")
+    w = synth.random_head(V, H, seed=191, std=0.02)
+    x = synth.random_acts(R, H, seed=192)
+    gh, (ow, osc) = make_heads(fmt, w)
+    out = draft_vs_topk(gh, dev_u16(x), k, tile=(fmt == "block"))
+    want = oracle.gemv(FMTS[fmt][1], ow, osc, x)
+    tols = check_logits(host(out["logits"]), want)
+    check_topk(host(out["ids"]), host(out["vals"]), want, k, tols)

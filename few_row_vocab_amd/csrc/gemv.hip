@@ -57,9 +57,14 @@ constexpr int kCacheNT = 2;              // gfx950 cache policy bit 1: non-tempo
 // non-temporal hint peaked with about 32 KiB in flight per compute unit (7.0 TB/s) and fell
 // with more (6.65 TB/s at 64 KiB).  In the GEMV at H = 5120, 32 KiB (FP8) and 48 KiB (bf16)
 // measured best, by about 1% over a whole tile in flight; 16 and 24 KiB (one FP8 block a
-// wave) were 15% slower.
+// wave) were slower.  16-row launches whose waves take 7 or 8 FP8 blocks (H from 6,145 to
+// 8,192) do better with one block a wave in flight (16 KiB): H = 7168, 169.6-169.9 against 172.8-173.2 us at one row (176.7
+// against 179.2-179.6 at 16 rows); H = 8192, 160.2-160.6 against 162.1-163.0 at one row;
+// at 6 blocks (H = 6144) one block was slower (119.8-120.3 against 116.1-116.6).
 template <int FMT>
 constexpr int tiled_ahead_kib() { return FMT == DH_BF16 ? 48 : 32; }
+template <int FMT, int KW>
+constexpr bool tiled_one_block() { return FMT != DH_BF16 && (KW == 7 || KW == 8); }
 constexpr int kMaxStageBytes = 64 * 1024;   // logits a block keeps in LDS until its end
 // A tile's sums in the stage.  Up to 16 rows (the draft's cut runs there) a tile is padded by
 // 16 floats: the cut reads one row's entries of four tiles in one instruction, and unpadded
@@ -472,7 +477,8 @@ __global__ __launch_bounds__(VW == 1 ? 1024 : 64 * kMaxWaves2) void gemv_kernel(
     // blocks a wave keeps in flight: a whole tile (row-major heads), or a window sized so a
     // full workgroup (16 / VW waves) holds about tiled_ahead_kib (tiled heads)
     constexpr int AHW = tiled_ahead_kib<FMT>() * VW / (kMaxWaves * RQ);
-    constexpr int AH = !TL ? (CH ? 4 : KW) : AHW < 1 ? 1 : AHW > KW ? KW : AHW;
+    constexpr bool ONE = !CH && NB == 1 && VW == 1 && tiled_one_block<FMT, KW>();
+    constexpr int AH = !TL ? (CH ? 4 : KW) : ONE || AHW < 1 ? 1 : AHW > KW ? KW : AHW;
     __shared__ float red[2][kMaxWaves][NB][4 * TR][kWave];   // [virtual wave][act block]
     extern __shared__ float stage[];             // [tile of this block][c][i] (TR == 1)
     __shared__ uint32_t cut_rng[2][16];          // the cut: each row's image range (min, max)

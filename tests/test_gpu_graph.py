@@ -180,3 +180,50 @@ def test_graph_topk_standalone(R, k):
         assert not host(sync).any(), rep
         dh.topk(lg, k, ws=ws)                # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("R", [1, 16])
+def test_graph_linear_workspace(R):
+    """dh_linear_ws on a linear wider than 8192 columns (its column chunks at once, then their
+    sum in order) and dh_linear beside it, in every output mode, captured in one graph: every
+    replay equals the eager results, and the two entries agree bit for bit."""
+    need_gpu()
+    N, K = 2051, 18432
+    w = synth.random_head(N, K, seed=201, std=0.02)
+    gr = dh.tile(dh.Head(dh.FP8_ROW, *dh.quantize(dev_u16(w).view(torch.bfloat16), dh.FP8_ROW)))
+    x = dev_u16(synth.random_acts(R, K, seed=202))
+    res = dev_u16(synth.random_acts(R, N, seed=203, std=0.5))
+    ws = dh.linear_workspace(R, N, K)
+    o = {"f32": torch.empty((R, N), dtype=torch.float32, device="cuda"),
+         "bf16": torch.empty((R, N), dtype=torch.int16, device="cuda"),
+         "add": torch.empty((R, N), dtype=torch.int16, device="cuda"),
+         "plain": torch.empty((R, N), dtype=torch.float32, device="cuda")}
+
+    def step():
+        dh.linear(gr, x, dh.OUT_F32, out=o["f32"], ws=ws)
+        dh.linear(gr, x, dh.OUT_BF16, out=o["bf16"], ws=ws)
+        dh.linear(gr, x, dh.OUT_ADD_BF16, residual=res, out=o["add"], ws=ws)
+        dh.linear(gr, x, dh.OUT_F32, out=o["plain"])
+
+    step()
+    torch.cuda.synchronize()
+    want = _snap(o)
+    assert np.array_equal(want["f32"].view(np.uint32), want["plain"].view(np.uint32))
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in o.values():
+            t.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same(want, _snap(o))
+        dh.linear(gr, x, dh.OUT_F32, out=o["plain"], ws=ws)   # eager work between replays
+        torch.cuda.synchronize()

@@ -116,3 +116,19 @@ def test_topk_softmax_preallocated_outputs():
         for a, b in zip(got, ref):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32))
         check_softmax(logits, k, got)
+
+
+@pytest.mark.parametrize("R", [1, 16, 32])
+def test_topk_softmax_largest_vocabulary(R):
+    """The largest vocabulary the top-k takes (V = 262,144) at k = 512: at one row the cut
+    pass's 256 chunks a row, from 16 rows on its largest chunks (64 a row, 4096 logits)."""
+    need_gpu()
+    V, k = 262144, 512
+    say(f"topk_softmax V={V} R={R}")
+    logits = _planted(R, V, seed=R + 262)
+    d = dev(logits)
+    got = dh.topk_softmax(d, k)
+    i2, v2, _ = dh.topk(d, k)
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], i2) and torch.equal(got[1].view(torch.int32), v2.view(torch.int32))
+    check_softmax(logits, k, got)

@@ -1,4 +1,6 @@
-"""Seeded random shapes across the whole range the library takes: rows 1..32, H a multiple
+"""Seeded random shapes across the whole range the library takes.
+
+dh_draft: rows 1..32, H a multiple
 of 32 up to 32,768 (so the chunked GEMV for H > 8192 and the one-pass form for 17-32 rows
 both come up), V up to 262,144 with ragged tails, k 1..512, the three head formats, row-major
 and tiled heads, one- and two-stage drafts.  Each case checks
@@ -12,6 +14,13 @@ and tiled heads, one- and two-stage drafts.  Each case checks
 * in the two-stage form, the exact logits against the oracle's rescore of the GPU's own
   candidates and the draft against the oracle's winner (the conditional oracle).
 
+dh_topk, dh_topk_mapped and dh_topk_softmax: rows 1..32, V up to 262,144, k 1..512, rows of
+every planted kind (NaN, -inf, ties, zeros of both signs, subnormals, sorted runs, few
+eligible entries), a strictly increasing id map half the time: bit for bit against the
+oracle's top-k, the softmax statistics within their stated tolerance.
+
+dh_linear: rows 1..32, K up to 32,768, N up to 40,000, the three formats and output modes.
+
 The oracle's work is bounded: V*H*R <= 1e9 multiply-adds and V*H <= 6e7 weights a case."""
 import numpy as np
 import pytest
@@ -20,9 +29,11 @@ import torch
 import oracle
 import synth
 from few_row_vocab_amd import dh
-from gpu_util import dev_u16, host, need_gpu, say
+from gpu_util import dev, dev_u16, host, need_gpu, say
 from parity import check_logits, check_topk
-from test_gpu_core import FMTS, check_topk_winner, make_heads
+from test_gpu_core import FMTS, _planted, check_topk_winner, make_heads
+from test_gpu_linear import _check_modes
+from test_gpu_softmax import check_softmax
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +97,53 @@ def test_random_shape_draft(seed):
     etol = check_logits(host(out["exact"]), oe, what="exact")
     for r in range(R):
         check_topk_winner(gd[r], oe[r], gi[r], etol[r], od[r])
+
+
+def _log_uniform(rng, lo, hi):
+    return int(np.exp(rng.uniform(np.log(lo), np.log(hi + 1))))
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_shape_topk(seed):
+    need_gpu()
+    rng = np.random.default_rng(9300 + seed)
+    R = int(rng.integers(1, dh.MAX_ROWS + 1))
+    V = min(_log_uniform(rng, 1, dh.MAX_VOCAB), dh.MAX_VOCAB)
+    k = int(rng.integers(1, min(dh.MAX_K, V) + 1))
+    mapped = bool(rng.random() < 0.5)
+    say(f"random top-k {seed}: R={R} V={V} k={k} mapped={mapped}")
+    logits = _planted(R, V, seed=9400 + seed)
+    d = dev(logits)
+    if mapped:
+        idmap = np.sort(rng.choice(2 * V + 7, V, replace=False)).astype(np.int32)
+        ids, vals, am = dh.topk_mapped(d, k, dev(idmap))
+        oi, ov = oracle.topk_mapped(logits, k, idmap)
+    else:
+        ids, vals, am = dh.topk(d, k)
+        oi, ov = oracle.topk(logits, k)
+        sm = dh.topk_softmax(d, k)
+    gi, gv = host(ids), host(vals)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.view(np.uint32), ov.view(np.uint32))
+    assert np.array_equal(host(am), oi[:, 0])
+    if not mapped:
+        check_softmax(logits, k, sm)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_linear(seed):
+    need_gpu()
+    rng = np.random.default_rng(9500 + seed)
+    fmt = ["bf16", "block", "row"][seed % 3]
+    R = int(rng.integers(1, dh.MAX_ROWS + 1))
+    K = 32 * _log_uniform(rng, 1, dh.MAX_HIDDEN // 32)
+    K = min(K, dh.MAX_HIDDEN)
+    N = max(1, min(_log_uniform(rng, 1, 40000), int(MACS // (K * R)), int(ELEMS // K)))
+    say(f"random linear {seed}: {fmt} R={R} N={N} K={K}")
+    w = synth.random_head(N, K, seed=9600 + seed, std=0.02)
+    x = synth.random_acts(R, K, seed=9700 + seed)
+    res = synth.random_acts(R, N, seed=9800 + seed, std=0.5)
+    gh, (ow, osc) = make_heads(fmt, w)
+    if rng.random() < 0.5 and dh.tiled_bytes(gh.format, N, K):
+        gh = dh.tile(gh)
+    _check_modes(gh, x, res, FMTS[fmt][1], ow, osc)

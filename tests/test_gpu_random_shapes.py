@@ -21,6 +21,10 @@ oracle's top-k, the softmax statistics within their stated tolerance.
 
 dh_linear: rows 1..32, K up to 32,768, N up to 40,000, the three formats and output modes.
 
+dh_draft_lowrank: rows 1..32, H up to 8,192, rank 32..1,024, V up to 262,144, k 1..512, the
+down and up heads in any of the three formats, one- and two-stage, by the rules of
+test_gpu_lowrank.py.
+
 The oracle's work is bounded: V*H*R <= 1e9 multiply-adds and V*H <= 6e7 weights a case."""
 import numpy as np
 import pytest
@@ -33,6 +37,7 @@ from gpu_util import dev, dev_u16, host, need_gpu, say
 from parity import check_logits, check_topk
 from test_gpu_core import FMTS, _planted, check_topk_winner, make_heads
 from test_gpu_linear import _check_modes
+from test_gpu_lowrank import run_and_check
 from test_gpu_softmax import check_softmax
 
 pytestmark = pytest.mark.gpu
@@ -147,3 +152,25 @@ def test_random_shape_linear(seed):
     if rng.random() < 0.5 and dh.tiled_bytes(gh.format, N, K):
         gh = dh.tile(gh)
     _check_modes(gh, x, res, FMTS[fmt][1], ow, osc)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shape_lowrank(seed):
+    need_gpu()
+    rng = np.random.default_rng(9900 + seed)
+    dfmt = ["bf16", "block", "row"][seed % 3]
+    ufmt = ["bf16", "block", "row"][(seed // 3) % 3]
+    R = int(rng.integers(1, dh.MAX_ROWS + 1))
+    H = 32 * _log_uniform(rng, 1, 256)
+    rk = 32 * _log_uniform(rng, 1, 32)
+    V = max(1, min(_log_uniform(rng, 16, dh.MAX_VOCAB), dh.MAX_VOCAB, int(MACS // (rk * R)),
+                   int(ELEMS // max(rk, H))))
+    k = int(rng.integers(1, min(dh.MAX_K, V) + 1))
+    two = bool(rng.random() < 0.3)
+    label = f"random lowrank {seed}: {dfmt}/{ufmt} R={R} H={H} r={rk} V={V} k={k} two={two}"
+    say(label)
+    down = synth.random_head(rk, H, seed=10000 + seed, std=1 / np.sqrt(H))
+    up = synth.random_head(V, rk, seed=10100 + seed, std=0.05)
+    x = synth.random_acts(R, H, seed=10200 + seed)
+    dense = synth.random_head(V, H, seed=10300 + seed, std=0.02) if two else None
+    run_and_check(dfmt, ufmt, down, up, x, k, dense, label)

@@ -21,6 +21,9 @@ oracle's top-k, the softmax statistics within their stated tolerance.
 
 dh_linear: rows 1..32, K up to 32,768, N up to 40,000, the three formats and output modes.
 
+dh_draft_mapped on a gathered subset head: rows 1..32, H up to 8,192, a subset of 1..V of
+the head's ids, bf16 or FP8 row-scale, one- and two-stage, by the rules of test_gpu_subset.py.
+
 dh_draft_lowrank: rows 1..32, H up to 8,192, rank 32..1,024, V up to 262,144, k 1..512, the
 down and up heads in any of the three formats, one- and two-stage, by the rules of
 test_gpu_lowrank.py.
@@ -38,6 +41,7 @@ from parity import check_logits, check_topk
 from test_gpu_core import FMTS, _planted, check_topk_winner, make_heads
 from test_gpu_linear import _check_modes
 from test_gpu_lowrank import run_and_check
+from test_gpu_subset import local_ids, oracle_subset
 from test_gpu_softmax import check_softmax
 
 pytestmark = pytest.mark.gpu
@@ -174,3 +178,45 @@ def test_random_shape_lowrank(seed):
     x = synth.random_acts(R, H, seed=10200 + seed)
     dense = synth.random_head(V, H, seed=10300 + seed, std=0.02) if two else None
     run_and_check(dfmt, ufmt, down, up, x, k, dense, label)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shape_mapped(seed):
+    need_gpu()
+    rng = np.random.default_rng(10400 + seed)
+    fmt = ["bf16", "row"][seed % 2]
+    R = int(rng.integers(1, dh.MAX_ROWS + 1))
+    H = 32 * _log_uniform(rng, 1, 256)
+    V = max(2, min(_log_uniform(rng, 16, dh.MAX_VOCAB), int(MACS // (H * R)), int(ELEMS // H)))
+    n = int(rng.integers(1, V + 1))
+    k = int(rng.integers(1, min(dh.MAX_K, n) + 1))
+    two = bool(rng.random() < 0.3)
+    say(f"random mapped {seed}: {fmt} R={R} H={H} V={V} n={n} k={k} two={two}")
+    w = synth.random_head(V, H, seed=10500 + seed, std=0.02)
+    x = synth.random_acts(R, H, seed=10600 + seed)
+    gh, oh = make_heads(fmt, w)
+    idmap = synth.token_ids(V, n, seed=10700 + seed)
+    im = dev(idmap)
+    sub = dh.gather_rows(gh, im)
+    dense = dh.Head(dh.BF16, dev_u16(w)) if two else None
+    xd = dev_u16(x)
+    out = dh.draft_mapped(sub, im, xd, k, dense=dense, keep_logits=True)
+    full = dh.gemv(gh, xd)
+    torch.cuda.synchronize()
+    glog, ids, vals, dr = (host(out[n_]) for n_ in ("logits", "ids", "vals", "draft"))
+    assert np.array_equal(glog.view(np.uint32), host(full)[:, idmap].view(np.uint32))
+    ofmt = FMTS[fmt][1]
+    ow, osc = oracle_subset(ofmt, oh, idmap)
+    want = oracle.gemv(ofmt, ow, osc, x)
+    tols = check_logits(glog, want)
+    oi, ov = oracle.topk_mapped(glog, k, idmap)
+    assert np.array_equal(ids, oi)
+    assert np.array_equal(vals.view(np.uint32), ov.view(np.uint32))
+    check_topk(local_ids(ids, vals, idmap), vals, want, k, tols)
+    if not two:
+        assert np.array_equal(dr, ids[:, 0])
+        return
+    oe, od = oracle.rescore(w, x, ids, vals > -np.inf)
+    etol = check_logits(host(out["exact"]), oe, what="exact")
+    for r in range(R):
+        check_topk_winner(dr[r], oe[r], ids[r], etol[r], od[r])

@@ -24,6 +24,9 @@ dh_linear: rows 1..32, K up to 32,768, N up to 40,000, the three formats and out
 dh_draft_mapped on a gathered subset head: rows 1..32, H up to 8,192, a subset of 1..V of
 the head's ids, bf16 or FP8 row-scale, one- and two-stage, by the rules of test_gpu_subset.py.
 
+dh_sample (the keyed pick) on dh_topk's lists: rows 1..32, V up to 262,144, k 1..512,
+temperature 0..2, top-p and min-p drawn at random, by the rules of test_gpu_sample.py.
+
 dh_draft_lowrank: rows 1..32, H up to 8,192, rank 32..1,024, V up to 262,144, k 1..512, the
 down and up heads in any of the three formats, one- and two-stage, by the rules of
 test_gpu_lowrank.py.
@@ -41,6 +44,7 @@ from parity import check_logits, check_topk
 from test_gpu_core import FMTS, _planted, check_topk_winner, make_heads
 from test_gpu_linear import _check_modes
 from test_gpu_lowrank import run_and_check
+from test_gpu_sample import check_picks
 from test_gpu_subset import local_ids, oracle_subset
 from test_gpu_softmax import check_softmax
 
@@ -220,3 +224,25 @@ def test_random_shape_mapped(seed):
     etol = check_logits(host(out["exact"]), oe, what="exact")
     for r in range(R):
         check_topk_winner(dr[r], oe[r], ids[r], etol[r], od[r])
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_shape_sample(seed):
+    need_gpu()
+    rng = np.random.default_rng(10800 + seed)
+    R = int(rng.integers(1, dh.MAX_ROWS + 1))
+    V = min(_log_uniform(rng, 1, dh.MAX_VOCAB), dh.MAX_VOCAB)
+    k = int(rng.integers(1, min(dh.MAX_K, V) + 1))
+    T = 0.0 if rng.random() < 0.15 else float(rng.uniform(0.02, 2.0))
+    top_p = 1.0 if rng.random() < 0.4 else float(rng.uniform(0.05, 1.0))
+    min_p = 0.0 if rng.random() < 0.5 else float(rng.uniform(0.0, 0.5))
+    key = int(rng.integers(0, 2**63)) * 2 + 1
+    say(f"random sample {seed}: R={R} V={V} k={k} T={T:.3f} top_p={top_p:.3f} "
+        f"min_p={min_p:.3f}")
+    logits = _planted(R, V, seed=10900 + seed)
+    ids, vals, _ = dh.topk(dev(logits), k)
+    pos = rng.integers(0, 2**40, R).astype(np.int64)
+    tok, kept = dh.sample(ids, vals, dev(pos), temperature=T, top_p=top_p, min_p=min_p,
+                          seed=key)
+    torch.cuda.synchronize()
+    check_picks(host(ids), host(vals), T, top_p, min_p, key, pos, host(tok), host(kept))

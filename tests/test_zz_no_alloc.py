@@ -56,6 +56,42 @@ def test_noalloc_equals_draft_two_calls(two_stage):
         say(f"  call {i}: V={V} H={H} R={R} k={k} equal")
 
 
+def test_noalloc_random_sequence():
+    """Twelve calls in a row of seeded random shapes (rows 1..32, H up to 8192, V up to 2^18,
+    k 1..512, three formats, row-major or tiled, one or two stages, logits kept or in the
+    scratch), each on the scratch the previous one left behind: bit-equal to dh_draft."""
+    need_gpu()
+    rng = np.random.default_rng(4242)
+    fmts = [dh.BF16, dh.FP8_BLOCK32, dh.FP8_ROW]
+    for i in range(12):
+        R = int(rng.integers(1, dh.MAX_ROWS + 1))
+        H = 32 * int(np.exp(rng.uniform(0, np.log(256))))
+        V = int(np.exp(rng.uniform(np.log(16), np.log(dh.MAX_VOCAB))))
+        V = max(16, min(V, int(3e7 // H)))
+        k = int(rng.integers(1, min(dh.MAX_K, V) + 1))
+        two = bool(rng.random() < 0.3)
+        keep = bool(rng.random() < 0.5)
+        while dh.workspace_bytes(R, V, k) + 4096 > dh.NOALLOC_SCRATCH_BYTES:
+            V //= 2                         # the top-k's workspace alone must fit the scratch
+        k = min(k, V)
+        if dh.workspace_bytes(R, V, k) + R * V * 4 + 4096 > dh.NOALLOC_SCRATCH_BYTES:
+            keep = True                     # the logits would not fit beside the workspace
+        f = fmts[i % 3]
+        say(f"  noalloc sequence {i}: fmt={f} R={R} H={H} V={V} k={k} two={two} keep={keep}")
+        w = synth.random_head(V, H, seed=500 + i, std=0.02)
+        wd, xd = dev_u16(w), dev_u16(synth.random_acts(R, H, seed=600 + i))
+        head = dh.Head(f, wd) if f == dh.BF16 else dh.Head(f, *dh.quantize(wd, f))
+        if rng.random() < 0.5 and dh.tiled_bytes(head.format, V, H):
+            head = dh.tile(head)
+        dense = dh.Head(dh.BF16, wd) if two else None
+        want = dh.draft(head, xd, k, dense=dense, keep_logits=keep)
+        got = _outs(R, k, V, two, keep)
+        dh.draft_noalloc(head, xd, k, dense=dense, out=got)
+        torch.cuda.synchronize()
+        for name in want:
+            assert torch.equal(got[name], want[name]), (i, name)
+
+
 def test_noalloc_refuses_beyond_its_scratch():
     need_gpu()
     V, H, R, k = 200000, 64, 32, 8

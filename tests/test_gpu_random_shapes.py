@@ -27,6 +27,10 @@ the head's ids, bf16 or FP8 row-scale, one- and two-stage, by the rules of test_
 dh_sample (the keyed pick) on dh_topk's lists: rows 1..32, V up to 262,144, k 1..512,
 temperature 0..2, top-p and min-p drawn at random, by the rules of test_gpu_sample.py.
 
+dh_rescore and dh_rescore_sync: thirty calls in a row through one sync buffer, rows 1..32,
+H up to 32,768, 1..512 candidates a row with duplicates and ids outside the head planted:
+the two bit-equal, the buffer all zero after each, the oracle's exact logits within tolerance.
+
 dh_draft_lowrank: rows 1..32, H up to 8,192, rank 32..1,024, V up to 262,144, k 1..512, the
 down and up heads in any of the three formats, one- and two-stage, by the rules of
 test_gpu_lowrank.py.
@@ -40,6 +44,7 @@ import oracle
 import synth
 from few_row_vocab_amd import dh
 from gpu_util import dev, dev_u16, host, need_gpu, say
+from test_gpu_rescore_sync import both
 from parity import check_logits, check_topk
 from test_gpu_core import FMTS, _planted, check_topk_winner, make_heads
 from test_gpu_linear import _check_modes
@@ -246,3 +251,32 @@ def test_random_shape_sample(seed):
                           seed=key)
     torch.cuda.synchronize()
     check_picks(host(ids), host(vals), T, top_p, min_p, key, pos, host(tok), host(kept))
+
+
+def test_random_shape_rescore_sequence():
+    need_gpu()
+    rng = np.random.default_rng(11000)
+    sync = dh.rescore_sync_buffer()
+    for i in range(30):
+        R = int(rng.integers(1, dh.MAX_ROWS + 1))
+        H = 32 * _log_uniform(rng, 1, dh.MAX_HIDDEN // 32)
+        H = min(H, dh.MAX_HIDDEN)
+        V = max(1, min(_log_uniform(rng, 1, 1 << 20), int(ELEMS // H)))
+        ck = int(rng.integers(1, dh.MAX_K + 1))
+        say(f"random rescore {i}: R={R} H={H} V={V} ck={ck}")
+        wd = synth.random_head(V, H, seed=11100 + i, std=0.02)
+        x = synth.random_acts(R, H, seed=11200 + i)
+        cand = rng.integers(0, V, (R, ck)).astype(np.int32)
+        bad = rng.random((R, ck)) < 0.02                 # ids outside the head: NaN, never read
+        cand[bad] = rng.choice([-1, V, V + 1000, np.iinfo(np.int32).max], int(bad.sum()))
+        if ck > 1:
+            cand[0, ck // 2:] = cand[0, 0]               # a run of one repeated id
+        dense = dh.Head(dh.BF16, dev_u16(wd))
+        e1, d1, e2, d2 = both(dense, dev_u16(x), dev(cand), sync)
+        assert np.array_equal(e1.view(np.uint32), e2.view(np.uint32)), i
+        assert np.array_equal(d1, d2), i
+        assert not host(sync).any(), f"call {i} left its sync buffer non-zero"
+        oe, od = oracle.rescore(wd, x, cand)
+        tols = check_logits(e2, oe, what="exact")
+        for r in range(R):
+            check_topk_winner(d2[r], oe[r], cand[r], tols[r], od[r])
